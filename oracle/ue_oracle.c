@@ -1,0 +1,299 @@
+/*
+ * ue_oracle.c -- plain, sequential CPU reference for the per-layer MoE
+ * expert-rebalancing path: exact expert load, quota replica planning,
+ * logical -> physical reroute, and the stable dispatch layout.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark load this file's library. The product
+ * library (the HIP path) never links, loads or calls it, and the two share
+ * no source, header, table or helper.
+ *
+ * What is computed, and where it comes from:
+ *  - UltraEP (arXiv 2606.04101) abstract: the balancer is "exact-load",
+ *    i.e. it works from the true per-expert token count of the current
+ *    routing, not from history.
+ *  - "How dots-infra/ultraep works" (gitdiagram), summary and connection
+ *    list: the framework passes post-gating routing; the manager profiles
+ *    loads, updates placement (plans replicas), syncs weights, then expands
+ *    routing to physical routing for token dispatch.
+ *  - UltraEP news write-up ("balansirovka MoE-ekspertov za 300 mks"),
+ *    section on how the 300 us balancing works: a quota-driven scheduler
+ *    rebalances every microbatch and every layer right after gating.
+ *  The pages give no quota formula, tie-break or slot model. The rule here
+ *  is the plainest reading consistent with them:
+ *    quota Q = ceil(sum(counts) / R);
+ *    expert e lives natively on rank e*R/E (= e / N with N = E/R experts
+ *    per rank), in slot e mod N; each rank also owns S empty spare slots;
+ *    physical slot id p = r*(N+S) + s (natives 0..N-1, spares N..N+S-1);
+ *    experts of overloaded ranks (load > Q) are visited heaviest first
+ *    (count desc, id asc); each spills its rank's excess, chunk by chunk,
+ *    into a spare slot of the least-loaded rank (ties: lowest rank id) that
+ *    has a free spare slot and load < Q; a chunk is the smallest of the
+ *    source's excess, the expert's remaining tokens and the destination's
+ *    headroom; if no destination exists the plan stops ("exhausted");
+ *    the j-th assignment of expert e, in flat (token, slot) order, goes to
+ *    the replica whose capacity prefix covers j (master first, then replicas
+ *    in creation order);
+ *    the dispatch permutation is the stable counting sort by physical slot.
+ *
+ * Everything is integer; there is nothing to round.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* Step 1. Exact per-expert load: counts[e] = number of assignments whose
+ * logical expert id is e. Ids outside [0, E) are not counted; the number
+ * of such ids is returned. */
+int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
+                 int32_t *counts)
+{
+    int64_t invalid = 0;
+    for (int32_t e = 0; e < n_experts; ++e)
+        counts[e] = 0;
+    for (int64_t a = 0; a < n_assign; ++a) {
+        int32_t e = routing[a];
+        if (e < 0 || e >= n_experts) {
+            ++invalid;
+            continue;
+        }
+        counts[e] += 1;
+    }
+    return invalid;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 2. Quota plan for one layer.
+ *
+ * scalars[0] = quota Q
+ * scalars[1] = exhausted (1 if an overloaded rank still had excess but no
+ *              rank was left with a free spare slot and load < Q)
+ * scalars[2] = residual = sum over ranks of max(0, load_after - Q)
+ * scalars[3] = n_rep, number of replica-table entries (masters included)
+ *
+ * Replica table (CSR by expert): entries rep_off[e] .. rep_off[e+1]-1 of
+ * rep_slot / rep_cap are the replicas of e; the first is always the native
+ * (master) slot, the rest follow in creation order. Entries at and after
+ * n_rep (the table has room for P = R*(N+S) entries) hold slot -1, cap 0.
+ *
+ * Slot tables over the P physical slots: slot_expert[p] is the expert held
+ * by p (-1 for an unused spare), slot_cap[p] its capacity (0 if unused),
+ * slot_off the exclusive prefix sum of slot_cap (P+1 entries).
+ *
+ * Returns 0, or -1 if the shape is not one the slot model covers. */
+int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
+             int32_t *scalars, int32_t *rep_off, int32_t *rep_slot,
+             int32_t *rep_cap, int32_t *slot_expert, int32_t *slot_cap,
+             int32_t *slot_off, int32_t *load_before, int32_t *load_after)
+{
+    if (E <= 0 || R <= 0 || S < 0 || E % R != 0)
+        return -1;
+    const int32_t N = E / R;       /* native experts per rank */
+    const int32_t NS = N + S;      /* physical slots per rank */
+    const int32_t P = R * NS;      /* physical slots in total */
+
+    int64_t *load = calloc((size_t)R, sizeof(int64_t));
+    int64_t *rem = calloc((size_t)E, sizeof(int64_t));
+    int32_t *nfree = calloc((size_t)R, sizeof(int32_t));
+    int32_t *cand = calloc((size_t)E, sizeof(int32_t));
+    /* spill records in creation order: expert, slot, amount */
+    int32_t *rec_e = calloc((size_t)(R * S + 1), sizeof(int32_t));
+    int32_t *rec_p = calloc((size_t)(R * S + 1), sizeof(int32_t));
+    int64_t *rec_m = calloc((size_t)(R * S + 1), sizeof(int64_t));
+    if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m) {
+        free(load); free(rem); free(nfree); free(cand);
+        free(rec_e); free(rec_p); free(rec_m);
+        return -1;
+    }
+
+    /* Quota and rank loads under the native placement. */
+    int64_t total = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        total += counts[e];
+        load[e / N] += counts[e];
+        rem[e] = counts[e];
+    }
+    const int64_t Q = (total + R - 1) / R;
+    for (int32_t r = 0; r < R; ++r) {
+        load_before[r] = (int32_t)load[r];
+        nfree[r] = S;
+    }
+
+    /* Candidates: experts of overloaded ranks, heaviest first (count desc,
+     * id asc). Plain insertion sort. */
+    int32_t ncand = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        if (load[e / N] <= Q)
+            continue;
+        int32_t i = ncand++;
+        while (i > 0) {
+            int32_t prev = cand[i - 1];
+            int before = counts[prev] > counts[e] ||
+                         (counts[prev] == counts[e] && prev < e);
+            if (before)
+                break;
+            cand[i] = prev;
+            --i;
+        }
+        cand[i] = e;
+    }
+
+    /* Spill loop. */
+    int exhausted = 0;
+    int32_t nrec = 0;
+    for (int32_t c = 0; c < ncand && !exhausted; ++c) {
+        const int32_t e = cand[c];
+        const int32_t r = e / N;
+        while (load[r] > Q && rem[e] > 0) {
+            /* least-loaded eligible destination; ascending scan with a
+             * strict comparison keeps the lowest rank id among ties */
+            int32_t d = -1;
+            for (int32_t x = 0; x < R; ++x) {
+                if (nfree[x] <= 0 || load[x] >= Q)
+                    continue;
+                if (d < 0 || load[x] < load[d])
+                    d = x;
+            }
+            if (d < 0) {
+                exhausted = 1;
+                break;
+            }
+            int64_t m = load[r] - Q;
+            if (rem[e] < m)
+                m = rem[e];
+            if (Q - load[d] < m)
+                m = Q - load[d];
+            /* lowest free spare slot of d */
+            const int32_t p = d * NS + N + (S - nfree[d]);
+            rec_e[nrec] = e;
+            rec_p[nrec] = p;
+            rec_m[nrec] = m;
+            ++nrec;
+            rem[e] -= m;
+            load[r] -= m;
+            load[d] += m;
+            nfree[d] -= 1;
+        }
+    }
+
+    /* Replica table: master first (keeps what was not spilled), then the
+     * spilled replicas in creation order. */
+    int32_t n = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        rep_off[e] = n;
+        rep_slot[n] = (e / N) * NS + (e % N);
+        rep_cap[n] = (int32_t)rem[e];
+        ++n;
+        for (int32_t i = 0; i < nrec; ++i) {
+            if (rec_e[i] != e)
+                continue;
+            rep_slot[n] = rec_p[i];
+            rep_cap[n] = (int32_t)rec_m[i];
+            ++n;
+        }
+    }
+    rep_off[E] = n;
+    for (int32_t i = n; i < P; ++i) {
+        rep_slot[i] = -1;
+        rep_cap[i] = 0;
+    }
+
+    /* Slot tables. */
+    for (int32_t p = 0; p < P; ++p) {
+        slot_expert[p] = -1;
+        slot_cap[p] = 0;
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        for (int32_t i = rep_off[e]; i < rep_off[e + 1]; ++i) {
+            slot_expert[rep_slot[i]] = e;
+            slot_cap[rep_slot[i]] = rep_cap[i];
+        }
+    }
+    slot_off[0] = 0;
+    for (int32_t p = 0; p < P; ++p)
+        slot_off[p + 1] = slot_off[p] + slot_cap[p];
+
+    int64_t residual = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        load_after[r] = (int32_t)load[r];
+        if (load[r] > Q)
+            residual += load[r] - Q;
+    }
+    scalars[0] = (int32_t)Q;
+    scalars[1] = exhausted;
+    scalars[2] = (int32_t)residual;
+    scalars[3] = n;
+
+    free(load); free(rem); free(nfree); free(cand);
+    free(rec_e); free(rec_p); free(rec_m);
+    return 0;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 3. Reroute and dispatch layout for one layer.
+ *
+ * For every assignment a in flat (token, slot) order with logical expert
+ * e = routing[a]: j = number of earlier assignments of e; the replica i of
+ * e whose capacity prefix covers j receives it:
+ *     phys[a]     = rep_slot[i]
+ *     pos         = slot_off[phys[a]] + (j - prefix_i)
+ *     perm[pos]   = a,  inv_perm[a] = pos
+ * rank_counts[r] counts the assignments whose physical slot is on rank r.
+ *
+ * Assignments with an id outside [0, E), beyond the plan's capacity for
+ * their expert, or whose position would fall outside [0, n_assign) (a plan
+ * made for other counts), get phys = -1 and inv_perm = -1, and are counted
+ * in the return value; perm entries nobody fills keep whatever the caller put
+ * there. */
+int64_t orc_reroute(const int32_t *routing, int64_t n_assign, int32_t E,
+                    int32_t R, int32_t S, const int32_t *rep_off,
+                    const int32_t *rep_slot, const int32_t *rep_cap,
+                    const int32_t *slot_off, int32_t *phys, int32_t *perm,
+                    int32_t *inv_perm, int32_t *rank_counts)
+{
+    const int32_t N = E / R;
+    const int32_t NS = N + S;
+    int64_t *seen = calloc((size_t)E, sizeof(int64_t));
+    if (!seen)
+        return -1;
+    int64_t faults = 0;
+    for (int32_t r = 0; r < R; ++r)
+        rank_counts[r] = 0;
+
+    for (int64_t a = 0; a < n_assign; ++a) {
+        const int32_t e = routing[a];
+        phys[a] = -1;
+        inv_perm[a] = -1;
+        if (e < 0 || e >= E) {
+            ++faults;
+            continue;
+        }
+        const int64_t j = seen[e]++;
+        int64_t prefix = 0;
+        int32_t hit = -1;
+        for (int32_t i = rep_off[e]; i < rep_off[e + 1]; ++i) {
+            if (j < prefix + rep_cap[i]) {
+                hit = i;
+                break;
+            }
+            prefix += rep_cap[i];
+        }
+        if (hit < 0) {
+            ++faults;
+            continue;
+        }
+        const int32_t p = rep_slot[hit];
+        const int64_t pos = slot_off[p] + (j - prefix);
+        if (pos < 0 || pos >= n_assign) {
+            ++faults;
+            continue;
+        }
+        phys[a] = p;
+        perm[pos] = (int32_t)a;
+        inv_perm[a] = (int32_t)pos;
+        rank_counts[p / NS] += 1;
+    }
+    free(seen);
+    return faults;
+}

@@ -1,0 +1,379 @@
+"""Checks that pin the CPU oracle to facts other than itself.
+
+Every check raises AssertionError on failure. They are used twice: against
+the oracle as built (``test_oracle_pins.py``) and against copies of the
+oracle with a planted mistake (``test_oracle_mutants.py``), which must each
+fail at least one check.
+
+Sources of truth, none of them the oracle's own code:
+  * hand-worked golden cases under ``tests/golden`` (planning rule read from
+    the pages: "quota-driven scheduler", UltraEP news write-up; "plans
+    replicas ... expands routing", gitdiagram summary; "exact-load", UltraEP
+    abstract);
+  * closed forms of degenerate cases (no spare slots, one rank, balanced
+    routing, a single hot expert);
+  * library routines: ``np.bincount`` for loads, ``np.argsort(kind="stable")``
+    for the dispatch permutation, ``np.searchsorted`` for the capacity-prefix
+    lookup, ``scipy.sparse.csgraph.maximum_flow`` for optimal placements;
+  * invariants any correct plan satisfies (conservation, one replica per
+    spare slot, quota respected whenever slots suffice, ...).
+"""
+from __future__ import annotations
+
+import glob
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                          "golden")
+
+
+# --------------------------------------------------------------------------
+# golden cases
+
+def golden_cases():
+    return [json.load(open(p)) for p in
+            sorted(glob.glob(os.path.join(GOLDEN_DIR, "*.json")))]
+
+
+def _eq(name, got, want):
+    got = [int(v) for v in np.asarray(got).reshape(-1)]
+    want = [int(v) for v in want]
+    assert got == want, f"{name}: got {got}, want {want}"
+
+
+def check_golden(g):
+    pl = oracle.plan(np.asarray(g["counts"], np.int32), g["R"], g["S"])
+    for key in ("quota", "exhausted", "residual", "n_rep"):
+        assert pl[key] == g[key], f"{g['name']}: {key} {pl[key]} != {g[key]}"
+    for key in ("load_before", "load_after", "rep_off", "slot_expert",
+                "slot_cap", "slot_off"):
+        _eq(f"{g['name']}: {key}", pl[key], g[key])
+    n = g["n_rep"]
+    _eq(f"{g['name']}: rep_slot", pl["rep_slot"][:n], g["rep_slot"])
+    _eq(f"{g['name']}: rep_cap", pl["rep_cap"][:n], g["rep_cap"])
+    assert np.all(pl["rep_slot"][n:] == -1) and np.all(pl["rep_cap"][n:] == 0)
+    if "routing" in g:
+        routing = np.asarray(g["routing"], np.int32)
+        counts, invalid = oracle.load(routing[None], g["E"])
+        _eq(f"{g['name']}: counts", counts[0], g["counts"])
+        assert invalid[0] == 0
+        rr = oracle.reroute(routing.reshape(-1), pl)
+        assert rr["faults"] == 0
+        for key in ("phys", "perm", "inv_perm", "rank_counts"):
+            _eq(f"{g['name']}: {key}", rr[key], g[key])
+
+
+# --------------------------------------------------------------------------
+# invariants on arbitrary instances
+
+def random_routing(rng, T, E, k, skew):
+    """T tokens with k distinct experts each, Zipf-like weights."""
+    if T == 0:
+        return np.zeros((0, k), np.int32)
+    w = np.arange(1, E + 1, dtype=np.float64) ** (-skew)
+    w = w[rng.permutation(E)]
+    p = w / w.sum()
+    # successive sampling without replacement via Gumbel keys
+    keys = np.log(p)[None, :] + rng.gumbel(size=(T, E))
+    return np.argsort(-keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def random_instance(rng, max_ranks=8, max_native=4, max_spare=3,
+                    max_tokens=64, max_k=4):
+    R = int(rng.integers(1, max_ranks + 1))
+    N = int(rng.integers(1, max_native + 1))
+    E = R * N
+    S = int(rng.integers(0, max_spare + 1))
+    k = int(rng.integers(1, min(E, max_k) + 1))
+    T = int(rng.integers(0, max_tokens + 1))
+    skew = float(rng.uniform(0.0, 3.0))
+    return random_routing(rng, T, E, k, skew), E, R, S
+
+
+def check_load(routing, E):
+    flat = np.asarray(routing, np.int32).reshape(-1)
+    counts, invalid = oracle.load(flat[None, None, :], E)
+    valid = flat[(flat >= 0) & (flat < E)]
+    want = np.bincount(valid, minlength=E)
+    assert np.array_equal(counts[0], want), "counts differ from bincount"
+    assert invalid[0] == flat.size - valid.size, "invalid id count"
+    return counts[0]
+
+
+def check_plan(counts, R, S, A=None):
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    N, NS = E // R, E // R + S
+    P = R * NS
+    pl = oracle.plan(counts.astype(np.int32), R, S)
+    Q = pl["quota"]
+    total = int(counts.sum())
+    A = total if A is None else A
+    assert Q == -(-total // R), "quota is ceil(total / ranks)"
+    assert pl["P"] == P and pl["N"] == N
+
+    rep_off, rep_slot, rep_cap = pl["rep_off"], pl["rep_slot"], pl["rep_cap"]
+    n = pl["n_rep"]
+    assert rep_off[0] == 0 and rep_off[E] == n and n <= P
+    assert np.all(np.diff(rep_off) >= 1), "every expert keeps its master"
+    assert np.all(rep_slot[n:] == -1) and np.all(rep_cap[n:] == 0)
+    assert np.all(rep_cap[:n] >= 0)
+
+    seen_slots = set()
+    ranks_used_spares = {r: [] for r in range(R)}
+    for e in range(E):
+        ents = range(rep_off[e], rep_off[e + 1])
+        first = rep_off[e]
+        home = e // N
+        assert rep_slot[first] == home * NS + e % N, "master is native slot"
+        assert sum(int(rep_cap[i]) for i in ents) == counts[e], \
+            "replica capacities sum to the expert's load"
+        hosts = set()
+        for i in ents:
+            p = int(rep_slot[i])
+            assert 0 <= p < P and p not in seen_slots, "one entry per slot"
+            seen_slots.add(p)
+            r = p // NS
+            assert r not in hosts, "one replica per rank per expert"
+            hosts.add(r)
+            if i != first:
+                assert p % NS >= N, "replicas live in spare slots"
+                assert r != home, "never a replica on the home rank"
+                assert rep_cap[i] > 0, "a created replica carries tokens"
+                ranks_used_spares[r].append(p % NS - N)
+    for r, used in ranks_used_spares.items():
+        assert sorted(used) == list(range(len(used))), \
+            "spare slots are taken lowest first"
+
+    slot_expert, slot_cap = pl["slot_expert"], pl["slot_cap"]
+    want_exp = np.full(P, -1)
+    want_cap = np.zeros(P, np.int64)
+    for p in range(P):
+        if p % NS < N:
+            want_exp[p] = (p // NS) * N + p % NS
+    for e in range(E):
+        for i in range(rep_off[e], rep_off[e + 1]):
+            want_exp[rep_slot[i]] = e
+            want_cap[rep_slot[i]] = rep_cap[i]
+    assert np.array_equal(slot_expert, want_exp), "slot owner table"
+    assert np.array_equal(slot_cap, want_cap), "slot capacity table"
+    assert np.array_equal(pl["slot_off"],
+                          np.concatenate([[0], np.cumsum(want_cap)])), \
+        "slot offsets are the exclusive prefix of capacities"
+
+    before = counts.reshape(R, N).sum(axis=1)
+    after = np.asarray(slot_cap, np.int64).reshape(R, NS).sum(axis=1)
+    assert np.array_equal(pl["load_before"], before), "native rank loads"
+    assert np.array_equal(pl["load_after"], after), "rank loads after plan"
+    assert after.sum() == total, "assignments are conserved"
+    residual = int(np.maximum(after - Q, 0).sum())
+    assert pl["residual"] == residual
+    for r in range(R):
+        if before[r] > Q:
+            assert Q <= after[r] <= before[r], "sources shed down to Q only"
+        else:
+            assert before[r] <= after[r] <= Q, "destinations fill up to Q"
+    if pl["exhausted"]:
+        assert residual > 0
+        free = np.array([S - len(ranks_used_spares[r]) for r in range(R)])
+        assert np.all((free == 0) | (after >= Q)), \
+            "exhausted only when no rank has room and a free spare"
+    else:
+        assert residual == 0 and after.max(initial=0) <= Q, \
+            "every rank within quota whenever slots suffice"
+    return pl
+
+
+def check_reroute(routing, pl):
+    flat = np.asarray(routing, np.int32).reshape(-1)
+    A = flat.size
+    E, R, S = pl["E"], pl["R"], pl["S"]
+    NS = pl["N"] + S
+    rr = oracle.reroute(flat, pl)
+    phys, perm, inv = rr["phys"], rr["perm"], rr["inv_perm"]
+    assert rr["faults"] == 0
+    # stable dispatch order == library stable sort by physical slot
+    assert np.array_equal(perm, np.argsort(phys, kind="stable")), \
+        "perm is the stable sort of assignments by physical slot"
+    assert np.array_equal(inv[perm], np.arange(A)), "inverse permutation"
+    assert np.array_equal(pl["slot_expert"][phys], flat), \
+        "physical slot holds the logical expert"
+    assert np.array_equal(np.bincount(phys, minlength=pl["P"]),
+                          pl["slot_cap"]), "slot hit counts equal capacities"
+    assert np.array_equal(rr["rank_counts"],
+                          np.bincount(phys // NS, minlength=R))
+    assert np.array_equal(rr["rank_counts"], pl["load_after"])
+    # j-th assignment of e (flat order) -> replica whose prefix covers j
+    order = np.argsort(flat, kind="stable")
+    j = np.empty(A, np.int64)
+    sorted_e = flat[order]
+    starts = np.searchsorted(sorted_e, sorted_e, side="left")
+    j[order] = np.arange(A) - starts
+    for a in range(A):
+        e = flat[a]
+        lo, hi = pl["rep_off"][e], pl["rep_off"][e + 1]
+        cum = np.cumsum(pl["rep_cap"][lo:hi])
+        idx = int(np.searchsorted(cum, j[a], side="right"))
+        assert phys[a] == pl["rep_slot"][lo + idx], \
+            "j-th assignment goes to the replica covering j"
+    return rr
+
+
+def check_instance(routing, E, R, S):
+    counts = check_load(routing, E)
+    pl = check_plan(counts, R, S)
+    check_reroute(routing, pl)
+    return pl
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+def check_no_spares(rng):
+    """S = 0: nothing can move, so physical ids equal logical ids
+    (p = r*N + s = e) and the plan is exhausted iff a rank is over quota."""
+    for _ in range(20):
+        routing, E, R, _ = random_instance(rng)
+        counts = check_load(routing, E)
+        pl = oracle.plan(counts, R, 0)
+        rr = oracle.reroute(routing.reshape(-1), pl)
+        assert np.array_equal(rr["phys"], routing.reshape(-1))
+        assert pl["n_rep"] == E
+        over = counts.reshape(R, -1).sum(axis=1) > pl["quota"]
+        assert pl["exhausted"] == int(over.any())
+
+
+def check_one_rank(rng):
+    """R = 1: the only rank carries everything and is never over quota."""
+    for _ in range(20):
+        E = int(rng.integers(1, 9))
+        k = int(rng.integers(1, E + 1))
+        routing = random_routing(rng, int(rng.integers(0, 40)), E, k, 1.0)
+        counts = check_load(routing, E)
+        S = int(rng.integers(0, 3))
+        pl = oracle.plan(counts, 1, S)
+        assert pl["quota"] == routing.size and pl["n_rep"] == E
+        assert pl["exhausted"] == 0
+        rr = oracle.reroute(routing.reshape(-1), pl)
+        assert np.array_equal(rr["phys"], routing.reshape(-1))
+
+
+def check_balanced():
+    """Round-robin routing loads every rank equally: no replicas."""
+    for R, N, S, k in ((4, 2, 1, 2), (8, 8, 2, 8), (16, 1, 1, 4)):
+        E = R * N
+        T = 3 * E
+        routing = (np.arange(T * k) % E).astype(np.int32).reshape(T, k)
+        counts = check_load(routing, E)
+        pl = oracle.plan(counts, R, S)
+        assert pl["n_rep"] == E and pl["exhausted"] == 0
+        assert np.all(pl["load_after"] == T * k // R)
+
+
+def check_single_hot(max_ranks=12):
+    """N = 1, k = 1, every token on expert 0: Q = ceil(L/R); the master keeps
+    Q and ranks 1, 2, ... receive one replica each, all of Q tokens except
+    the last, which takes what is left."""
+    for R in range(2, max_ranks + 1):
+        for L in range(1, 5 * R + 3):
+            counts = np.zeros(R, np.int32)
+            counts[0] = L
+            pl = oracle.plan(counts, R, 1)
+            Q = -(-L // R)
+            assert pl["quota"] == Q
+            n_extra = -(-L // Q) - 1
+            lo, hi = pl["rep_off"][0], pl["rep_off"][1]
+            slots = list(pl["rep_slot"][lo:hi])
+            caps = list(pl["rep_cap"][lo:hi])
+            assert slots == [0] + [2 * r + 1 for r in range(1, n_extra + 1)]
+            last = (L - Q) - Q * (n_extra - 1) if n_extra else None
+            want = [Q] + [Q] * (n_extra - 1) + ([last] if n_extra else [])
+            assert caps == want, (R, L, caps, want)
+            assert pl["exhausted"] == 0
+
+
+def check_invalid_ids():
+    """Ids outside [0, E) are not counted, and are reported."""
+    routing = np.array([[0, 5], [-1, 2], [4, 1], [7, 3]], np.int32)
+    counts, invalid = oracle.load(routing[None], 5)
+    assert list(counts[0]) == [1, 1, 1, 1, 1] and invalid[0] == 3
+    counts, invalid = oracle.load(routing[None], 8)
+    assert invalid[0] == 1 and counts[0].sum() == 7
+
+
+# --------------------------------------------------------------------------
+# brute force: optimal placement over every choice of spare-slot contents
+
+def _min_max_load(counts, hosts, R):
+    """Smallest M such that every expert's tokens can be spread over the
+    ranks hosting it with no rank above M (integral max-flow)."""
+    from scipy.sparse import csr_matrix
+    from scipy.sparse.csgraph import maximum_flow
+
+    E = len(counts)
+    total = int(sum(counts))
+    if total == 0:
+        return 0
+    src, sink = 0, E + R + 1
+
+    def feasible(M):
+        rows, cols, caps = [], [], []
+        for e in range(E):
+            rows.append(src), cols.append(1 + e), caps.append(int(counts[e]))
+            for r in hosts[e]:
+                rows.append(1 + e), cols.append(1 + E + r)
+                caps.append(int(counts[e]))
+        for r in range(R):
+            rows.append(1 + E + r), cols.append(sink), caps.append(int(M))
+        g = csr_matrix((np.array(caps, np.int32), (rows, cols)),
+                       shape=(E + R + 2, E + R + 2))
+        return maximum_flow(g, src, sink).flow_value == total
+
+    lo = -(-total // R)
+    hi = max(sum(int(counts[e]) for e in range(E) if e // (E // R) == r)
+             for r in range(R))
+    while lo < hi:
+        mid = (lo + hi) // 2
+        if feasible(mid):
+            hi = mid
+        else:
+            lo = mid + 1
+    return lo
+
+
+def optimum_max_load(counts, R, S):
+    E = len(counts)
+    N = E // R
+    slots = [(r, i) for r in range(R) for i in range(S)]
+    options = [[-1] + [e for e in range(E) if e // N != r and counts[e] > 0]
+               for (r, _) in slots]
+    best = math.inf
+    for combo in itertools.product(*options):
+        hosts = [{e // N} for e in range(E)]
+        for (r, _), e in zip(slots, combo):
+            if e >= 0:
+                hosts[e].add(r)
+        best = min(best, _min_max_load(counts, hosts, R))
+    return best
+
+
+def check_against_optimum(counts, R, S):
+    """Returns greedy / optimum. The greedy plan is one of the placements
+    enumerated, so the optimum can never exceed it; every placement has a
+    rank at or above ceil(total / R) = Q, so when slots suffice the greedy
+    (which then ends with every rank <= Q) is optimal."""
+    pl = check_plan(counts, R, S)
+    greedy = int(pl["load_after"].max(initial=0))
+    opt = optimum_max_load(list(counts), R, S)
+    assert opt <= greedy, "greedy beats the exhaustive optimum"
+    assert opt >= pl["quota"], "no placement beats the quota"
+    if not pl["exhausted"]:
+        assert greedy == opt == pl["quota"]
+    return greedy / opt if opt else 1.0

@@ -1,0 +1,68 @@
+"""The CPU oracle checked against hand-worked cases, closed forms, library
+routines and brute force (see ``pins.py``)."""
+import numpy as np
+import pytest
+
+import pins
+
+
+@pytest.mark.parametrize("case", pins.golden_cases(), ids=lambda g: g["name"])
+def test_golden(case):
+    pins.check_golden(case)
+
+
+def test_invariants_random():
+    rng = np.random.default_rng(20260602)
+    for _ in range(1500):
+        pins.check_instance(*pins.random_instance(rng))
+
+
+def test_invariants_larger():
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        routing, E, R, S = pins.random_instance(
+            rng, max_ranks=32, max_native=8, max_spare=3, max_tokens=2000,
+            max_k=8)
+        pins.check_instance(routing, E, R, S)
+
+
+def test_no_spares():
+    pins.check_no_spares(np.random.default_rng(1))
+
+
+def test_one_rank():
+    pins.check_one_rank(np.random.default_rng(2))
+
+
+def test_balanced():
+    pins.check_balanced()
+
+
+def test_single_hot_expert():
+    pins.check_single_hot()
+
+
+def test_invalid_ids():
+    pins.check_invalid_ids()
+
+
+def test_brute_force_optimum():
+    """Exhaustive optimum on tiny instances: greedy == optimum == Q whenever
+    slots suffice; otherwise the optimum never exceeds greedy. The worst
+    observed greedy/optimum ratio is reported."""
+    rng = np.random.default_rng(3)
+    worst = 1.0
+    n_exhausted = 0
+    for _ in range(60):
+        R = int(rng.integers(2, 4))
+        N = int(rng.integers(1, 3))
+        S = int(rng.integers(1, 3 if R == 2 else 2))
+        E = R * N
+        counts = rng.integers(0, 9, size=E).astype(np.int32)
+        counts[rng.integers(0, E)] += int(rng.integers(0, 12))
+        ratio = pins.check_against_optimum(counts, R, S)
+        worst = max(worst, ratio)
+        n_exhausted += ratio > 1.0
+    print(f"greedy/optimum worst {worst:.3f}; above optimum in "
+          f"{n_exhausted}/60")
+    assert worst <= 2.0
