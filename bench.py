@@ -1,0 +1,337 @@
+"""Benchmark of the per-layer MoE expert-rebalancing path on one MI355X.
+
+One step is one rebalance of the DeepSeek-V3-scale routing workload: 58 MoE
+layers batched, E=256 experts, top-k=8, R=64 simulated expert-parallel ranks
+(4 native + 1 spare slot each), T=65536 tokens per layer; load -> plan ->
+reroute (physical routing, per-rank counts, stable dispatch permutation and
+its inverse). Inputs are seeded synthetic routing, resident in HBM before
+timing. ``value`` is routed assignments per second over the whole job.
+
+The same run also measures, each on its own workload: the large-EP
+rebalance latency (R=256, T=262144, one layer); replica weight sync and
+gradient reduction on 32 DeepSeek-V3 experts with 64 replica buffers (GB/s
+and fraction of the 8 TB/s HBM peak, algorithmic bytes); the dispatch gather
+of one pipeline microbatch ([131072, 4096] bf16 -> [1048576, 4096]); and the
+oracle on the host as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+       [--no-cpu] [--only rebalance|stream|gather|large_ep]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+METRIC = ("µs per rebalance + assignments/s at E=256,k=8; "
+          "GB/s (%HBM) sync/reduce")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+class Rebalance:
+    """Preallocated buffers and the three ABI calls of one rebalance."""
+
+    def __init__(self, ue, cfg, routing, dev):
+        import torch
+        self.ue = ue
+        L, T, k = routing.shape
+        self.ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk,
+                              T, L, device=dev)
+        self.routing = routing
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.counts = torch.empty((L, cfg.experts), **i32)
+        self.placement = self.ctx.new_placement(L)
+        self.out = dict(phys=torch.empty((L, T, k), **i32),
+                        rank_counts=torch.empty((L, cfg.ranks), **i32),
+                        perm=torch.empty((L, T * k), **i32),
+                        inv_perm=torch.empty((L, T * k), **i32),
+                        faults=torch.empty((L,), **i32))
+
+    def load(self):
+        self.ue.ue_load(self.ctx, self.routing, self.counts)
+
+    def plan(self):
+        self.ue.ue_plan(self.ctx, self.counts, self.placement)
+
+    def reroute(self):
+        self.ue.ue_reroute(self.ctx, self.routing, self.placement, **self.out)
+
+    def step(self):
+        self.load()
+        self.plan()
+        self.reroute()
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = events(2)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps        # ms per step
+
+
+def phase_times(rb, steps):
+    """Per-kernel durations from events recorded around each launch on the
+    launch stream (torch's current stream), averaged over ``steps``."""
+    import torch
+    ev = [events(4) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        rb.load()
+        ev[i][1].record()
+        rb.plan()
+        ev[i][2].record()
+        rb.reroute()
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    t = {"k_load": [], "k_plan": [], "k_reroute": []}
+    for e in ev:
+        t["k_load"].append(e[0].elapsed_time(e[1]))
+        t["k_plan"].append(e[1].elapsed_time(e[2]))
+        t["k_reroute"].append(e[2].elapsed_time(e[3]))
+    return {k: statistics.mean(v) for k, v in t.items()}
+
+
+def imbalance(rb, cfg):
+    import numpy as np
+    f = rb.ctx.placement_fields(rb.placement)
+    mean = cfg.assignments / cfg.ranks
+    before = f["load_before"].max(dim=1).values.cpu().numpy() / mean
+    after = f["load_after"].max(dim=1).values.cpu().numpy() / mean
+    exh = int(f["exhausted"].sum())
+    return {"before_min_med_max": [round(float(np.min(before)), 4),
+                                   round(float(np.median(before)), 4),
+                                   round(float(np.max(before)), 4)],
+            "after_min_med_max": [round(float(np.min(after)), 4),
+                                  round(float(np.median(after)), 4),
+                                  round(float(np.max(after)), 4)],
+            "layers_exhausted": exh, "layers": int(f["exhausted"].numel())}
+
+
+def bench_rebalance(ue, W, dev, steps, warmup):
+    import torch
+    cfg = W.CONFIGS["dsv3"]
+    log("dsv3: generating routing on the device")
+    routing = W.make_routing(cfg, device=dev)
+    rb = Rebalance(ue, cfg, routing, dev)
+    rb.step()
+    torch.cuda.synchronize()
+    assert int(rb.out["faults"].sum()) == 0
+    log(f"dsv3: timing {steps} steps after {warmup} warmup")
+    ms = time_steps(rb.step, steps, warmup)
+    phases = phase_times(rb, max(steps, 10))
+    single = Rebalance(ue, cfg, routing[:1].contiguous(), dev)
+    ms_one = time_steps(single.step, 50, 10)
+    return cfg, rb, ms, phases, ms_one
+
+
+def bench_large_ep(ue, W, dev):
+    import torch
+    cfg = W.CONFIGS["large_ep"]
+    routing = W.make_routing(cfg, device=dev)
+    rb = Rebalance(ue, cfg, routing, dev)
+    for _ in range(20):
+        rb.step()
+    torch.cuda.synchronize()
+    reps = 200
+    ev = [events(2) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        rb.step()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(e[0].elapsed_time(e[1]) * 1000.0 for e in ev)
+    phases = phase_times(rb, 50)
+    return {"workload": "large_ep: E=256 k=8 R=256 (1 native + 1 spare) "
+                        "T=262144, 1 layer",
+            "us_per_rebalance_p10_p50_p90": [round(t[reps // 10], 2),
+                                             round(t[reps // 2], 2),
+                                             round(t[9 * reps // 10], 2)],
+            "assignments_per_s": cfg.assignments / (t[reps // 2] * 1e-6),
+            "kernel_us": {k: round(v * 1000.0, 2) for k, v in phases.items()},
+            "imbalance": imbalance(rb, cfg)}
+
+
+def bench_stream(ue, W, dev):
+    import torch
+    log("stream: allocating 32 experts x 3 matrices, 64 replica buffers")
+    sb = W.make_stream_buffers(device=dev)
+    ctx = ue.Context(32, 1, 0, 1, 1, device=dev)
+    M = sb.master_w.shape[1]
+    ctx.register_experts([sb.elems] * M, sb.tables("master_w"),
+                         sb.tables("master_g"), sb.tables("spare_w"),
+                         sb.tables("spare_g"))
+    rep_off = torch.tensor(sb.rep_off, dtype=torch.int32, device=dev)
+    rep_buf = torch.tensor(sb.rep_buf, dtype=torch.int32, device=dev)
+    fan = [sb.rep_off[e + 1] - sb.rep_off[e] - 1 for e in range(32)]
+    mat_bytes_w = sb.elems * 2 * M
+    mat_bytes_g = sb.elems * 4 * M
+    sync_bytes = sum((1 + f) * mat_bytes_w for f in fan if f)
+    red_bytes = sum((2 + f) * mat_bytes_g for f in fan if f)
+    res = {}
+    for name, fn, nbytes in (
+            ("weight_sync", lambda: ctx.weight_sync(rep_off, rep_buf),
+             sync_bytes),
+            ("grad_reduce", lambda: ctx.grad_reduce(rep_off, rep_buf),
+             red_bytes)):
+        ms = time_steps(fn, 30, 5)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"ms": round(ms, 4), "bytes": nbytes,
+                     "GB_per_s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    # plain device copy of the same number of bytes for reference
+    src = sb.spare_g.view(-1)
+    dst = torch.empty_like(src)
+    ms = time_steps(lambda: dst.copy_(src), 20, 3)
+    res["torch_copy_reference"] = {
+        "bytes": 2 * src.numel() * 4,
+        "GB_per_s": round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)}
+    del sb, src, dst
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_gather(ue, W, dev):
+    import torch
+    cfg = W.CONFIGS["pipeline"]
+    routing = W.make_routing(cfg, device=dev, layers=1)
+    rb = Rebalance(ue, cfg, routing, dev)
+    rb.step()
+    x = W.make_activations(cfg.tokens, cfg.hidden, 0, device=dev)
+    out = torch.empty((cfg.assignments, cfg.hidden), dtype=torch.bfloat16,
+                      device=dev)
+    inv = rb.out["inv_perm"][0]
+    ms = time_steps(lambda: rb.ctx.gather_rows(x, inv, out=out), 20, 3)
+    nbytes = 2 * cfg.hidden * (cfg.tokens + cfg.assignments)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": "pipeline microbatch: [131072, 4096] bf16 -> "
+                       "[1048576, 4096] by the dispatch permutation",
+           "ms": round(ms, 4), "bytes": nbytes, "GB_per_s": round(gbs, 1),
+           "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del out, x
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(W, routing_layers=4):
+    """The oracle as it stands on a bounded sample of the same workload:
+    the first ``routing_layers`` layers of the dsv3 routing (same seeds),
+    load + plan + reroute per layer, single thread."""
+    import numpy as np
+    import oracle
+    cfg = W.CONFIGS["dsv3"]
+    r = W.make_routing(cfg, device="cpu", layers=routing_layers).numpy()
+    t0 = time.perf_counter()
+    oracle.rebalance(r, cfg.experts, cfg.ranks, cfg.spare)
+    dt = time.perf_counter() - t0
+    n = routing_layers * cfg.assignments
+    return {"value": n / dt, "unit": "assignments/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{routing_layers} of 58 dsv3 layers "
+                      f"({n} assignments), load+plan+reroute, "
+                      f"{dt:.2f} s on one host thread of {os.cpu_count()}",
+            "seconds": round(dt, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} given); "
+              "the simulated expert-parallel ranks are partitions of one "
+              "device's routing", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_expert_load_ue_amd as ue
+    from moe_expert_load_ue_amd import workloads as W
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cfg, rb, ms, phases, ms_one = bench_rebalance(ue, W, dev, args.steps,
+                                                  args.warmup)
+    L = cfg.layers
+    n_assign = L * cfg.assignments
+    value = n_assign / (ms * 1e-3)
+    # dominant kernel: the reroute pass; algorithmic bytes per assignment:
+    # read the id (4) + write phys, perm and inv_perm (12)
+    rr_ms = phases["k_reroute"]
+    rr_bytes = 16 * n_assign
+    achieved = rr_bytes / (rr_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "assignments/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": "dsv3 routing: E=256, k=8, R=64 "
+                               "(4 native + 1 spare), T=65536, 58 layers "
+                               "batched; load+plan+reroute",
+                   "layers": L, "tokens": cfg.tokens, "experts": cfg.experts,
+                   "topk": cfg.topk, "ranks": cfg.ranks,
+                   "spare_per_rank": cfg.spare},
+        "us_per_rebalance": {"dsv3_58_layers": round(ms * 1000.0, 2),
+                             "dsv3_per_layer_batched":
+                                 round(ms * 1000.0 / L, 3),
+                             "dsv3_single_layer": round(ms_one * 1000.0, 2)},
+        "kernel_us": {k: round(v * 1000.0, 2) for k, v in phases.items()},
+        "roofline": {"bound": "hbm", "kernel": "k_reroute",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": rr_bytes},
+        "imbalance": imbalance(rb, cfg),
+    }
+    del rb
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        log("large_ep")
+        line["large_ep"] = bench_large_ep(ue, W, dev)
+        log("stream")
+        line["stream"] = bench_stream(ue, W, dev)
+        log("gather")
+        line["gather"] = bench_gather(ue, W, dev)
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(W, args.cpu_layers)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * ue.h -- C ABI of the MI355X (gfx950) per-layer MoE expert-rebalancing
+ * library (libue.so).
+ *
+ * The library implements the data-parallel hot path of an exact-load,
+ * real-time expert balancer: count each expert's load from the post-gating
+ * routing, plan replicas of hot experts onto spare slots of expert-parallel
+ * ranks under a quota, expand logical expert ids to physical replica ids
+ * with the stable dispatch permutation, copy master weights into replicas,
+ * and sum replica gradients into the masters.
+ *
+ * Sources: the gitdiagram page "How dots-infra/ultraep works" (summary and
+ * connection list: the framework registers expert pointers and passes
+ * routing; the manager profiles loads, updates placement, syncs weights,
+ * reroutes tokens and reduces gradients); the UltraEP news write-up
+ * ("UltraEP ot Xiaohongshu: balansirovka MoE-ekspertov za 300 mks"), section
+ * on how balancing in 300 microseconds works (quota-driven scheduler, every
+ * microbatch and layer, right after gating; persistent tile streaming of
+ * expert state); the UltraEP abstract, arXiv 2606.04101 ("exact-load,
+ * real-time balancer").
+ *
+ * Conventions for every call:
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device (e.g. torch CUDA tensors on ROCm). Host pointers are
+ *    read before the call returns and not kept, unless stated.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *    Every call is asynchronous and stream-ordered; results are valid once
+ *    the stream reaches that point. No call synchronises with the host.
+ *  - The return value is UE_OK (0) or a negative ue_status. Every argument
+ *    is validated before anything is launched or written: a refused call
+ *    leaves all outputs untouched. The reason is in ue_last_error().
+ *  - A context is not thread-safe: use one context per concurrent stream.
+ *    Calls on one context must not overlap in time on different streams.
+ *  - All shapes are int32; the number of assignments per layer, T*k, must
+ *    stay below 2^30.
+ */
+#ifndef UE_H
+#define UE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ue_status {
+    UE_OK = 0,
+    UE_EINVAL = -1,       /* null pointer, bad alignment, bad value       */
+    UE_ESHAPE = -2,       /* dimensions outside what the context allows   */
+    UE_ENOMEM = -3,       /* device allocation failed                     */
+    UE_EHIP = -4,         /* a HIP runtime call failed                    */
+    UE_EUNSUPPORTED = -5, /* configuration outside what the kernels cover */
+    UE_ESTATE = -6        /* call made in the wrong state (e.g. unregistered) */
+} ue_status;
+
+/* Shape of the simulated expert-parallel machine and the size limits of
+ * one context.
+ *   num_experts E      logical experts, 1..1024
+ *   num_ranks R        expert-parallel ranks, divides E; N = E / R experts
+ *                      live natively on each rank (expert e on rank e / N,
+ *                      native slot e mod N)
+ *   spare_per_rank S   empty replica slots per rank, 0..64; physical slot id
+ *                      p = r*(N+S) + s, natives s < N, spares N <= s < N+S;
+ *                      P = R*(N+S) <= 4096
+ *   topk k             experts per token, 1..E
+ *   max_tokens         largest T of any call (T*k < 2^30)
+ *   max_layers         largest L (layers or microbatches) of any call      */
+typedef struct ue_config {
+    int32_t num_experts;
+    int32_t num_ranks;
+    int32_t spare_per_rank;
+    int32_t topk;
+    int32_t max_tokens;
+    int32_t max_layers;
+} ue_config;
+
+typedef struct ue_ctx ue_ctx;
+
+/* Creates a context on the current HIP device and allocates its device
+ * workspace once (per-tile scan state and counters, sized from the
+ * limits). *out is set only on success. Errors: UE_EINVAL (null),
+ * UE_EUNSUPPORTED (limits above), UE_ENOMEM, UE_EHIP. */
+int ue_create(const ue_config *cfg, ue_ctx **out);
+
+/* Frees the workspace and the context. Registered expert memory is the
+ * caller's and is not freed. Waits for the device to finish pending work
+ * of the context. NULL is accepted. */
+void ue_destroy(ue_ctx *ctx);
+
+/* Last error message of the context ("" if none); valid until the next
+ * call on the context. */
+const char *ue_last_error(const ue_ctx *ctx);
+
+/* Short name of a status code. */
+const char *ue_status_name(int status);
+
+/* ---------------------------------------------------------------------
+ * Placement block: one per layer, int32 words at fixed offsets.
+ * ue_get_placement_layout() reports the offsets (in int32 words from the start
+ * of a layer's block) and the block size. Fields:
+ *   quota        Q = ceil(sum(counts) / R)
+ *   exhausted    1 if overloaded ranks kept excess because no rank had a
+ *                free spare slot and load < Q, else 0
+ *   residual     sum over ranks of max(0, load_after - Q)
+ *   n_rep        entries used in the replica table (masters included)
+ *   rep_off[E+1] replica table offsets per expert (CSR)
+ *   rep_slot[P]  physical slot of each replica; per expert the master
+ *                (native slot) first, then replicas in creation order;
+ *                entries >= n_rep hold -1
+ *   rep_cap[P]   assignments routed to each replica (0 beyond n_rep)
+ *   slot_expert[P] logical expert held by each slot, -1 for an unused spare
+ *   slot_cap[P]  assignments routed to each slot (0 if unused)
+ *   slot_off[P+1] exclusive prefix sum of slot_cap: where each slot's
+ *                assignments start in the dispatch permutation
+ *   load_before[R], load_after[R]  rank loads under the native placement
+ *                and after the plan                                        */
+typedef struct ue_placement_layout {
+    int32_t words;          /* int32 words per layer block */
+    int32_t quota, exhausted, residual, n_rep;
+    int32_t rep_off, rep_slot, rep_cap;
+    int32_t slot_expert, slot_cap, slot_off;
+    int32_t load_before, load_after;
+} ue_placement_layout;
+
+int ue_get_placement_layout(const ue_ctx *ctx, ue_placement_layout *out);
+
+/* Bytes of one layer's placement block (words * 4). 0 for a NULL ctx. */
+size_t ue_placement_bytes(const ue_ctx *ctx);
+
+/* ---------------------------------------------------------------------
+ * Exact per-expert load ("Load computation"; the balancer is exact-load).
+ *   routing  device, int32 [L, T, k], logical expert ids, flat assignment
+ *            order a = t*k + j within a layer
+ *   counts   device, int32 [L, E] out: counts[l][e] = #{a : routing = e}
+ *   invalid  device, int32 [L] out, may be NULL: ids outside [0, E) per
+ *            layer (such ids are not counted)
+ * L in 1..max_layers, T in 0..max_tokens. */
+int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
+            int32_t *counts, int32_t *invalid, void *stream);
+
+/* Quota replica plan ("Placement planning", the quota-driven scheduler),
+ * per layer, from counts alone:
+ *   Q = ceil(sum(counts)/R); experts of ranks whose load exceeds Q are
+ *   visited heaviest first (count desc, id asc); each spills its rank's
+ *   excess, chunk by chunk, into the lowest free spare slot of the
+ *   least-loaded rank (ties: lowest id) that has a free spare slot and load
+ *   < Q; chunk = min(source excess, expert remainder, destination
+ *   headroom); with no such rank the plan stops (exhausted = 1).
+ *   counts     device, int32 [L, E] (e.g. from ue_load)
+ *   placement  device, L blocks of ue_placement_bytes() bytes, out
+ * Fully on the device; nothing returns to the host. */
+int ue_plan(ue_ctx *ctx, const int32_t *counts, int32_t L, void *placement,
+            void *stream);
+
+/* Routing expansion and dispatch layout ("Routing expansion": physical
+ * routing for token dispatch). For every assignment a of layer l with
+ * logical expert e, j = number of earlier assignments of e in flat order;
+ * the replica of e whose capacity prefix (master first) covers j gets it:
+ *   phys        device, int32 [L, T, k] out: physical slot id
+ *   rank_counts device, int32 [L, R] out: assignments per rank, counted
+ *               from phys
+ *   perm        device, int32 [L, T*k] out: perm[pos] = a, the stable sort
+ *               of assignments by physical slot (pos = slot_off[p] + j -
+ *               prefix)
+ *   inv_perm    device, int32 [L, T*k] out, may be NULL: inv_perm[a] = pos
+ *   faults      device, int32 [L] out, may be NULL: assignments that could
+ *               not be placed (id outside [0, E), or beyond the plan's
+ *               capacity for its expert); their phys and inv_perm are -1
+ * The placement must come from ue_plan on the counts of this routing; with
+ * faults > 0 perm is unspecified. */
+int ue_reroute(ue_ctx *ctx, const int32_t *routing, const void *placement,
+               int32_t L, int32_t T, int32_t *phys, int32_t *rank_counts,
+               int32_t *perm, int32_t *inv_perm, int32_t *faults,
+               void *stream);
+
+/* ---------------------------------------------------------------------
+ * Expert state ("registers expert pointers"). Stores device pointers to
+ * n_experts master experts and n_buffers replica buffers, each made of
+ * n_mats matrices; matrix m has mat_elems[m] elements in every expert and
+ * buffer. Weights are bf16 (2 bytes per element), gradients fp32.
+ *   mat_elems  host, int64 [n_mats]
+ *   master_w   host array of device pointers [n_experts * n_mats], index
+ *              e*n_mats + m; master_g likewise (float*)
+ *   spare_w    host array of device pointers [n_buffers * n_mats];
+ *              spare_g likewise
+ * Every pointer must be 16-byte aligned. The memory stays the caller's;
+ * the context keeps the pointers (copied to the device) until the next
+ * registration or ue_destroy. n_mats in 1..16. Any of master_g/spare_g
+ * may be NULL (then ue_grad_reduce is refused), any of master_w/spare_w
+ * may be NULL (then ue_weight_sync is refused). */
+int ue_register_experts(ue_ctx *ctx, int32_t n_experts, int32_t n_mats,
+                        const int64_t *mat_elems, void *const *master_w,
+                        float *const *master_g, int32_t n_buffers,
+                        void *const *spare_w, float *const *spare_g);
+
+/* Replica weight sync ("Replica weight sync": replicas receive the master
+ * weights before expert compute). Replica table as device CSR:
+ *   rep_off  device, int32 [n_experts + 1]
+ *   rep_buf  device, int32 [rep_off[n_experts]]; for expert e the entries
+ *            rep_off[e] .. rep_off[e+1]-1: the first stands for the master
+ *            and is ignored, the others are replica buffer indices
+ * Every matrix of every replica becomes a bitwise copy of its master's.
+ * The master is read once per tile and written to all its replicas.
+ * n_experts must not exceed the registered count; buffer indices must be
+ * < n_buffers (entries outside are skipped). Replica buffers must not
+ * alias masters or each other. */
+int ue_weight_sync(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
+                   int32_t n_experts, void *stream);
+
+/* Replica gradient reduction ("Replica gradient reduction": replica
+ * gradients are summed into master gradients during backward). Same CSR as
+ * ue_weight_sync. Per element, in fp32 with round-to-nearest-even and no
+ * reassociation: g = master; g += replica_1; g += replica_2; ...;
+ * master = g. Replica gradients are left unchanged. */
+int ue_grad_reduce(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
+                   int32_t n_experts, void *stream);
+
+/* Token dispatch into physical-expert order on one device: out[pos, :] =
+ * x[perm[pos] div k, :], done source-major through the inverse
+ * permutation (every token row is read once and written to its k
+ * positions).
+ *   x        device, bf16 [T, H], 16-byte aligned rows (H % 8 == 0)
+ *   inv_perm device, int32 [T*k] (from ue_reroute, one layer)
+ *   out      device, bf16 [T*k, H]
+ * Positions outside [0, T*k) are skipped. */
+int ue_gather_rows(ue_ctx *ctx, const void *x, const int32_t *inv_perm,
+                   int32_t T, int32_t k, int32_t H, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UE_H */

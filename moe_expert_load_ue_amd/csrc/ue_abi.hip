@@ -1,0 +1,400 @@
+// C ABI of libue: context, argument validation and kernel launches.
+//
+// Every entry point validates all of its host-visible arguments before it
+// launches or writes anything, so a refused call leaves every output as it
+// was; the reason goes to ue_last_error(). Device-side conditions (an
+// exhausted plan, ids out of range, assignments beyond a plan's capacity)
+// are results, reported in the outputs, not errors.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "ue_internal.h"
+
+namespace {
+
+int fail(ue_ctx *c, int code, const char *fmt, ...)
+    __attribute__((format(printf, 3, 4)));
+
+int fail(ue_ctx *c, int code, const char *fmt, ...) {
+    if (c) {
+        char buf[512];
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(buf, sizeof(buf), fmt, ap);
+        va_end(ap);
+        c->err = buf;
+    }
+    return code;
+}
+
+int hip_fail(ue_ctx *c, hipError_t e, const char *what) {
+    return fail(c, UE_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int bits_for(int n) {   // smallest b with (1 << b) >= n
+    int b = 0;
+    while ((1 << b) < n) ++b;
+    return b;
+}
+
+bool aligned(const void *p, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ue_status_name(int status) {
+    switch (status) {
+        case UE_OK: return "UE_OK";
+        case UE_EINVAL: return "UE_EINVAL";
+        case UE_ESHAPE: return "UE_ESHAPE";
+        case UE_ENOMEM: return "UE_ENOMEM";
+        case UE_EHIP: return "UE_EHIP";
+        case UE_EUNSUPPORTED: return "UE_EUNSUPPORTED";
+        case UE_ESTATE: return "UE_ESTATE";
+        default: return "UE_UNKNOWN";
+    }
+}
+
+const char *ue_last_error(const ue_ctx *ctx) {
+    return ctx ? ctx->err.c_str() : "null context";
+}
+
+int ue_create(const ue_config *cfg, ue_ctx **out) {
+    if (!cfg || !out) return UE_EINVAL;
+    const int E = cfg->num_experts, R = cfg->num_ranks,
+              S = cfg->spare_per_rank, k = cfg->topk;
+    if (E < 1 || E > ue::kMaxExperts || R < 1 || E % R != 0 || S < 0 ||
+        S > ue::kMaxSpare || k < 1 || k > E || cfg->max_tokens < 0 ||
+        cfg->max_layers < 1)
+        return UE_EUNSUPPORTED;
+    const int N = E / R, NS = N + S;
+    const int64_t P = static_cast<int64_t>(R) * NS;
+    const int64_t A = static_cast<int64_t>(cfg->max_tokens) * k;
+    if (P > ue::kMaxSlots || A >= (int64_t(1) << 30)) return UE_EUNSUPPORTED;
+
+    ue_ctx *c = new (std::nothrow) ue_ctx();
+    if (!c) return UE_ENOMEM;
+    c->cfg = *cfg;
+    c->E = E;
+    c->R = R;
+    c->S = S;
+    c->N = N;
+    c->NS = NS;
+    c->P = static_cast<int>(P);
+    c->k = k;
+    c->ebits = bits_for(E);
+    c->rbits = bits_for(R);
+
+    hipError_t he = hipGetDevice(&c->device);
+    if (he != hipSuccess) {
+        int rc = hip_fail(c, he, "hipGetDevice");
+        delete c;
+        return rc;
+    }
+    hipDeviceProp_t prop;
+    he = hipGetDeviceProperties(&prop, c->device);
+    if (he != hipSuccess) {
+        delete c;
+        return UE_EHIP;
+    }
+    c->num_cu = prop.multiProcessorCount;
+
+    // Placement block layout (int32 words).
+    ue_placement_layout &l = c->lay;
+    int w = 0;
+    l.quota = w++;
+    l.exhausted = w++;
+    l.residual = w++;
+    l.n_rep = w++;
+    l.rep_off = w; w += E + 1;
+    l.rep_slot = w; w += c->P;
+    l.rep_cap = w; w += c->P;
+    l.slot_expert = w; w += c->P;
+    l.slot_cap = w; w += c->P;
+    l.slot_off = w; w += c->P + 1;
+    l.load_before = w; w += R;
+    l.load_after = w; w += R;
+    l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
+
+    c->plan_lds = ue::plan_lds_bytes(E, R, c->P);
+    c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P);
+    const size_t lds_cap = prop.sharedMemPerBlock;
+    if (c->plan_lds + 64 > lds_cap || c->reroute_lds + 64 > lds_cap) {
+        delete c;
+        return UE_EUNSUPPORTED;
+    }
+    if (c->plan_lds > 65536 && ue::plan_prepare(c->plan_lds) != hipSuccess) {
+        delete c;
+        return UE_EUNSUPPORTED;
+    }
+
+    const int Lmax = cfg->max_layers;
+    int64_t rr_tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
+    if (rr_tiles < 1) rr_tiles = 1;
+    c->max_rr_tiles = static_cast<int>(rr_tiles);
+
+    // Workspace carve-up, each piece 256-byte aligned.
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = round_up(off + bytes, 256);
+        return o;
+    };
+    const size_t o_load_acc = take(sizeof(int32_t) * Lmax * E);
+    const size_t o_load_inv = take(sizeof(int32_t) * Lmax);
+    const size_t o_load_done = take(sizeof(uint32_t) * Lmax);
+    const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
+    const size_t o_ticket = take(sizeof(uint32_t) * Lmax);
+    const size_t o_done = take(sizeof(uint32_t) * Lmax);
+    const size_t o_epoch = take(sizeof(uint32_t) * Lmax);
+    const size_t o_rank = take(sizeof(int32_t) * Lmax * R);
+    const size_t o_fault = take(sizeof(int32_t) * Lmax);
+    c->ws_bytes = off;
+    he = hipMalloc(&c->ws, c->ws_bytes);
+    if (he != hipSuccess) {
+        delete c;
+        return UE_ENOMEM;
+    }
+    he = hipMemset(c->ws, 0, c->ws_bytes);
+    if (he == hipSuccess) he = hipDeviceSynchronize();
+    if (he != hipSuccess) {
+        (void)hipFree(c->ws);
+        delete c;
+        return UE_EHIP;
+    }
+    char *b = static_cast<char *>(c->ws);
+    c->load_acc = reinterpret_cast<int32_t *>(b + o_load_acc);
+    c->load_inv = reinterpret_cast<int32_t *>(b + o_load_inv);
+    c->load_done = reinterpret_cast<uint32_t *>(b + o_load_done);
+    c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
+    c->rr_ticket = reinterpret_cast<uint32_t *>(b + o_ticket);
+    c->rr_done = reinterpret_cast<uint32_t *>(b + o_done);
+    c->rr_epoch = reinterpret_cast<uint32_t *>(b + o_epoch);
+    c->rr_rank_acc = reinterpret_cast<int32_t *>(b + o_rank);
+    c->rr_fault_acc = reinterpret_cast<int32_t *>(b + o_fault);
+    *out = c;
+    return UE_OK;
+}
+
+void ue_destroy(ue_ctx *ctx) {
+    if (!ctx) return;
+    (void)hipDeviceSynchronize();
+    if (ctx->ws) (void)hipFree(ctx->ws);
+    if (ctx->reg_tables) (void)hipFree(ctx->reg_tables);
+    delete ctx;
+}
+
+int ue_get_placement_layout(const ue_ctx *ctx, ue_placement_layout *out) {
+    if (!ctx || !out) return UE_EINVAL;
+    *out = ctx->lay;
+    return UE_OK;
+}
+
+size_t ue_placement_bytes(const ue_ctx *ctx) {
+    return ctx ? static_cast<size_t>(ctx->lay.words) * sizeof(int32_t) : 0;
+}
+
+static int check_LT(ue_ctx *c, int32_t L, int32_t T) {
+    if (L < 1 || L > c->cfg.max_layers)
+        return fail(c, UE_ESHAPE, "L=%d outside 1..%d", L, c->cfg.max_layers);
+    if (T < 0 || T > c->cfg.max_tokens)
+        return fail(c, UE_ESHAPE, "T=%d outside 0..%d", T, c->cfg.max_tokens);
+    return UE_OK;
+}
+
+int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
+            int32_t *counts, int32_t *invalid, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (int rc = check_LT(ctx, L, T)) return rc;
+    if ((!routing && T > 0) || !counts)
+        return fail(ctx, UE_EINVAL, "ue_load: null routing or counts");
+    if (!aligned(routing, 4) || !aligned(counts, 4) || !aligned(invalid, 4))
+        return fail(ctx, UE_EINVAL, "ue_load: int32 arrays must be 4-byte aligned");
+    const int64_t A = static_cast<int64_t>(T) * ctx->k;
+    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid,
+                                    static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_load launch");
+}
+
+int ue_plan(ue_ctx *ctx, const int32_t *counts, int32_t L, void *placement,
+            void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (L < 1 || L > ctx->cfg.max_layers)
+        return fail(ctx, UE_ESHAPE, "L=%d outside 1..%d", L, ctx->cfg.max_layers);
+    if (!counts || !placement)
+        return fail(ctx, UE_EINVAL, "ue_plan: null counts or placement");
+    if (!aligned(counts, 4) || !aligned(placement, 4))
+        return fail(ctx, UE_EINVAL, "ue_plan: arrays must be 4-byte aligned");
+    hipError_t he = ue::launch_plan(*ctx, counts, L,
+                                    static_cast<int32_t *>(placement),
+                                    static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_plan launch");
+}
+
+int ue_reroute(ue_ctx *ctx, const int32_t *routing, const void *placement,
+               int32_t L, int32_t T, int32_t *phys, int32_t *rank_counts,
+               int32_t *perm, int32_t *inv_perm, int32_t *faults,
+               void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (int rc = check_LT(ctx, L, T)) return rc;
+    if (!placement || !rank_counts || (T > 0 && (!routing || !phys || !perm)))
+        return fail(ctx, UE_EINVAL, "ue_reroute: null required pointer");
+    if (!aligned(routing, 4) || !aligned(placement, 4) || !aligned(phys, 4) ||
+        !aligned(rank_counts, 4) || !aligned(perm, 4) ||
+        !aligned(inv_perm, 4) || !aligned(faults, 4))
+        return fail(ctx, UE_EINVAL, "ue_reroute: arrays must be 4-byte aligned");
+    const int64_t A = static_cast<int64_t>(T) * ctx->k;
+    hipError_t he = ue::launch_reroute(
+        *ctx, routing, static_cast<const int32_t *>(placement), L, A, phys,
+        rank_counts, perm, inv_perm, faults, static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_reroute launch");
+}
+
+int ue_register_experts(ue_ctx *ctx, int32_t n_experts, int32_t n_mats,
+                        const int64_t *mat_elems, void *const *master_w,
+                        float *const *master_g, int32_t n_buffers,
+                        void *const *spare_w, float *const *spare_g) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (n_experts < 1 || n_mats < 1 || n_mats > ue::kMaxMats ||
+        n_buffers < 0 || !mat_elems)
+        return fail(ctx, UE_ESHAPE, "ue_register_experts: bad counts");
+    const bool has_w = master_w && (spare_w || n_buffers == 0);
+    const bool has_g = master_g && (spare_g || n_buffers == 0);
+    if (!has_w && !has_g)
+        return fail(ctx, UE_EINVAL, "ue_register_experts: no weights or gradients");
+    for (int m = 0; m < n_mats; ++m)
+        if (mat_elems[m] < 0)
+            return fail(ctx, UE_EINVAL, "ue_register_experts: negative size");
+    const int64_t nm = static_cast<int64_t>(n_experts) * n_mats;
+    const int64_t nb = static_cast<int64_t>(n_buffers) * n_mats;
+    for (int64_t i = 0; i < nm; ++i) {
+        if (has_w && (!master_w[i] || !aligned(master_w[i], 16)))
+            return fail(ctx, UE_EINVAL, "master weight %lld null or unaligned",
+                        static_cast<long long>(i));
+        if (has_g && (!master_g[i] || !aligned(master_g[i], 16)))
+            return fail(ctx, UE_EINVAL, "master grad %lld null or unaligned",
+                        static_cast<long long>(i));
+    }
+    for (int64_t i = 0; i < nb; ++i) {
+        if (has_w && (!spare_w[i] || !aligned(spare_w[i], 16)))
+            return fail(ctx, UE_EINVAL, "replica weight %lld null or unaligned",
+                        static_cast<long long>(i));
+        if (has_g && (!spare_g[i] || !aligned(spare_g[i], 16)))
+            return fail(ctx, UE_EINVAL, "replica grad %lld null or unaligned",
+                        static_cast<long long>(i));
+    }
+    const size_t bytes = sizeof(void *) * static_cast<size_t>(2 * nm + 2 * nb + 4);
+    void *tables = nullptr;
+    hipError_t he = hipMalloc(&tables, bytes);
+    if (he != hipSuccess) return fail(ctx, UE_ENOMEM, "pointer tables");
+    void **host = new (std::nothrow) void *[2 * nm + 2 * nb + 4];
+    if (!host) {
+        (void)hipFree(tables);
+        return fail(ctx, UE_ENOMEM, "pointer tables (host)");
+    }
+    for (int64_t i = 0; i < nm; ++i) {
+        host[i] = has_w ? master_w[i] : nullptr;
+        host[nm + i] = has_g ? static_cast<void *>(master_g[i]) : nullptr;
+    }
+    for (int64_t i = 0; i < nb; ++i) {
+        host[2 * nm + i] = has_w ? spare_w[i] : nullptr;
+        host[2 * nm + nb + i] = has_g ? static_cast<void *>(spare_g[i]) : nullptr;
+    }
+    he = hipMemcpy(tables, host, sizeof(void *) * (2 * nm + 2 * nb),
+                   hipMemcpyHostToDevice);
+    delete[] host;
+    if (he != hipSuccess) {
+        (void)hipFree(tables);
+        return hip_fail(ctx, he, "pointer table upload");
+    }
+    if (ctx->reg_tables) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(ctx->reg_tables);
+    }
+    ctx->reg_tables = tables;
+    void **t = static_cast<void **>(tables);
+    ctx->d_master_w = t;
+    ctx->d_master_g = reinterpret_cast<float **>(t + nm);
+    ctx->d_spare_w = t + 2 * nm;
+    ctx->d_spare_g = reinterpret_cast<float **>(t + 2 * nm + nb);
+    ctx->reg_experts = n_experts;
+    ctx->reg_mats = n_mats;
+    ctx->reg_buffers = n_buffers;
+    for (int m = 0; m < n_mats; ++m) ctx->mat_elems[m] = mat_elems[m];
+    ctx->has_w = has_w;
+    ctx->has_g = has_g;
+    return UE_OK;
+}
+
+static int check_stream_call(ue_ctx *ctx, const int32_t *rep_off,
+                             const int32_t *rep_buf, int32_t n_experts,
+                             bool weights) {
+    if (ctx->reg_mats == 0)
+        return fail(ctx, UE_ESTATE, "no experts registered");
+    if (weights ? !ctx->has_w : !ctx->has_g)
+        return fail(ctx, UE_ESTATE, "%s not registered",
+                    weights ? "weights" : "gradients");
+    if (n_experts < 0 || n_experts > ctx->reg_experts)
+        return fail(ctx, UE_ESHAPE, "n_experts=%d outside 0..%d", n_experts,
+                    ctx->reg_experts);
+    if (n_experts > 0 && (!rep_off || !rep_buf))
+        return fail(ctx, UE_EINVAL, "null replica table");
+    if (!aligned(rep_off, 4) || !aligned(rep_buf, 4))
+        return fail(ctx, UE_EINVAL, "replica table must be 4-byte aligned");
+    return UE_OK;
+}
+
+int ue_weight_sync(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
+                   int32_t n_experts, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (int rc = check_stream_call(ctx, rep_off, rep_buf, n_experts, true))
+        return rc;
+    if (n_experts == 0) return UE_OK;
+    hipError_t he = ue::launch_weight_sync(*ctx, rep_off, rep_buf, n_experts,
+                                           static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_weight_sync launch");
+}
+
+int ue_grad_reduce(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
+                   int32_t n_experts, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (int rc = check_stream_call(ctx, rep_off, rep_buf, n_experts, false))
+        return rc;
+    if (n_experts == 0) return UE_OK;
+    hipError_t he = ue::launch_grad_reduce(*ctx, rep_off, rep_buf, n_experts,
+                                           static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_grad_reduce launch");
+}
+
+int ue_gather_rows(ue_ctx *ctx, const void *x, const int32_t *inv_perm,
+                   int32_t T, int32_t k, int32_t H, void *out, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (T < 0 || k < 1 || H < 0 || H % 8 != 0)
+        return fail(ctx, UE_ESHAPE, "ue_gather_rows: T=%d k=%d H=%d", T, k, H);
+    if (static_cast<int64_t>(T) * k >= (int64_t(1) << 31))
+        return fail(ctx, UE_ESHAPE, "ue_gather_rows: T*k too large");
+    if (T > 0 && (!x || !inv_perm || !out))
+        return fail(ctx, UE_EINVAL, "ue_gather_rows: null pointer");
+    if (!aligned(x, 16) || !aligned(out, 16) || !aligned(inv_perm, 4))
+        return fail(ctx, UE_EINVAL, "ue_gather_rows: x/out need 16-byte alignment");
+    if (H == 0) return UE_OK;
+    hipError_t he = ue::launch_gather_rows(*ctx, x, inv_perm, T, k, H, out,
+                                           static_cast<hipStream_t>(stream));
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_gather_rows launch");
+}
+
+}  // extern "C"

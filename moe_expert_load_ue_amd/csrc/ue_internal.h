@@ -1,0 +1,184 @@
+// Internal declarations of libue: the context, workspace layout, kernel
+// launchers and small wave-level helpers for gfx950 (wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+
+#include "../../include/ue.h"
+
+namespace ue {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxSlots = 4096;      // P = R * (N + S)
+constexpr int kMaxSpare = 64;
+constexpr int kMaxMats = 16;
+constexpr int kBlock = 256;          // threads per workgroup (4 waves)
+constexpr int kWaves = kBlock / 64;
+
+// Routing tiles. A load tile covers kLoadItems ids per thread; a reroute
+// tile covers kRerouteItems ids per thread, processed as kRerouteItems
+// rounds of 64 consecutive ids per wave.
+constexpr int kLoadItems = 32;
+constexpr int kLoadTile = kBlock * kLoadItems;
+constexpr int kRerouteItems = 16;
+constexpr int kRerouteTile = kBlock * kRerouteItems;
+
+}  // namespace ue
+
+struct ue_ctx {
+    ue_config cfg{};
+    int E = 0, R = 0, S = 0, N = 0, NS = 0, P = 0, k = 0;
+    int ebits = 0;          // bits to hold an expert id (ceil(log2 E))
+    int rbits = 0;          // bits to hold a rank id (ceil(log2 R))
+    int device = 0;
+    int num_cu = 0;
+    ue_placement_layout lay{};
+    int max_rr_tiles = 0;   // reroute tiles of the largest layer
+
+    // One device allocation holds the whole workspace; the counters and
+    // accumulators below are zero between calls (each kernel's last
+    // workgroup returns them to zero).
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+    int32_t *load_acc = nullptr;   // [max_layers][E]
+    int32_t *load_inv = nullptr;   // [max_layers]
+    uint32_t *load_done = nullptr; // [max_layers]
+    uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
+    uint32_t *rr_ticket = nullptr; // [max_layers]
+    uint32_t *rr_done = nullptr;   // [max_layers]
+    uint32_t *rr_epoch = nullptr;  // [max_layers]
+    int32_t *rr_rank_acc = nullptr;// [max_layers][R]
+    int32_t *rr_fault_acc = nullptr;// [max_layers]
+
+    size_t plan_lds = 0;
+    size_t reroute_lds = 0;
+
+    // Registered expert state (device pointer tables).
+    int reg_experts = 0, reg_mats = 0, reg_buffers = 0;
+    int64_t mat_elems[ue::kMaxMats] = {};
+    bool has_w = false, has_g = false;
+    void *reg_tables = nullptr;    // device: master_w, master_g, spare_w, spare_g
+    void **d_master_w = nullptr;
+    float **d_master_g = nullptr;
+    void **d_spare_w = nullptr;
+    float **d_spare_g = nullptr;
+
+    std::string err;
+};
+
+namespace ue {
+
+// Launchers (each returns a hipError_t from the launch).
+hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
+                       int64_t A, int32_t *counts, int32_t *invalid,
+                       hipStream_t s);
+hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
+                       int32_t *placement, hipStream_t s);
+hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
+                          const int32_t *placement, int L, int64_t A,
+                          int32_t *phys, int32_t *rank_counts, int32_t *perm,
+                          int32_t *inv_perm, int32_t *faults, hipStream_t s);
+hipError_t launch_weight_sync(const ue_ctx &c, const int32_t *rep_off,
+                              const int32_t *rep_buf, int n_experts,
+                              hipStream_t s);
+hipError_t launch_grad_reduce(const ue_ctx &c, const int32_t *rep_off,
+                              const int32_t *rep_buf, int n_experts,
+                              hipStream_t s);
+hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
+                              const int32_t *inv_perm, int T, int k, int H,
+                              void *out, hipStream_t s);
+
+size_t plan_lds_bytes(int E, int R, int P);
+// Raise the dynamic LDS limit of the planner kernel when it needs more
+// than 64 KiB.
+hipError_t plan_prepare(size_t lds_bytes);
+size_t reroute_lds_bytes(int E, int R, int P);
+
+// ---------------------------------------------------------------------
+// wave64 helpers
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ uint32_t mask_rank(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(
+        static_cast<uint32_t>(mask >> 32),
+        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+// Minimum of v over the 64 lanes, returned wave-uniform. Row reduction with
+// DPP (quad swaps, half-row and row mirrors), then the four row minima are
+// read from lanes 0, 16, 32, 48.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+    auto dpp_min = [](uint32_t x, int ctrl) -> uint32_t {
+        uint32_t y;
+        switch (ctrl) {
+            case 0: y = __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false); break;
+            case 1: y = __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false); break;
+            case 2: y = __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false); break;
+            default: y = __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false); break;
+        }
+        return x < y ? x : y;
+    };
+    v = dpp_min(v, 0);
+    v = dpp_min(v, 1);
+    v = dpp_min(v, 2);
+    v = dpp_min(v, 3);
+    uint32_t a = __builtin_amdgcn_readlane(v, 0);
+    uint32_t b = __builtin_amdgcn_readlane(v, 16);
+    uint32_t c = __builtin_amdgcn_readlane(v, 32);
+    uint32_t d = __builtin_amdgcn_readlane(v, 48);
+    a = a < b ? a : b;
+    c = c < d ? c : d;
+    return a < c ? a : c;
+}
+
+// Inclusive sum over lanes below and including this one.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Exclusive prefix sum of one value per thread over a kBlock-thread
+// workgroup. `wsum` is kWaves ints of LDS. Returns the prefix; the block
+// total goes to `total`. Contains barriers: every thread must call it.
+__device__ __forceinline__ int block_exclusive_sum(int v, int *wsum,
+                                                   int &total) {
+    const int w = threadIdx.x >> 6;
+    int x = wave_inclusive_sum(v);
+    if (lane_id() == 63) wsum[w] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        int s = wsum[i];
+        before += (i < w) ? s : 0;
+        total += s;
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
+__device__ __forceinline__ uint64_t atomic_load_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace ue

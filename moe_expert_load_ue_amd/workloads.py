@@ -216,15 +216,25 @@ def make_activations(tokens: int, hidden: int, microbatch: int,
 class StreamBuffers:
     """Expert state for replica weight sync / gradient reduction.
 
-    ``master_w[e, m]`` / ``master_g[e, m]`` are expert e's matrix m (flat);
-    ``spare_w[b, m]`` / ``spare_g[b, m]`` are replica buffer b's. Matrices of
-    one expert have equal sizes here, so each set is one dense tensor."""
-    master_w: torch.Tensor   # bf16 [E, M, n]
-    master_g: torch.Tensor   # fp32 [E, M, n]
-    spare_w: torch.Tensor    # bf16 [B, M, n]
-    spare_g: torch.Tensor    # fp32 [B, M, n]
+    Each set is one dense tensor ``[experts or buffers, matrices, stride]``
+    whose rows are padded to a multiple of 64 elements so every matrix starts
+    16-byte aligned; ``elems`` is the matrix size and :meth:`mat` gives the
+    exact view of one matrix."""
+    master_w: torch.Tensor   # bf16 [E, M, stride]
+    master_g: torch.Tensor   # fp32 [E, M, stride]
+    spare_w: torch.Tensor    # bf16 [B, M, stride]
+    spare_g: torch.Tensor    # fp32 [B, M, stride]
     rep_off: list            # CSR offsets per expert (entry 0 = master)
     rep_buf: list            # CSR entries: -1 for the master, else buffer id
+    elems: int = 0
+
+    def mat(self, name: str, i: int, m: int) -> torch.Tensor:
+        return getattr(self, name)[i, m, :self.elems]
+
+    def tables(self, name: str) -> list:
+        t = getattr(self, name)
+        return [[t[i, m, :self.elems] for m in range(t.shape[1])]
+                for i in range(t.shape[0])]
 
 
 def stream_csr(fanout=STREAM_FANOUT):
@@ -245,18 +255,18 @@ def make_stream_buffers(elems: int = STREAM_MATS[0], n_mats: int = 3,
                         seed: int = STREAM_SEED) -> StreamBuffers:
     rep_off, rep_buf, n_buf = stream_csr(fanout)
     E = len(fanout)
+    stride = (elems + 63) // 64 * 64
     g = _gen(device, seed_of(seed, 0))
-    mw = torch.empty((E, n_mats, elems), dtype=torch.bfloat16, device=device)
-    mg = torch.empty((E, n_mats, elems), dtype=torch.float32, device=device)
-    sg = torch.empty((n_buf, n_mats, elems), dtype=torch.float32,
+    mw = torch.zeros((E, n_mats, stride), dtype=torch.bfloat16, device=device)
+    mg = torch.zeros((E, n_mats, stride), dtype=torch.float32, device=device)
+    sg = torch.zeros((n_buf, n_mats, stride), dtype=torch.float32,
                      device=device)
     for t in (mw, mg, sg):
         for i in range(t.shape[0]):
             chunk = torch.randn((n_mats, elems), generator=g, device=device,
                                 dtype=torch.float32) * 0.02
-            t[i].copy_(chunk)
-    sw = torch.empty((n_buf, n_mats, elems), dtype=torch.bfloat16,
+            t[i, :, :elems].copy_(chunk)
+    sw = torch.empty((n_buf, n_mats, stride), dtype=torch.bfloat16,
                      device=device)
     sw.view(torch.int16).fill_(-1)      # 0xFFFF sentinel: a bf16 NaN
-    return StreamBuffers(mw, mg, sw, sg, rep_off, rep_buf)
-
+    return StreamBuffers(mw, mg, sw, sg, rep_off, rep_buf, elems)

@@ -1,0 +1,181 @@
+"""HIP path (through the C ABI) against the CPU oracle, bit-exact: expert
+counts, the whole placement block, physical routing, per-rank counts, the
+dispatch permutation and its inverse."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_load_ue_amd as ue
+import pins
+from gpu_helpers import compare_with_oracle, gpu_rebalance, say
+from moe_expert_load_ue_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def make_ctx(E, R, S, k, T, L=1):
+    return ue.Context(E, R, S, k, max(T, 1), L, device=DEV)
+
+
+@pytest.mark.parametrize("case", [g for g in pins.golden_cases()
+                                  if "routing" in g], ids=lambda g: g["name"])
+def test_golden_cases(case):
+    say("golden", case["name"])
+    routing = np.asarray(case["routing"], np.int32)[None]
+    ctx = make_ctx(case["E"], case["R"], case["S"], case["k"], case["T"])
+    res = gpu_rebalance(ctx, torch.from_numpy(routing))
+    for key in ("phys", "perm", "inv_perm", "rank_counts"):
+        assert res[key].reshape(-1).tolist() == case[key], key
+    compare_with_oracle(res, routing, case["E"], case["R"], case["S"])
+
+
+def test_golden_planner_only():
+    for case in pins.golden_cases():
+        say("golden plan", case["name"])
+        ctx = make_ctx(case["E"], case["R"], case["S"], 1, 1)
+        counts = torch.tensor(case["counts"], dtype=torch.int32,
+                              device=DEV)[None]
+        f = ctx.placement_fields(ue.ue_plan(ctx, counts))
+        for key in ("quota", "exhausted", "residual", "n_rep"):
+            assert int(f[key][0]) == case[key], key
+        for key in ("load_before", "load_after", "rep_off", "slot_expert",
+                    "slot_cap", "slot_off"):
+            assert f[key][0].tolist() == case[key], key
+        n = case["n_rep"]
+        assert f["rep_slot"][0, :n].tolist() == case["rep_slot"]
+        assert f["rep_cap"][0, :n].tolist() == case["rep_cap"]
+
+
+def test_random_instances():
+    """Seeded random shapes: tiny to several tiles with ragged tails, skew
+    from uniform to extreme, S = 0..3, one to four layers."""
+    rng = np.random.default_rng(99)
+    for it in range(60):
+        R = int(rng.integers(1, 17))
+        N = int(rng.integers(1, 9))
+        E = R * N
+        if E > 1024:
+            continue
+        S = int(rng.integers(0, 4))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([0, 1, 7, 100, 511, 2048, 3001, 9000]))
+        L = int(rng.integers(1, 5))
+        skew = float(rng.uniform(0, 3))
+        routing = np.stack([pins.random_routing(rng, T, E, k, skew)
+                            for _ in range(L)])
+        say(f"random {it}: E={E} R={R} S={S} k={k} T={T} L={L}")
+        ctx = make_ctx(E, R, S, k, T, L)
+        res = gpu_rebalance(ctx, torch.from_numpy(routing))
+        compare_with_oracle(res, routing, E, R, S)
+
+
+@pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
+def test_configs_full_size(name):
+    """Every routing workload at its full size, every layer, bit-exact."""
+    cfg = W.CONFIGS[name]
+    say("full size", name)
+    routing = W.make_routing(cfg, device=DEV)
+    ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
+                   cfg.layers)
+    res = gpu_rebalance(ctx, routing)
+    compare_with_oracle(res, routing.cpu().numpy(), cfg.experts, cfg.ranks,
+                        cfg.spare)
+
+
+def test_invalid_ids_and_faults():
+    rng = np.random.default_rng(5)
+    E, R, S, k, T = 32, 4, 2, 4, 3000
+    routing = pins.random_routing(rng, T, E, k, 1.0)
+    routing[0, 0] = -1
+    routing[17, 3] = E
+    routing[2999, 1] = 12345
+    say("invalid ids")
+    ctx = make_ctx(E, R, S, k, T)
+    res = gpu_rebalance(ctx, torch.from_numpy(routing[None]))
+    assert int(res["invalid"][0]) == 3
+    assert int(res["faults"][0]) == 3
+    compare_with_oracle(res, routing[None], E, R, S)
+
+
+def test_plan_from_other_counts_faults():
+    """A plan made for fewer tokens than routed: the overflow is reported,
+    never written out of bounds."""
+    rng = np.random.default_rng(6)
+    E, R, S, k, T = 16, 4, 1, 2, 500
+    routing = torch.from_numpy(pins.random_routing(rng, T, E, k, 1.5)[None])
+    half = routing[:, : T // 2].contiguous()
+    say("plan from other counts")
+    ctx = make_ctx(E, R, S, k, T)
+    counts = ue.ue_load(ctx, half.to(DEV))
+    pl = ue.ue_plan(ctx, counts)
+    out = ue.ue_reroute(ctx, routing.to(DEV), pl)
+    torch.cuda.synchronize()
+    assert int(out["faults"][0]) == T * k - (T // 2) * k
+
+
+def test_deterministic_repeats():
+    cfg = W.CONFIGS["large_ep"]
+    routing = W.make_routing(cfg, device=DEV)
+    ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens)
+    say("repeats large_ep")
+    first = gpu_rebalance(ctx, routing)
+    for _ in range(10):
+        again = gpu_rebalance(ctx, routing)
+        for key in ("counts", "placement", "phys", "perm", "inv_perm",
+                    "rank_counts"):
+            assert np.array_equal(first[key], again[key]), key
+
+
+def test_batched_equals_single_layers():
+    cfg = W.CONFIGS["dsv3"]
+    routing = W.make_routing(cfg, device=DEV, layers=8)
+    ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens, 8)
+    say("batched vs single dsv3 x8")
+    batched = gpu_rebalance(ctx, routing)
+    for layer in range(8):
+        one = gpu_rebalance(ctx, routing[layer:layer + 1].contiguous())
+        for key in ("counts", "placement", "phys", "perm", "inv_perm",
+                    "rank_counts"):
+            assert np.array_equal(batched[key][layer], one[key][0]), key
+
+
+def test_refusals_leave_outputs_untouched():
+    E, R, S, k, T = 64, 8, 2, 8, 1000
+    ctx = make_ctx(E, R, S, k, T, 2)
+    routing = torch.zeros((1, T, k), dtype=torch.int32, device=DEV)
+    sentinel = torch.full((1, E), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    counts = sentinel.clone()
+    lib = ue.library()
+    import ctypes
+    say("refusals")
+    # too many tokens, too many layers, null counts, misaligned pointer
+    assert lib.ue_load(ctx._h, ctypes.c_void_p(routing.data_ptr()), 1, T + 1,
+                       ctypes.c_void_p(counts.data_ptr()), None,
+                       None) == -2
+    assert lib.ue_load(ctx._h, ctypes.c_void_p(routing.data_ptr()), 3, T,
+                       ctypes.c_void_p(counts.data_ptr()), None, None) == -2
+    assert lib.ue_load(ctx._h, ctypes.c_void_p(routing.data_ptr()), 1, T,
+                       None, None, None) == -1
+    assert lib.ue_load(ctx._h, ctypes.c_void_p(routing.data_ptr() + 2), 1, T,
+                       ctypes.c_void_p(counts.data_ptr()), None, None) == -1
+    assert "aligned" in ue.ue_last_error(ctx)
+    placement = torch.full((1, ctx.placement_words), 77, dtype=torch.int32,
+                           device=DEV)
+    assert lib.ue_plan(ctx._h, None, 1, ctypes.c_void_p(placement.data_ptr()),
+                       None) == -1
+    assert lib.ue_plan(ctx._h, ctypes.c_void_p(counts.data_ptr()), 0,
+                       ctypes.c_void_p(placement.data_ptr()), None) == -2
+    phys = torch.full((1, T, k), 9, dtype=torch.int32, device=DEV)
+    assert lib.ue_reroute(ctx._h, ctypes.c_void_p(routing.data_ptr()),
+                          ctypes.c_void_p(placement.data_ptr()), 1, T,
+                          ctypes.c_void_p(phys.data_ptr()), None, None, None,
+                          None, None) == -1
+    assert lib.ue_weight_sync(ctx._h, None, None, 1, None) == -6
+    torch.cuda.synchronize()
+    assert torch.equal(counts, sentinel)
+    assert bool((placement == 77).all()) and bool((phys == 9).all())
+    # unsupported configurations are refused at creation
+    for bad in ((63, 8, 1, 8), (2048, 8, 1, 8), (64, 8, 100, 8), (64, 8, 1, 65)):
+        with pytest.raises(ue.UEError):
+            ue.Context(*bad, 100, 1, device=DEV)

@@ -1,0 +1,167 @@
+"""Replica weight sync, replica gradient reduction and the dispatch gather
+on the device, against the oracle (numpy): bitwise for the copies, within
+the fp32 summation bound for the gradient sums."""
+import numpy as np
+import pytest
+import torch
+
+import moe_expert_load_ue_amd as ue
+import oracle
+from gpu_helpers import gpu_rebalance, say
+from moe_expert_load_ue_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+U = 2.0 ** -24          # unit roundoff of fp32
+
+
+def sum_bound(terms_abs_sum, n_adds):
+    """|fl(sum) - sum| <= gamma_n * sum |terms| for n left-to-right adds."""
+    g = n_adds * U / (1 - n_adds * U)
+    return g * terms_abs_sum
+
+
+def register(ctx, sb):
+    M = sb.master_w.shape[1]
+    ctx.register_experts([sb.elems] * M, sb.tables("master_w"),
+                         sb.tables("master_g"), sb.tables("spare_w"),
+                         sb.tables("spare_g"))
+
+
+def csr_tensors(sb):
+    return (torch.tensor(sb.rep_off, dtype=torch.int32, device=DEV),
+            torch.tensor(sb.rep_buf, dtype=torch.int32, device=DEV))
+
+
+@pytest.mark.parametrize("elems", [8, 1000, 4099, 70001, 262144])
+def test_sync_and_reduce_small(elems):
+    """Odd sizes: partial last chunks and tails not a multiple of a vector."""
+    say("stream small", elems)
+    fan = (3, 0, 1, 2, 4)
+    sb = W.make_stream_buffers(elems=elems, n_mats=3, fanout=fan, device=DEV)
+    sb.spare_w.view(torch.int16).fill_(-1)
+    ctx = ue.Context(8, 1, 0, 1, 1, device=DEV)
+    register(ctx, sb)
+    rep_off, rep_buf = csr_tensors(sb)
+    n = sb.elems
+    master_w = sb.master_w[..., :n].cpu().numpy().view(np.uint16)
+    master_g = sb.master_g[..., :n].cpu().numpy().astype(np.float64)
+    spare_g = sb.spare_g[..., :n].cpu().numpy()
+    ctx.weight_sync(rep_off, rep_buf)
+    ctx.grad_reduce(rep_off, rep_buf)
+    torch.cuda.synchronize()
+    got_w = sb.spare_w[..., :n].cpu().numpy().view(np.uint16)
+    got_g = sb.master_g[..., :n].cpu().numpy()
+    for e, f in enumerate(fan):
+        bufs = sb.rep_buf[sb.rep_off[e] + 1: sb.rep_off[e + 1]]
+        want = oracle.weight_sync(master_w[e], len(bufs))
+        for b, w in zip(bufs, want):
+            assert np.array_equal(got_w[b], w), (e, b)
+        ref = oracle.grad_reduce(master_g[e], [spare_g[b] for b in bufs])
+        terms = np.abs(master_g[e]) + sum(np.abs(spare_g[b]) for b in bufs)
+        err = np.abs(got_g[e].astype(np.float64) - ref)
+        assert np.all(err <= sum_bound(terms, len(bufs)) + 1e-45), e
+        if not bufs:
+            assert np.array_equal(got_g[e], master_g[e].astype(np.float32))
+    # replicas' gradients are left unchanged
+    assert np.array_equal(sb.spare_g[..., :n].cpu().numpy(), spare_g)
+    # nothing beyond the matrices was written
+    assert bool((sb.spare_w[..., n:].view(torch.int16) == -1).all())
+
+
+def test_reduce_order_is_left_to_right():
+    """1 + 2^-24 + 2^-24: left to right each add ties to even and stays 1;
+    any other grouping gives 1 + 2^-23. The oracle (float64) gives the exact
+    sum, which the fp32 result meets within the summation bound."""
+    say("reduce order")
+    n = 4096
+    mg = torch.ones((2, 1, n), dtype=torch.float32, device=DEV)
+    sg = torch.full((2, 1, n), 2.0 ** -24, dtype=torch.float32, device=DEV)
+    mw = torch.zeros((2, 1, n), dtype=torch.bfloat16, device=DEV)
+    sw = torch.zeros((2, 1, n), dtype=torch.bfloat16, device=DEV)
+    ctx = ue.Context(2, 1, 0, 1, 1, device=DEV)
+    ctx.register_experts([n], [[mw[0, 0]], [mw[1, 0]]],
+                         [[mg[0, 0]], [mg[1, 0]]], [[sw[0, 0]], [sw[1, 0]]],
+                         [[sg[0, 0]], [sg[1, 0]]])
+    rep_off = torch.tensor([0, 3, 4], dtype=torch.int32, device=DEV)
+    rep_buf = torch.tensor([-1, 0, 1, -1], dtype=torch.int32, device=DEV)
+    ctx.grad_reduce(rep_off, rep_buf)
+    torch.cuda.synchronize()
+    assert bool((mg[0] == 1.0).all()) and bool((mg[1] == 1.0).all())
+    exact = oracle.grad_reduce(np.ones(1), [np.full(1, 2.0 ** -24)] * 2)[0]
+    assert abs(1.0 - exact) <= sum_bound(1.0 + 2 * 2.0 ** -24, 2)
+
+
+def test_sync_reduce_full_size_sampled():
+    """32 experts x 3 DeepSeek-V3 expert matrices, 64 replica buffers:
+    every replica equals its master bitwise (checked on the device), and
+    sampled gradient elements match the oracle within the bound."""
+    say("stream full size")
+    sb = W.make_stream_buffers(device=DEV)
+    ctx = ue.Context(32, 1, 0, 1, 1, device=DEV)
+    register(ctx, sb)
+    rep_off, rep_buf = csr_tensors(sb)
+    rng = np.random.default_rng(4)
+    n = sb.elems
+    idx = np.concatenate([rng.integers(0, n, 4000), [0, n - 1]])
+    idx_t = torch.from_numpy(idx).to(DEV)
+    before_m = sb.master_g[:, :, idx_t].cpu().numpy().astype(np.float64)
+    before_s = sb.spare_g[:, :, idx_t].cpu().numpy().astype(np.float64)
+    ctx.weight_sync(rep_off, rep_buf)
+    ctx.grad_reduce(rep_off, rep_buf)
+    torch.cuda.synchronize()
+    after = sb.master_g[:, :, idx_t].cpu().numpy().astype(np.float64)
+    for e in range(32):
+        bufs = sb.rep_buf[sb.rep_off[e] + 1: sb.rep_off[e + 1]]
+        for b in bufs:
+            assert torch.equal(sb.spare_w[b, :, :n].view(torch.int16),
+                               sb.master_w[e, :, :n].view(torch.int16)), (e, b)
+        ref = oracle.grad_reduce(before_m[e], [before_s[b] for b in bufs])
+        terms = np.abs(before_m[e]) + sum(np.abs(before_s[b]) for b in bufs)
+        assert np.all(np.abs(after[e] - ref) <= sum_bound(terms, len(bufs)))
+        rel = np.abs(after[e] - ref) / np.maximum(terms, 1e-30)
+        assert rel.max() <= 1e-6
+
+
+def test_gather_small():
+    rng = np.random.default_rng(8)
+    for T, k, H in ((1, 1, 8), (37, 3, 24), (300, 8, 1032), (1000, 2, 4096)):
+        say("gather", T, k, H)
+        x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)
+                             ).to(torch.bfloat16).to(DEV)
+        perm = rng.permutation(T * k).astype(np.int32)
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(T * k, dtype=np.int32)
+        ctx = ue.Context(8, 1, 0, k, T, device=DEV)
+        out = torch.full((T * k, H), -1, dtype=torch.int16, device=DEV
+                         ).view(torch.bfloat16)
+        ctx.gather_rows(x, torch.from_numpy(inv).to(DEV), out=out)
+        torch.cuda.synchronize()
+        want = oracle.gather(x.view(torch.int16).cpu().numpy(), perm, k)
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), want)
+
+
+def test_gather_pipeline_microbatch_sampled():
+    """One microbatch of the pipeline workload at full size: rebalance,
+    then gather [131072, 4096] bf16 into physical-expert order; sampled
+    rows checked against the oracle's permutation."""
+    cfg = W.CONFIGS["pipeline"]
+    say("gather pipeline full size")
+    routing = W.make_routing(cfg, device=DEV, layers=1)
+    ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
+                     1, device=DEV)
+    res = gpu_rebalance(ctx, routing)
+    pl = oracle.plan(oracle.load(routing.cpu().numpy(), cfg.experts)[0][0],
+                     cfg.ranks, cfg.spare)
+    rr = oracle.reroute(routing.cpu().numpy().reshape(-1), pl)
+    x = W.make_activations(cfg.tokens, cfg.hidden, 0, device=DEV)
+    inv = torch.from_numpy(res["inv_perm"][0]).to(DEV)
+    out = ctx.gather_rows(x, inv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(9)
+    rows = np.concatenate([rng.integers(0, cfg.assignments, 3000),
+                           [0, cfg.assignments - 1]])
+    got = out[torch.from_numpy(rows).to(DEV)].view(torch.int16).cpu().numpy()
+    x_host = x.view(torch.int16).cpu().numpy()
+    want = oracle.gather(x_host, rr["perm"][rows], cfg.topk)
+    assert np.array_equal(got, want)
