@@ -165,9 +165,12 @@ __global__ __launch_bounds__(kBlock) void k_plan(
             int Lr = __builtin_amdgcn_readfirstlane(s.load[r]);
             int rem_e = __builtin_amdgcn_readfirstlane(s.rem[e]);
             const int first = nrec;
-            // each chunk takes one spare slot: at most R*S chunks in all
-            while (Lr > Q && rem_e > 0 && nrec < R * S) {
-                const uint32_t best = wave_min_u32(my_key);
+            while (Lr > Q && rem_e > 0) {
+                // Each chunk takes one spare slot, so with all R*S taken no
+                // rank is eligible; checking the count first also bounds
+                // the loop whatever the keys hold.
+                const uint32_t best =
+                    nrec < R * S ? wave_min_u32(my_key) : 0xFFFFFFFFu;
                 if (best == 0xFFFFFFFFu) {
                     exhausted = 1;
                     break;
@@ -260,6 +263,9 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     }
     int resid_total;
     block_exclusive_sum(resid, wsum, resid_total);
+    // the block's alignment padding is written too, so a block is fully
+    // defined by its counts
+    for (int i = lay.load_after + R + tid; i < lay.words; i += kBlock) out[i] = 0;
     if (tid == 0) {
         out[lay.slot_off + P] = slot_total;
         out[lay.quota] = s_quota;

@@ -44,13 +44,15 @@ def test_sync_and_reduce_small(elems):
     register(ctx, sb)
     rep_off, rep_buf = csr_tensors(sb)
     n = sb.elems
-    master_w = sb.master_w[..., :n].cpu().numpy().view(np.uint16)
+    master_w = sb.master_w[..., :n].view(torch.int16).cpu().numpy().view(
+        np.uint16)
     master_g = sb.master_g[..., :n].cpu().numpy().astype(np.float64)
     spare_g = sb.spare_g[..., :n].cpu().numpy()
     ctx.weight_sync(rep_off, rep_buf)
     ctx.grad_reduce(rep_off, rep_buf)
     torch.cuda.synchronize()
-    got_w = sb.spare_w[..., :n].cpu().numpy().view(np.uint16)
+    got_w = sb.spare_w[..., :n].view(torch.int16).cpu().numpy().view(
+        np.uint16)
     got_g = sb.master_g[..., :n].cpu().numpy()
     for e, f in enumerate(fan):
         bufs = sb.rep_buf[sb.rep_off[e] + 1: sb.rep_off[e + 1]]
