@@ -33,6 +33,10 @@ struct PlanLds {
     int32_t *rec_e, *rec_p, *rec_m, *slot_cap, *slot_exp, *rep_off;
 };
 
+__device__ __forceinline__ int32_t *carve_end(const PlanLds &s, int P) {
+    return s.slot_exp + P;
+}
+
 __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
     PlanLds s;
     int32_t *p = base;
@@ -73,9 +77,127 @@ __device__ int block_scan_inplace(int32_t *data, int n, int *wsum) {
     return total;
 }
 
+// Per-lane register state of the ranks a lane owns (lane, lane+64, ...),
+// read and written with a wave-uniform slot index through unrolled selects.
+template <int RPL>
+struct RankRegs {
+    int load[RPL];
+    int nfree[RPL];
+
+    __device__ __forceinline__ int get_load(int k) const {
+        int v = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) v = (i == k) ? load[i] : v;
+        return v;
+    }
+    __device__ __forceinline__ int get_free(int k) const {
+        int v = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) v = (i == k) ? nfree[i] : v;
+        return v;
+    }
+    // smallest key (load << rbits | rank) among this lane's eligible ranks
+    __device__ __forceinline__ uint32_t key(int lane, int R, int Q,
+                                            int rbits) const {
+        uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int r = lane + 64 * i;
+            const uint32_t k = (static_cast<uint32_t>(load[i]) << rbits) |
+                               static_cast<uint32_t>(r);
+            const bool ok = r < R && nfree[i] > 0 && load[i] < Q;
+            best = (ok && k < best) ? k : best;
+        }
+        return best;
+    }
+};
+
+// The spill loop, run by wave 0 alone. Everything that decides the next
+// step is wave-uniform: the candidate, its rank's load, the expert's
+// remainder and the reduced minimum key. Only the lane owning the chosen
+// destination changes its registers and refreshes its cached key.
+template <int RPL>
+__device__ void spill_loop(PlanLds &s, int ncand, int R, int S, int N, int NS,
+                           int Q, int rbits, int &nrec_out,
+                           int &exhausted_out) {
+    const int lane = threadIdx.x & 63;
+    RankRegs<RPL> st;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int r = lane + 64 * i;
+        st.load[i] = r < R ? s.load[r] : 0;
+        st.nfree[i] = r < R ? S : 0;
+    }
+    uint32_t my_key = st.key(lane, R, Q, rbits);
+    const uint32_t rmask = (1u << rbits) - 1u;
+    const int max_rec = R * S;
+    int nrec = 0;
+    int exhausted = 0;
+    for (int c = 0; c < ncand && !exhausted; ++c) {
+        const int e = __builtin_amdgcn_readfirstlane(s.sorted[c]);
+        const int r = e / N;
+        int Lr = __builtin_amdgcn_readlane(st.get_load(r >> 6), r & 63);
+        int rem_e = __builtin_amdgcn_readfirstlane(s.rem[e]);
+        const int first = nrec;
+        while (Lr > Q && rem_e > 0) {
+            // each chunk takes one spare slot: with all R*S taken no rank
+            // is eligible (this also bounds the loop whatever the keys hold)
+            const uint32_t best =
+                nrec < max_rec ? wave_min_u32(my_key) : 0xFFFFFFFFu;
+            if (best == 0xFFFFFFFFu) {
+                exhausted = 1;
+                break;
+            }
+            const int d = static_cast<int>(best & rmask);
+            const int Ld = static_cast<int>(best >> rbits);
+            int m = Lr - Q;
+            m = rem_e < m ? rem_e : m;
+            m = (Q - Ld) < m ? (Q - Ld) : m;
+            const int dk = d >> 6;
+            const int fr = __builtin_amdgcn_readlane(st.get_free(dk), d & 63);
+            const int p = d * NS + N + (S - fr);
+            if (lane == 0) {
+                s.rec_e[nrec] = e;
+                s.rec_p[nrec] = p;
+                s.rec_m[nrec] = m;
+            }
+            ++nrec;
+            rem_e -= m;
+            Lr -= m;
+            if (lane == (d & 63)) {
+#pragma unroll
+                for (int i = 0; i < RPL; ++i) {
+                    if (i == dk) {
+                        st.load[i] = Ld + m;
+                        st.nfree[i] -= 1;
+                    }
+                }
+                my_key = st.key(lane, R, Q, rbits);
+            }
+        }
+        if (lane == (r & 63)) {
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                if (i == (r >> 6)) st.load[i] = Lr;
+        }
+        if (lane == 0) {
+            s.rem[e] = rem_e;
+            s.first_rec[e] = first;
+            s.nrec_e[e] = nrec - first;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+        const int r = lane + 64 * i;
+        if (r < R) s.load[r] = st.load[i];
+    }
+    nrec_out = nrec;
+    exhausted_out = exhausted;
+}
+
 __global__ __launch_bounds__(kBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
-    int P, int rbits, ue_placement_layout lay,
+    int P, int rbits, uint32_t lds_bytes, ue_placement_layout lay,
     int32_t *__restrict__ placement) {
     extern __shared__ int32_t lds[];
     __shared__ int wsum[kWaves];
@@ -86,6 +208,8 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     const int32_t *cin = counts + static_cast<int64_t>(layer) * E;
     int32_t *out = placement + static_cast<int64_t>(layer) * lay.words;
     PlanLds s = carve(lds, E, R, P);
+    // the carve-up must fit the launch's LDS (checked, not assumed)
+    if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) return;
 
     // ---- A. loads, quota, candidates ----------------------------------
     int part = 0;
@@ -140,70 +264,17 @@ __global__ __launch_bounds__(kBlock) void k_plan(
 
     // ---- B. sequential spill loop on wave 0 ------------------------------
     if (tid < 64) {
-        const int lane = tid;
-        const uint32_t rmask = (1u << rbits) - 1u;
-        auto lane_key = [&](void) -> uint32_t {
-            uint32_t best = 0xFFFFFFFFu;
-            for (int r = lane; r < R; r += 64) {
-                const int l = s.load[r];
-                if (s.nfree[r] > 0 && l < Q) {
-                    const uint32_t key =
-                        (static_cast<uint32_t>(l) << rbits) |
-                        static_cast<uint32_t>(r);
-                    best = key < best ? key : best;
-                }
-            }
-            return best;
-        };
-        uint32_t my_key = lane_key();
-        int nrec = 0;
-        int exhausted = 0;
-        for (int c = 0; c < ncand && !exhausted; ++c) {
-            // every lane holds the same values; make them wave-uniform
-            const int e = __builtin_amdgcn_readfirstlane(s.sorted[c]);
-            const int r = e / N;
-            int Lr = __builtin_amdgcn_readfirstlane(s.load[r]);
-            int rem_e = __builtin_amdgcn_readfirstlane(s.rem[e]);
-            const int first = nrec;
-            while (Lr > Q && rem_e > 0) {
-                // Each chunk takes one spare slot, so with all R*S taken no
-                // rank is eligible; checking the count first also bounds
-                // the loop whatever the keys hold.
-                const uint32_t best =
-                    nrec < R * S ? wave_min_u32(my_key) : 0xFFFFFFFFu;
-                if (best == 0xFFFFFFFFu) {
-                    exhausted = 1;
-                    break;
-                }
-                const int d = static_cast<int>(best & rmask);
-                const int Ld = static_cast<int>(best >> rbits);
-                int m = Lr - Q;
-                m = rem_e < m ? rem_e : m;
-                m = (Q - Ld) < m ? (Q - Ld) : m;
-                const int fr = __builtin_amdgcn_readfirstlane(s.nfree[d]);
-                const int p = d * NS + N + (S - fr);
-                if (lane == 0) {
-                    s.rec_e[nrec] = e;
-                    s.rec_p[nrec] = p;
-                    s.rec_m[nrec] = m;
-                }
-                ++nrec;
-                rem_e -= m;
-                Lr -= m;
-                if (lane == (d & 63)) {
-                    s.load[d] = Ld + m;
-                    s.nfree[d] = fr - 1;
-                    my_key = lane_key();
-                }
-            }
-            if (lane == 0) {
-                s.rem[e] = rem_e;
-                s.load[r] = Lr;
-                s.first_rec[e] = first;
-                s.nrec_e[e] = nrec - first;
-            }
+        int nrec = 0, exhausted = 0;
+        switch ((R + 63) / 64) {
+            case 1: spill_loop<1>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 2: spill_loop<2>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 3:
+            case 4: spill_loop<4>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 5: case 6: case 7:
+            case 8: spill_loop<8>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            default: spill_loop<16>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
         }
-        if (lane == 0) {
+        if (tid == 0) {
             s_nrec = nrec;
             s_exhausted = exhausted;
             s_quota = Q;
@@ -290,8 +361,8 @@ hipError_t plan_prepare(size_t lds_bytes) {
 hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        int32_t *placement, hipStream_t s) {
     hipLaunchKernelGGL(k_plan, dim3(L), dim3(kBlock), c.plan_lds, s, counts,
-                       c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits, c.lay,
-                       placement);
+                       c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
+                       static_cast<uint32_t>(c.plan_lds), c.lay, placement);
     return hipGetLastError();
 }
 

@@ -8,36 +8,31 @@
 // the stable sort of assignments by physical slot.
 //
 // j needs, for every assignment, the number of earlier assignments of the
-// same expert in the whole layer. Each workgroup takes a tile by an atomic
-// ticket (so it only ever waits on tiles that have already started), and:
+// same expert in the whole layer. Each workgroup takes a tile by ticket (so
+// it only ever waits on tiles that have already started) and:
 //   1. each wave ranks its ids in rounds of 64 consecutive assignments:
 //      lanes with equal ids are found with one ballot per id bit, a lane's
 //      rank among its peers is the popcount of peers below it, and a
 //      per-wave LDS counter per expert carries the count across rounds;
-//   2. per expert, the per-wave counts are scanned across the 4 waves;
-//   3. decoupled lookback over earlier tiles, one expert per thread: the
-//      tile publishes its per-expert count, then walks back over the tiles
-//      before it, adding their published counts until it meets a published
-//      inclusive prefix, then publishes its own inclusive prefix. Each
-//      64-bit status word holds {call epoch, flag, value}, so stale words of
-//      earlier calls are never mistaken for current ones and nothing has to
-//      be cleared between calls;
+//   2. per expert, the per-wave counts are scanned across the 4 waves, and
+//      the tile counts across experts (the tile's own sorted order);
+//   3. decoupled lookback over earlier tiles (ue_internal.h) gives the count
+//      of each expert before this tile;
 //   4. j = tile prefix + wave prefix + rank; the replica is found by a short
-//      scan of the expert's capacity prefixes held in LDS.
-// The last workgroup of a layer publishes rank counts and fault counts and
-// returns the ticket and completion counters to zero.
+//      scan of the expert's capacity prefixes held in LDS; phys and inv_perm
+//      are written straight out (coalesced); perm entries are first placed
+//      in LDS in the tile's (expert, j) order, where neighbours have
+//      consecutive dispatch positions, then written out in that order so
+//      that stores land in contiguous runs;
+//   5. the tile with the last ticket knows every expert's total; per-rank
+//      counts are the overlaps of [0, total) with the replicas' capacity
+//      intervals, and faults are the ids out of range plus the assignments
+//      beyond an expert's capacity.
+// No fences and no global atomics on data.
 #include "ue_internal.h"
 
 namespace ue {
 namespace {
-
-constexpr uint64_t kFlagAgg = 1;
-constexpr uint64_t kFlagPrefix = 2;
-
-__device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint64_t flag,
-                                               uint32_t value) {
-    return (static_cast<uint64_t>(epoch) << 32) | (flag << 30) | value;
-}
 
 struct RerouteArgs {
     const int32_t *routing;
@@ -45,18 +40,18 @@ struct RerouteArgs {
     int64_t A;                 // assignments per layer
     int E, R, NS, P, ebits, tiles, max_tiles;
     uint32_t spin_limit;       // bound on one lookback wait
+    uint32_t lds_bytes;        // dynamic LDS the launch provides
     ue_placement_layout lay;
     int32_t *phys, *perm, *inv_perm;
-    uint64_t *state;
-    uint32_t *ticket, *done, *epoch;
-    int32_t *rank_acc, *fault_acc, *rank_counts, *faults;
+    uint64_t *state;           // [max_layers][max_tiles][E]
+    uint32_t *ticket, *epoch;  // [max_layers]
+    int32_t *rank_counts, *faults;
 };
 
 __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     extern __shared__ int32_t lds[];
     __shared__ int wsum[kWaves];
     __shared__ uint32_t s_ticket, s_epoch;
-    __shared__ int s_last;
 
     const int E = g.E, P = g.P, R = g.R;
     const int layer = blockIdx.y;
@@ -64,27 +59,33 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int w = tid >> 6;
     const int lane = tid & 63;
 
-    // LDS: per-wave counters [kWaves][E], tile prefix [E], replica table
-    // (rep_off [E+1], rep_slot [P], rep_lo [P] prefix start, rep_hi [P]
-    // prefix end), slot_off [P], rank histogram [R].
+    // LDS: per-wave counters [kWaves][E] (then wave prefixes), tile counts
+    // [E], tile order offsets [E], earlier-tile prefix [E], replica table
+    // (rep_off [E+1], rep_slot [P], rep_lo [P], rep_hi [P]), slot_off [P],
+    // rank histogram [R], staged perm (assignment, position) [2][tile].
     int32_t *whist = lds;
-    int32_t *tile_base = whist + kWaves * E;
-    int32_t *rep_off = tile_base + E;
+    int32_t *tcount = whist + kWaves * E;
+    int32_t *torder = tcount + E;
+    int32_t *tbase = torder + E;
+    int32_t *rep_off = tbase + E;
     int32_t *rep_slot = rep_off + E + 1;
     int32_t *rep_lo = rep_slot + P;
     int32_t *rep_hi = rep_lo + P;
     int32_t *slot_off = rep_hi + P;
     int32_t *rank_hist = slot_off + P;
+    int32_t *stage_a = rank_hist + R;
+    int32_t *stage_pos = stage_a + kRerouteTile;
+    // the carve-up must fit the launch's LDS (checked, not assumed)
+    if (static_cast<size_t>(stage_pos + kRerouteTile - lds) * 4 > g.lds_bytes)
+        return;
 
-    if (tid == 0) {
-        s_ticket = atomicAdd(&g.ticket[layer], 1u);
-        s_epoch = atomic_load_agent(&g.epoch[layer]) + 1u;
-    }
+    if (tid == 0) take_ticket(g.ticket + layer, g.epoch + layer, g.tiles,
+                              s_ticket, s_epoch);
     const int32_t *pl = g.placement + static_cast<int64_t>(layer) * g.lay.words;
     for (int i = tid; i < kWaves * E; i += kBlock) whist[i] = 0;
     for (int r = tid; r < R; r += kBlock) rank_hist[r] = 0;
-    // The table is read as written by the planner, but every index is
-    // clamped so that a corrupt block can only produce faults.
+    // The table is read as the planner wrote it, with every index clamped,
+    // so a corrupt block can only produce faults.
     for (int e = tid; e <= E; e += kBlock) {
         const int v = pl[g.lay.rep_off + e];
         rep_off[e] = v < 0 ? 0 : (v > P ? P : v);
@@ -95,7 +96,6 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         slot_off[p] = pl[g.lay.slot_off + p];
     }
     __syncthreads();
-    // capacity prefix of each replica within its expert
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
         const int hi = rep_off[e + 1];
@@ -106,19 +106,13 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             rep_hi[i] = run;
         }
     }
-    __syncthreads();
-
-    // Tickets run 0..tiles-1 within a launch; anything else means the
-    // workspace counters were left inconsistent by an earlier failed launch.
-    if (s_ticket >= static_cast<uint32_t>(g.tiles)) {
-        if (tid == 0) atomicOr(&g.fault_acc[layer], 0x40000000);
-        return;
-    }
     const int tile = static_cast<int>(s_ticket);
+    if (tile >= g.tiles) return;    // only after a corrupted earlier launch
     const uint32_t epoch = s_epoch;
     const int64_t base = static_cast<int64_t>(layer) * g.A;
-    const int64_t a0 = static_cast<int64_t>(tile) * kRerouteTile +
-                       static_cast<int64_t>(w) * 64 * kRerouteItems + lane;
+    const int64_t tile0 = static_cast<int64_t>(tile) * kRerouteTile;
+    const int64_t a0 = tile0 + static_cast<int64_t>(w) * 64 * kRerouteItems +
+                       lane;
 
     // ---- 1. per-wave stable ranks ----------------------------------------
     int32_t ids[kRerouteItems];
@@ -134,12 +128,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     for (int i = 0; i < kRerouteItems; ++i) {
         const int id = ids[i];
         const bool valid = static_cast<uint32_t>(id) < static_cast<uint32_t>(E);
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < g.ebits; ++b) {
-            const bool bit = (id >> b) & 1;
-            const uint64_t ones = __ballot(bit);
-            peers &= bit ? ones : ~ones;
-        }
+        const uint64_t peers = match_peers(id, valid, g.ebits);
         const uint32_t below = mask_rank(peers);
         int before = 0;
         if (valid) before = my_hist[id];
@@ -149,10 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
     __syncthreads();
 
-    // ---- 2. scan the per-wave counts, publish the tile's counts ------------
-    uint64_t *st = g.state +
-                   (static_cast<int64_t>(layer) * g.max_tiles) * E;
-    uint64_t *mine = st + static_cast<int64_t>(tile) * E;
+    // ---- 2. wave prefixes and tile counts per expert ------------------------
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
 #pragma unroll
@@ -161,49 +147,33 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             whist[v * E + e] = run;
             run += c;
         }
-        tile_base[e] = run;   // this tile's count until the lookback ends
-        atomic_store_agent(mine + e,
-                           pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg,
-                                      static_cast<uint32_t>(run)));
-    }
-    // ---- 3. lookback over earlier tiles, one expert per thread -------------
-    // Every tile before this one was taken by a workgroup that has started,
-    // and each publishes all its counts before it waits on anything, so the
-    // walk always ends at tile 0 at the latest. The wait is still bounded;
-    // running out of patience is reported as a fault (bit 30 of the count).
-    for (int e = tid; e < E; e += kBlock) {
-        if (tile == 0) {
-            tile_base[e] = 0;
-            continue;
-        }
-        const int run = tile_base[e];
-        uint32_t excl = 0;
-        int t = tile - 1;
-        uint32_t spins = 0;
-        while (true) {
-            const uint64_t v =
-                atomic_load_agent(st + static_cast<int64_t>(t) * E + e);
-            if (static_cast<uint32_t>(v >> 32) != epoch ||
-                ((v >> 30) & 3u) == 0) {
-                if (++spins > g.spin_limit) {
-                    atomicOr(&g.fault_acc[layer], 0x40000000);
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-                continue;
-            }
-            excl += static_cast<uint32_t>(v & 0x3FFFFFFFu);
-            if (((v >> 30) & 3u) == kFlagPrefix || t == 0) break;
-            --t;
-        }
-        atomic_store_agent(mine + e, pack_state(epoch, kFlagPrefix,
-                                                excl + static_cast<uint32_t>(run)));
-        tile_base[e] = static_cast<int32_t>(excl);
+        tcount[e] = run;
+        torder[e] = run;
     }
     __syncthreads();
+    {
+        // exclusive scan of the tile counts over experts (the tile order)
+        const int per = (E + kBlock - 1) / kBlock;
+        const int b = tid * per;
+        const int eend = (b + per < E) ? b + per : E;
+        int local = 0;
+        for (int e = b; e < eend; ++e) local += torder[e];
+        int total;
+        int run = block_exclusive_sum(local, wsum, total);
+        for (int e = b; e < eend; ++e) {
+            const int c = torder[e];
+            torder[e] = run;
+            run += c;
+        }
+    }
+
+    // ---- 3. lookback: count of each expert in earlier tiles -----------------
+    uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
+    const bool bad = tile_lookback(st, tile, E, epoch, tcount, tbase,
+                                   g.spin_limit);
+    const int poisoned = __syncthreads_or(bad);
 
     // ---- 4. outputs ---------------------------------------------------------
-    int nfault = 0;
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
         const int64_t a = a0 + 64 * i;
@@ -211,62 +181,82 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         const int id = ids[i];
         int p = -1, pos = -1;
         if (static_cast<uint32_t>(id) < static_cast<uint32_t>(E)) {
-            const int j = tile_base[id] + my_hist[id] + rank[i];
+            const int jt = my_hist[id] + rank[i];      // j within the tile
+            const int j = tbase[id] + jt;
             for (int r = rep_off[id]; r < rep_off[id + 1]; ++r) {
                 if (j < rep_hi[r]) {
                     if (j >= rep_lo[r] && rep_slot[r] >= 0) {
-                        p = rep_slot[r];
-                        pos = slot_off[p] + (j - rep_lo[r]);
+                        const int q = rep_slot[r];
+                        const int at = slot_off[q] + (j - rep_lo[r]);
+                        if (at >= 0 && at < g.A) {
+                            p = q;
+                            pos = at;
+                        }
                     }
                     break;
                 }
             }
-        }
-        if (p >= 0 && pos >= 0 && pos < g.A) {
-            __builtin_nontemporal_store(static_cast<int32_t>(a),
-                                        g.perm + base + pos);
-            atomicAdd(&rank_hist[p / g.NS], 1);
-        } else {
-            p = -1;
-            pos = -1;
-            ++nfault;
+            const int s = torder[id] + jt;             // tile (expert, j) order
+            stage_a[s] = static_cast<int32_t>(a);
+            stage_pos[s] = pos;
         }
         __builtin_nontemporal_store(p, g.phys + base + a);
         if (g.inv_perm) __builtin_nontemporal_store(pos, g.inv_perm + base + a);
     }
-    int fault_total;
-    block_exclusive_sum(nfault, wsum, fault_total);   // barrier: rank_hist
-    for (int r = tid; r < R; r += kBlock) {
-        const int c = rank_hist[r];
-        if (c) atomicAdd(&g.rank_acc[static_cast<int64_t>(layer) * R + r], c);
-    }
-    if (tid == 0 && fault_total) atomicAdd(&g.fault_acc[layer], fault_total);
-    __threadfence();
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t prev = atomicAdd(&g.done[layer], 1u);
-        s_last = (prev == static_cast<uint32_t>(g.tiles - 1));
+    const int n_valid = torder[E - 1] + tcount[E - 1];
+    for (int s = tid; s < n_valid; s += kBlock) {
+        const int pos = stage_pos[s];
+        if (pos >= 0) g.perm[base + pos] = stage_a[s];
     }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+
+    // ---- 5. last tile: per-rank counts and faults ----------------------------
+    if (tile != g.tiles - 1) return;
+    // Assignments j in [lo, top) of a replica land at slot_off + (j - lo);
+    // those whose position falls outside [0, A) (a plan made for other
+    // counts) are faults like those beyond the expert's capacity.
+    int part_valid = 0, part_over = 0;
+    for (int e = tid; e < E; e += kBlock) {
+        const int total = tbase[e] + tcount[e];
+        part_valid += total;
+        int placed = 0;
+        for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
+            const int lo = rep_lo[r], hi = rep_hi[r];
+            const int top = total < hi ? total : hi;
+            if (top <= lo || rep_slot[r] < 0) continue;
+            const int64_t first = slot_off[rep_slot[r]];
+            const int64_t n = top - lo;
+            int64_t lo_ok = first < 0 ? -first : 0;
+            int64_t hi_ok = g.A - first < n ? g.A - first : n;
+            const int in_range = hi_ok > lo_ok ? static_cast<int>(hi_ok - lo_ok) : 0;
+            if (in_range) atomicAdd(&rank_hist[rep_slot[r] / g.NS], in_range);
+            placed += in_range;
+        }
+        part_over += total - placed;
+    }
+    int tot_valid, tot_over;
+    block_exclusive_sum(part_valid, wsum, tot_valid);
+    block_exclusive_sum(part_over, wsum, tot_over);
     for (int r = tid; r < R; r += kBlock)
-        g.rank_counts[static_cast<int64_t>(layer) * R + r] =
-            atomicExch(&g.rank_acc[static_cast<int64_t>(layer) * R + r], 0);
-    if (tid == 0) {
-        const int f = atomicExch(&g.fault_acc[layer], 0);
-        if (g.faults) g.faults[layer] = f;
-        atomic_store_agent(&g.ticket[layer], 0u);
-        atomic_store_agent(&g.done[layer], 0u);
-        atomic_store_agent(&g.epoch[layer], epoch);
-    }
+        g.rank_counts[static_cast<int64_t>(layer) * R + r] = rank_hist[r];
+    if (tid == 0 && g.faults)
+        g.faults[layer] = static_cast<int32_t>(g.A - tot_valid + tot_over) |
+                          (poisoned ? kPoisonBit : 0);
 }
 
 }  // namespace
 
 size_t reroute_lds_bytes(int E, int R, int P) {
-    return sizeof(int32_t) *
-           (static_cast<size_t>(kWaves + 2) * E + 1 + 4 * P + R);
+    // whist, tcount, torder, tbase, rep_off (+1), four P-sized tables,
+    // the rank histogram and the two staging arrays
+    return sizeof(int32_t) * (static_cast<size_t>(kWaves + 4) * E + 1 + 4 * P +
+                              R + 2 * kRerouteTile);
+}
+
+hipError_t reroute_prepare(size_t lds_bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_reroute),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               static_cast<int>(lds_bytes));
 }
 
 hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
@@ -287,16 +277,14 @@ hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
     g.tiles = tiles;
     g.max_tiles = c.max_rr_tiles;
     g.spin_limit = 1u << 22;
+    g.lds_bytes = static_cast<uint32_t>(c.reroute_lds);
     g.lay = c.lay;
     g.phys = phys;
     g.perm = perm;
     g.inv_perm = inv_perm;
     g.state = c.scan_state;
     g.ticket = c.rr_ticket;
-    g.done = c.rr_done;
     g.epoch = c.rr_epoch;
-    g.rank_acc = c.rr_rank_acc;
-    g.fault_acc = c.rr_fault_acc;
     g.rank_counts = rank_counts;
     g.faults = faults;
     hipLaunchKernelGGL(k_reroute, dim3(tiles, L), dim3(kBlock), c.reroute_lds,

@@ -125,12 +125,17 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
 
     c->plan_lds = ue::plan_lds_bytes(E, R, c->P);
     c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P);
-    const size_t lds_cap = prop.sharedMemPerBlock;
-    if (c->plan_lds + 64 > lds_cap || c->reroute_lds + 64 > lds_cap) {
+    size_t lds_cap = prop.sharedMemPerBlock;
+    if (prop.sharedMemPerBlockOptin > lds_cap)
+        lds_cap = prop.sharedMemPerBlockOptin;
+    if (c->plan_lds + 256 > lds_cap || c->reroute_lds + 256 > lds_cap ||
+        ue::load_lds_bytes(E) + 256 > lds_cap) {
         delete c;
         return UE_EUNSUPPORTED;
     }
-    if (c->plan_lds > 65536 && ue::plan_prepare(c->plan_lds) != hipSuccess) {
+    if ((c->plan_lds > 65536 && ue::plan_prepare(c->plan_lds) != hipSuccess) ||
+        (c->reroute_lds > 65536 &&
+         ue::reroute_prepare(c->reroute_lds) != hipSuccess)) {
         delete c;
         return UE_EUNSUPPORTED;
     }
@@ -138,7 +143,10 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     const int Lmax = cfg->max_layers;
     int64_t rr_tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
     if (rr_tiles < 1) rr_tiles = 1;
+    int64_t ld_tiles = (A + ue::kLoadTile - 1) / ue::kLoadTile;
+    if (ld_tiles < 1) ld_tiles = 1;
     c->max_rr_tiles = static_cast<int>(rr_tiles);
+    c->max_load_tiles = static_cast<int>(ld_tiles);
 
     // Workspace carve-up, each piece 256-byte aligned.
     size_t off = 0;
@@ -147,15 +155,12 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         off = round_up(off + bytes, 256);
         return o;
     };
-    const size_t o_load_acc = take(sizeof(int32_t) * Lmax * E);
-    const size_t o_load_inv = take(sizeof(int32_t) * Lmax);
-    const size_t o_load_done = take(sizeof(uint32_t) * Lmax);
+    const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_tiles * E);
+    const size_t o_lticket = take(sizeof(uint32_t) * Lmax);
+    const size_t o_lepoch = take(sizeof(uint32_t) * Lmax);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_ticket = take(sizeof(uint32_t) * Lmax);
-    const size_t o_done = take(sizeof(uint32_t) * Lmax);
     const size_t o_epoch = take(sizeof(uint32_t) * Lmax);
-    const size_t o_rank = take(sizeof(int32_t) * Lmax * R);
-    const size_t o_fault = take(sizeof(int32_t) * Lmax);
     c->ws_bytes = off;
     he = hipMalloc(&c->ws, c->ws_bytes);
     if (he != hipSuccess) {
@@ -170,15 +175,12 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         return UE_EHIP;
     }
     char *b = static_cast<char *>(c->ws);
-    c->load_acc = reinterpret_cast<int32_t *>(b + o_load_acc);
-    c->load_inv = reinterpret_cast<int32_t *>(b + o_load_inv);
-    c->load_done = reinterpret_cast<uint32_t *>(b + o_load_done);
+    c->load_state = reinterpret_cast<uint64_t *>(b + o_lstate);
+    c->load_ticket = reinterpret_cast<uint32_t *>(b + o_lticket);
+    c->load_epoch = reinterpret_cast<uint32_t *>(b + o_lepoch);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_ticket = reinterpret_cast<uint32_t *>(b + o_ticket);
-    c->rr_done = reinterpret_cast<uint32_t *>(b + o_done);
     c->rr_epoch = reinterpret_cast<uint32_t *>(b + o_epoch);
-    c->rr_rank_acc = reinterpret_cast<int32_t *>(b + o_rank);
-    c->rr_fault_acc = reinterpret_cast<int32_t *>(b + o_fault);
     *out = c;
     return UE_OK;
 }

@@ -38,20 +38,19 @@ struct ue_ctx {
     ue_placement_layout lay{};
     int max_rr_tiles = 0;   // reroute tiles of the largest layer
 
-    // One device allocation holds the whole workspace; the counters and
-    // accumulators below are zero between calls (each kernel's last
-    // workgroup returns them to zero).
+    // One device allocation holds the whole workspace: per-tile lookback
+    // words and, per layer, a tile ticket and a call epoch for each of the
+    // two scanning kernels. Tickets return to zero at the end of every
+    // launch and epochs only grow, so nothing is cleared between calls.
     void *ws = nullptr;
     size_t ws_bytes = 0;
-    int32_t *load_acc = nullptr;   // [max_layers][E]
-    int32_t *load_inv = nullptr;   // [max_layers]
-    uint32_t *load_done = nullptr; // [max_layers]
+    int max_load_tiles = 0;        // load tiles of the largest layer
+    uint64_t *load_state = nullptr;// [max_layers][max_load_tiles][E]
+    uint32_t *load_ticket = nullptr;// [max_layers]
+    uint32_t *load_epoch = nullptr;// [max_layers]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint32_t *rr_ticket = nullptr; // [max_layers]
-    uint32_t *rr_done = nullptr;   // [max_layers]
     uint32_t *rr_epoch = nullptr;  // [max_layers]
-    int32_t *rr_rank_acc = nullptr;// [max_layers][R]
-    int32_t *rr_fault_acc = nullptr;// [max_layers]
 
     size_t plan_lds = 0;
     size_t reroute_lds = 0;
@@ -91,11 +90,12 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
                               const int32_t *inv_perm, int T, int k, int H,
                               void *out, hipStream_t s);
 
+size_t load_lds_bytes(int E);
 size_t plan_lds_bytes(int E, int R, int P);
-// Raise the dynamic LDS limit of the planner kernel when it needs more
-// than 64 KiB.
-hipError_t plan_prepare(size_t lds_bytes);
 size_t reroute_lds_bytes(int E, int R, int P);
+// Raise the dynamic LDS limit of a kernel that needs more than 64 KiB.
+hipError_t plan_prepare(size_t lds_bytes);
+hipError_t reroute_prepare(size_t lds_bytes);
 
 // ---------------------------------------------------------------------
 // wave64 helpers
@@ -168,6 +168,18 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum,
     return before + x - v;
 }
 
+// Set of lanes holding the same value as this lane, among lanes where
+// `valid`: one ballot per bit of the value (values < 2^bits).
+__device__ __forceinline__ uint64_t match_peers(int v, bool valid, int bits) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (v >> b) & 1;
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
+    }
+    return peers;
+}
+
 __device__ __forceinline__ uint64_t atomic_load_agent(const uint64_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -179,6 +191,98 @@ __device__ __forceinline__ uint32_t atomic_load_agent(const uint32_t *p) {
 }
 __device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------
+// Decoupled lookback across the tiles of one layer.
+//
+// A tile publishes, per bin, a 64-bit word {epoch:32 | flag:2 | value:30}:
+// first its own count (flag AGG, or PREFIX for tile 0), then, after walking
+// back over earlier tiles until it meets a PREFIX, its inclusive prefix.
+// Words of earlier calls carry an older epoch and are never taken for
+// current ones, so nothing is cleared between calls. A wait that outlasts
+// `spin_limit` polls gives up and publishes POISON instead, which every
+// later tile propagates; callers report it.
+constexpr uint32_t kFlagAgg = 1;
+constexpr uint32_t kFlagPrefix = 2;
+constexpr uint32_t kFlagPoison = 3;
+constexpr uint32_t kValueMask = 0x3FFFFFFFu;
+constexpr int32_t kPoisonBit = 0x40000000;   // reported in fault counts
+
+__device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint32_t flag,
+                                               uint32_t value) {
+    return (static_cast<uint64_t>(epoch) << 32) |
+           (static_cast<uint64_t>(flag) << 30) | (value & kValueMask);
+}
+
+// Every thread calls it. `st` points at the layer's words [tiles][nbins];
+// `cnt` (LDS) holds this tile's per-bin counts; on return `excl` (LDS) holds
+// the per-bin count of all earlier tiles (visible after the caller's
+// barrier). Returns true in a thread that saw a poisoned or timed-out wait.
+__device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
+                                              int nbins, uint32_t epoch,
+                                              const int32_t *cnt,
+                                              int32_t *excl,
+                                              uint32_t spin_limit) {
+    const int tid = threadIdx.x;
+    uint64_t *mine = st + static_cast<int64_t>(tile) * nbins;
+    for (int b = tid; b < nbins; b += kBlock)
+        atomic_store_agent(mine + b,
+                           pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg,
+                                      static_cast<uint32_t>(cnt[b])));
+    bool poisoned = false;
+    for (int b = tid; b < nbins; b += kBlock) {
+        if (tile == 0) {
+            excl[b] = 0;
+            continue;
+        }
+        uint32_t acc = 0;
+        bool bad = false;
+        int t = tile - 1;
+        uint32_t spins = 0;
+        while (true) {
+            const uint64_t v =
+                atomic_load_agent(st + static_cast<int64_t>(t) * nbins + b);
+            const uint32_t flag = static_cast<uint32_t>(v >> 30) & 3u;
+            if (static_cast<uint32_t>(v >> 32) != epoch || flag == 0) {
+                if (++spins > spin_limit) {
+                    bad = true;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+                continue;
+            }
+            acc += static_cast<uint32_t>(v) & kValueMask;
+            if (flag == kFlagPoison) {
+                bad = true;
+                break;
+            }
+            if (flag == kFlagPrefix || t == 0) break;
+            --t;
+            spins = 0;
+        }
+        atomic_store_agent(mine + b,
+                           pack_state(epoch, bad ? kFlagPoison : kFlagPrefix,
+                                      acc + static_cast<uint32_t>(cnt[b])));
+        excl[b] = static_cast<int32_t>(acc);
+        poisoned |= bad;
+    }
+    return poisoned;
+}
+
+// Tile ticket and call epoch of one launch over one layer. Tickets come
+// from atomicInc with wrap-around at tiles-1, so a complete launch leaves the
+// counter at zero without any reset. Every workgroup reads the epoch before
+// it takes its ticket; the holder of the last ticket then stores the new
+// epoch, after every other workgroup of the launch has read the old one.
+__device__ __forceinline__ void take_ticket(uint32_t *ticket, uint32_t *epoch,
+                                            int tiles, uint32_t &my_ticket,
+                                            uint32_t &my_epoch) {
+    const uint32_t e = atomic_load_agent(epoch) + 1u;
+    const uint32_t t = atomicInc(ticket, static_cast<uint32_t>(tiles - 1));
+    if (t == static_cast<uint32_t>(tiles - 1)) atomic_store_agent(epoch, e);
+    my_ticket = t;
+    my_epoch = e;
 }
 
 }  // namespace ue
