@@ -45,7 +45,8 @@ def events(n):
 
 
 class Rebalance:
-    """Preallocated buffers and the three ABI calls of one rebalance."""
+    """Preallocated buffers and the one ABI call of a rebalance
+    (ue_rebalance: load -> plan -> reroute on the stream)."""
 
     def __init__(self, ue, cfg, routing, dev):
         import torch
@@ -55,27 +56,18 @@ class Rebalance:
                               T, L, device=dev)
         self.routing = routing
         i32 = dict(dtype=torch.int32, device=dev)
-        self.counts = torch.empty((L, cfg.experts), **i32)
-        self.placement = self.ctx.new_placement(L)
-        self.out = dict(phys=torch.empty((L, T, k), **i32),
+        self.out = dict(counts=torch.empty((L, cfg.experts), **i32),
+                        invalid=torch.empty((L,), **i32),
+                        placement=self.ctx.new_placement(L),
+                        phys=torch.empty((L, T, k), **i32),
                         rank_counts=torch.empty((L, cfg.ranks), **i32),
                         perm=torch.empty((L, T * k), **i32),
                         inv_perm=torch.empty((L, T * k), **i32),
                         faults=torch.empty((L,), **i32))
-
-    def load(self):
-        self.ue.ue_load(self.ctx, self.routing, self.counts)
-
-    def plan(self):
-        self.ue.ue_plan(self.ctx, self.counts, self.placement)
-
-    def reroute(self):
-        self.ue.ue_reroute(self.ctx, self.routing, self.placement, **self.out)
+        self.placement = self.out["placement"]
 
     def step(self):
-        self.load()
-        self.plan()
-        self.reroute()
+        self.ue.ue_rebalance(self.ctx, self.routing, **self.out)
 
 
 def time_steps(fn, steps, warmup):
@@ -93,25 +85,18 @@ def time_steps(fn, steps, warmup):
 
 
 def phase_times(rb, steps):
-    """Per-kernel durations from events recorded around each launch on the
-    launch stream (torch's current stream), averaged over ``steps``."""
-    import torch
-    ev = [events(4) for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record()
-        rb.load()
-        ev[i][1].record()
-        rb.plan()
-        ev[i][2].record()
-        rb.reroute()
-        ev[i][3].record()
-    torch.cuda.synchronize()
+    """Per-kernel durations of the rebalance, from the HIP events the
+    library records on the launch stream around each kernel, averaged over
+    ``steps`` calls."""
+    ue = rb.ue
+    ue.ue_set_timing(rb.ctx, True)
     t = {"k_load": [], "k_plan": [], "k_reroute": []}
-    for e in ev:
-        t["k_load"].append(e[0].elapsed_time(e[1]))
-        t["k_plan"].append(e[1].elapsed_time(e[2]))
-        t["k_reroute"].append(e[2].elapsed_time(e[3]))
+    for _ in range(steps):
+        rb.step()
+        ms = ue.ue_kernel_times(rb.ctx)
+        for name, v in zip(t, ms):
+            t[name].append(v)
+    ue.ue_set_timing(rb.ctx, False)
     return {k: statistics.mean(v) for k, v in t.items()}
 
 
@@ -139,7 +124,7 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     rb = Rebalance(ue, cfg, routing, dev)
     rb.step()
     torch.cuda.synchronize()
-    assert int(rb.out["faults"].sum()) == 0
+    assert int(rb.out["faults"].sum()) == 0 and int(rb.out["invalid"].sum()) == 0
     log(f"dsv3: timing {steps} steps after {warmup} warmup")
     ms = time_steps(rb.step, steps, warmup)
     phases = phase_times(rb, max(steps, 10))
@@ -283,7 +268,8 @@ def main():
     n_assign = L * cfg.assignments
     value = n_assign / (ms * 1e-3)
     # dominant kernel: the reroute pass; algorithmic bytes per assignment:
-    # read the id (4) + write phys, perm and inv_perm (12)
+    # read the id (4) + write phys, perm and inv_perm (12). The tile
+    # prefixes it reads (E words per tile) are not counted.
     rr_ms = phases["k_reroute"]
     rr_bytes = 16 * n_assign
     achieved = rr_bytes / (rr_ms * 1e-3) / 1e9
@@ -302,7 +288,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "dsv3 routing: E=256, k=8, R=64 "
                                "(4 native + 1 spare), T=65536, 58 layers "
-                               "batched; load+plan+reroute",
+                               "batched; one ue_rebalance (load, plan, "
+                               "reroute + dispatch layout)",
                    "layers": L, "tokens": cfg.tokens, "experts": cfg.experts,
                    "topk": cfg.topk, "ranks": cfg.ranks,
                    "spare_per_rank": cfg.spare},

@@ -174,6 +174,30 @@ int ue_reroute(ue_ctx *ctx, const int32_t *routing, const void *placement,
                int32_t *perm, int32_t *inv_perm, int32_t *faults,
                void *stream);
 
+/* One rebalance of L layers in one call: ue_load, ue_plan and ue_reroute
+ * with the same arguments and results as those three calls in a row (every
+ * output of each is an output here; invalid and inv_perm may be NULL). The
+ * pages rebalance right after gating, on the critical path, for every
+ * microbatch and layer; this entry point is that path as three launches
+ * with no host work between them. The reroute reuses the per-tile expert
+ * prefixes the load kernel publishes, so it reads the routing once more but
+ * never waits on another workgroup. Arguments are validated before the first
+ * launch; a refusal leaves every output untouched. */
+int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
+                 int32_t *counts, int32_t *invalid, void *placement,
+                 int32_t *phys, int32_t *rank_counts, int32_t *perm,
+                 int32_t *inv_perm, int32_t *faults, void *stream);
+
+/* Kernel timing. With timing enabled, every call records a HIP event on its
+ * stream before its first kernel and after each kernel it launches.
+ * ue_kernel_times waits for the latest call's last event and writes the
+ * duration in milliseconds of each of its kernels, in launch order, to
+ * ms[0 .. *n-1] (at most max_n values; *n is the number that call launched).
+ * Off by default; enabling it costs one event per kernel. Errors:
+ * UE_ESTATE if timing is off or no call has run since it was enabled. */
+int ue_set_timing(ue_ctx *ctx, int enable);
+int ue_kernel_times(ue_ctx *ctx, float *ms, int32_t max_n, int32_t *n);
+
 /* ---------------------------------------------------------------------
  * Expert state ("registers expert pointers"). Stores device pointers to
  * n_experts master experts and n_buffers replica buffers, each made of

@@ -7,6 +7,7 @@ raises at import of the first call if ``libue.so`` is not built; there is no
 fallback implementation.
 
 Functions carry the C names (``ue_load``, ``ue_plan``, ``ue_reroute``,
+``ue_rebalance``,
 ``ue_weight_sync``, ``ue_grad_reduce``, ``ue_gather_rows``, ...) and take a
 :class:`Context` plus torch tensors; :class:`Context` also exposes them as
 methods without the prefix.
@@ -65,6 +66,11 @@ SIGNATURES = {
     "ue_plan": (ctypes.c_int, [_vp, _vp, _i32, _vp, _vp]),
     "ue_reroute": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp,
                                   _vp, _vp, _vp]),
+    "ue_rebalance": (ctypes.c_int, [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, _vp, _vp, _vp]),
+    "ue_set_timing": (ctypes.c_int, [_vp, ctypes.c_int]),
+    "ue_kernel_times": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_float),
+                                       _i32, ctypes.POINTER(_i32)]),
     "ue_register_experts": (ctypes.c_int, [_vp, _i32, _i32,
                                            ctypes.POINTER(_i64),
                                            ctypes.POINTER(_vp),
@@ -193,6 +199,9 @@ class Context:
     def reroute(self, routing, placement, **kw):
         return ue_reroute(self, routing, placement, **kw)
 
+    def rebalance(self, routing, **kw):
+        return ue_rebalance(self, routing, **kw)
+
     def register_experts(self, *a, **kw):
         return ue_register_experts(self, *a, **kw)
 
@@ -299,6 +308,58 @@ def ue_reroute(ctx: Context, routing, placement, phys=None, rank_counts=None,
                               _stream(stream, dev))
     ctx._check(rc, "ue_reroute")
     return dict(phys=phys, rank_counts=rank_counts, perm=perm,
+                inv_perm=inv_perm, faults=faults)
+
+
+def ue_set_timing(ctx: Context, enable: bool = True):
+    ctx._check(library().ue_set_timing(ctx._h, int(bool(enable))),
+               "ue_set_timing")
+
+
+def ue_kernel_times(ctx: Context) -> list:
+    """Durations (ms) of the kernels of the latest timed call."""
+    ms = (ctypes.c_float * 8)()
+    n = ctypes.c_int32()
+    ctx._check(library().ue_kernel_times(ctx._h, ms, 8, ctypes.byref(n)),
+               "ue_kernel_times")
+    return [ms[i] for i in range(n.value)]
+
+
+def ue_rebalance(ctx: Context, routing, counts=None, invalid=None,
+                 placement=None, phys=None, rank_counts=None, perm=None,
+                 inv_perm=None, faults=None, with_inv=True, stream=None):
+    """load -> plan -> reroute in one call (see ``ue_rebalance`` in ue.h).
+    Returns a dict with every output tensor."""
+    routing, L, T = _routing_shape(ctx, routing)
+    _need(routing, "routing", torch.int32, ctx.device)
+    A = T * ctx.k
+    dev = ctx.device
+
+    def mk(t, shape, name, need=True):
+        if t is None and need:
+            t = torch.empty(shape, dtype=torch.int32, device=dev)
+        if t is not None:
+            n = 1
+            for s in shape:
+                n *= s
+            _need(t, name, torch.int32, dev, n)
+        return t
+
+    counts = mk(counts, (L, ctx.E), "counts")
+    invalid = mk(invalid, (L,), "invalid")
+    placement = mk(placement, (L, ctx.placement_words), "placement")
+    phys = mk(phys, (L, T, ctx.k), "phys")
+    rank_counts = mk(rank_counts, (L, ctx.R), "rank_counts")
+    perm = mk(perm, (L, A), "perm")
+    inv_perm = mk(inv_perm, (L, A), "inv_perm", with_inv)
+    faults = mk(faults, (L,), "faults")
+    rc = library().ue_rebalance(ctx._h, _ptr(routing), L, T, _ptr(counts),
+                                _ptr(invalid), _ptr(placement), _ptr(phys),
+                                _ptr(rank_counts), _ptr(perm), _ptr(inv_perm),
+                                _ptr(faults), _stream(stream, dev))
+    ctx._check(rc, "ue_rebalance")
+    return dict(counts=counts, invalid=invalid, placement=placement,
+                phys=phys, rank_counts=rank_counts, perm=perm,
                 inv_perm=inv_perm, faults=faults)
 
 

@@ -45,6 +45,17 @@ bool aligned(const void *p, size_t a) {
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Kernel timing: tbegin() before a call's first launch, tmark() after each.
+void tbegin(ue_ctx *c, hipStream_t s) {
+    if (!c->timing) return;
+    c->n_ev = 0;
+    if (hipEventRecord(c->ev[c->n_ev], s) == hipSuccess) ++c->n_ev;
+}
+void tmark(ue_ctx *c, hipStream_t s) {
+    if (!c->timing || c->n_ev == 0 || c->n_ev >= ue_ctx::kMaxEvents) return;
+    if (hipEventRecord(c->ev[c->n_ev], s) == hipSuccess) ++c->n_ev;
+}
+
 }  // namespace
 
 extern "C" {
@@ -124,7 +135,7 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
 
     c->plan_lds = ue::plan_lds_bytes(E, R, c->P);
-    c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P);
+    c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P, k);
     size_t lds_cap = prop.sharedMemPerBlock;
     if (prop.sharedMemPerBlockOptin > lds_cap)
         lds_cap = prop.sharedMemPerBlockOptin;
@@ -156,11 +167,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         return o;
     };
     const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_tiles * E);
-    const size_t o_lticket = take(sizeof(uint32_t) * Lmax);
-    const size_t o_lepoch = take(sizeof(uint32_t) * Lmax);
+    const size_t o_ltick = take(sizeof(uint64_t) * Lmax);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
-    const size_t o_ticket = take(sizeof(uint32_t) * Lmax);
-    const size_t o_epoch = take(sizeof(uint32_t) * Lmax);
+    const size_t o_tick = take(sizeof(uint64_t) * Lmax);
     c->ws_bytes = off;
     he = hipMalloc(&c->ws, c->ws_bytes);
     if (he != hipSuccess) {
@@ -176,11 +185,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     }
     char *b = static_cast<char *>(c->ws);
     c->load_state = reinterpret_cast<uint64_t *>(b + o_lstate);
-    c->load_ticket = reinterpret_cast<uint32_t *>(b + o_lticket);
-    c->load_epoch = reinterpret_cast<uint32_t *>(b + o_lepoch);
+    c->load_tick = reinterpret_cast<uint64_t *>(b + o_ltick);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
-    c->rr_ticket = reinterpret_cast<uint32_t *>(b + o_ticket);
-    c->rr_epoch = reinterpret_cast<uint32_t *>(b + o_epoch);
+    c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
     *out = c;
     return UE_OK;
 }
@@ -190,6 +197,8 @@ void ue_destroy(ue_ctx *ctx) {
     (void)hipDeviceSynchronize();
     if (ctx->ws) (void)hipFree(ctx->ws);
     if (ctx->reg_tables) (void)hipFree(ctx->reg_tables);
+    for (auto &e : ctx->ev)
+        if (e) (void)hipEventDestroy(e);
     delete ctx;
 }
 
@@ -201,6 +210,38 @@ int ue_get_placement_layout(const ue_ctx *ctx, ue_placement_layout *out) {
 
 size_t ue_placement_bytes(const ue_ctx *ctx) {
     return ctx ? static_cast<size_t>(ctx->lay.words) * sizeof(int32_t) : 0;
+}
+
+int ue_set_timing(ue_ctx *ctx, int enable) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (enable && !ctx->ev[0]) {
+        for (auto &e : ctx->ev) {
+            hipError_t he = hipEventCreate(&e);
+            if (he != hipSuccess) return hip_fail(ctx, he, "hipEventCreate");
+        }
+    }
+    ctx->timing = enable != 0;
+    ctx->n_ev = 0;
+    return UE_OK;
+}
+
+int ue_kernel_times(ue_ctx *ctx, float *ms, int32_t max_n, int32_t *n) {
+    if (!ctx || !ms || !n || max_n < 0) return UE_EINVAL;
+    ctx->err.clear();
+    if (!ctx->timing || ctx->n_ev < 2)
+        return fail(ctx, UE_ESTATE, "no timed call");
+    hipError_t he = hipEventSynchronize(ctx->ev[ctx->n_ev - 1]);
+    if (he != hipSuccess) return hip_fail(ctx, he, "hipEventSynchronize");
+    const int k = ctx->n_ev - 1;
+    for (int i = 0; i < k && i < max_n; ++i) {
+        float t = 0.f;
+        he = hipEventElapsedTime(&t, ctx->ev[i], ctx->ev[i + 1]);
+        if (he != hipSuccess) return hip_fail(ctx, he, "hipEventElapsedTime");
+        ms[i] = t;
+    }
+    *n = k;
+    return UE_OK;
 }
 
 static int check_LT(ue_ctx *c, int32_t L, int32_t T) {
@@ -221,8 +262,10 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
     if (!aligned(routing, 4) || !aligned(counts, 4) || !aligned(invalid, 4))
         return fail(ctx, UE_EINVAL, "ue_load: int32 arrays must be 4-byte aligned");
     const int64_t A = static_cast<int64_t>(T) * ctx->k;
-    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid,
-                                    static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid, s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_load launch");
 }
 
@@ -236,9 +279,11 @@ int ue_plan(ue_ctx *ctx, const int32_t *counts, int32_t L, void *placement,
         return fail(ctx, UE_EINVAL, "ue_plan: null counts or placement");
     if (!aligned(counts, 4) || !aligned(placement, 4))
         return fail(ctx, UE_EINVAL, "ue_plan: arrays must be 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
     hipError_t he = ue::launch_plan(*ctx, counts, L,
-                                    static_cast<int32_t *>(placement),
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<int32_t *>(placement), s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_plan launch");
 }
 
@@ -256,9 +301,44 @@ int ue_reroute(ue_ctx *ctx, const int32_t *routing, const void *placement,
         !aligned(inv_perm, 4) || !aligned(faults, 4))
         return fail(ctx, UE_EINVAL, "ue_reroute: arrays must be 4-byte aligned");
     const int64_t A = static_cast<int64_t>(T) * ctx->k;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
     hipError_t he = ue::launch_reroute(
         *ctx, routing, static_cast<const int32_t *>(placement), L, A, phys,
-        rank_counts, perm, inv_perm, faults, static_cast<hipStream_t>(stream));
+        rank_counts, perm, inv_perm, faults, s);
+    tmark(ctx, s);
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_reroute launch");
+}
+
+int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
+                 int32_t *counts, int32_t *invalid, void *placement,
+                 int32_t *phys, int32_t *rank_counts, int32_t *perm,
+                 int32_t *inv_perm, int32_t *faults, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (int rc = check_LT(ctx, L, T)) return rc;
+    if (!counts || !placement || !rank_counts ||
+        (T > 0 && (!routing || !phys || !perm)))
+        return fail(ctx, UE_EINVAL, "ue_rebalance: null required pointer");
+    if (!aligned(routing, 4) || !aligned(counts, 4) || !aligned(invalid, 4) ||
+        !aligned(placement, 4) || !aligned(phys, 4) ||
+        !aligned(rank_counts, 4) || !aligned(perm, 4) ||
+        !aligned(inv_perm, 4) || !aligned(faults, 4))
+        return fail(ctx, UE_EINVAL,
+                    "ue_rebalance: arrays must be 4-byte aligned");
+    const int64_t A = static_cast<int64_t>(T) * ctx->k;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid, s);
+    if (he != hipSuccess) return hip_fail(ctx, he, "k_load launch");
+    tmark(ctx, s);
+    he = ue::launch_plan(*ctx, counts, L, static_cast<int32_t *>(placement), s);
+    if (he != hipSuccess) return hip_fail(ctx, he, "k_plan launch");
+    tmark(ctx, s);
+    he = ue::launch_reroute_after_load(
+        *ctx, routing, static_cast<const int32_t *>(placement), L, A, phys,
+        rank_counts, perm, inv_perm, faults, s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_reroute launch");
 }
 
@@ -364,8 +444,10 @@ int ue_weight_sync(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
     if (int rc = check_stream_call(ctx, rep_off, rep_buf, n_experts, true))
         return rc;
     if (n_experts == 0) return UE_OK;
-    hipError_t he = ue::launch_weight_sync(*ctx, rep_off, rep_buf, n_experts,
-                                           static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_weight_sync(*ctx, rep_off, rep_buf, n_experts, s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_weight_sync launch");
 }
 
@@ -376,8 +458,10 @@ int ue_grad_reduce(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
     if (int rc = check_stream_call(ctx, rep_off, rep_buf, n_experts, false))
         return rc;
     if (n_experts == 0) return UE_OK;
-    hipError_t he = ue::launch_grad_reduce(*ctx, rep_off, rep_buf, n_experts,
-                                           static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_grad_reduce(*ctx, rep_off, rep_buf, n_experts, s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_grad_reduce launch");
 }
 
@@ -394,8 +478,10 @@ int ue_gather_rows(ue_ctx *ctx, const void *x, const int32_t *inv_perm,
     if (!aligned(x, 16) || !aligned(out, 16) || !aligned(inv_perm, 4))
         return fail(ctx, UE_EINVAL, "ue_gather_rows: x/out need 16-byte alignment");
     if (H == 0) return UE_OK;
-    hipError_t he = ue::launch_gather_rows(*ctx, x, inv_perm, T, k, H, out,
-                                           static_cast<hipStream_t>(stream));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_gather_rows(*ctx, x, inv_perm, T, k, H, out, s);
+    tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_gather_rows launch");
 }
 

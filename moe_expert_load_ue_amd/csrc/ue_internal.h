@@ -18,13 +18,13 @@ constexpr int kMaxMats = 16;
 constexpr int kBlock = 256;          // threads per workgroup (4 waves)
 constexpr int kWaves = kBlock / 64;
 
-// Routing tiles. A load tile covers kLoadItems ids per thread; a reroute
-// tile covers kRerouteItems ids per thread, processed as kRerouteItems
-// rounds of 64 consecutive ids per wave.
-constexpr int kLoadItems = 32;
-constexpr int kLoadTile = kBlock * kLoadItems;
+// Routing tiles: kRerouteItems assignments per thread, processed as rounds
+// of 64 consecutive assignments per wave. The load kernel uses the same
+// tiles, so the per-tile prefixes it publishes serve the fused reroute.
 constexpr int kRerouteItems = 16;
 constexpr int kRerouteTile = kBlock * kRerouteItems;
+constexpr int kLoadItems = kRerouteItems;
+constexpr int kLoadTile = kRerouteTile;
 
 }  // namespace ue
 
@@ -46,11 +46,9 @@ struct ue_ctx {
     size_t ws_bytes = 0;
     int max_load_tiles = 0;        // load tiles of the largest layer
     uint64_t *load_state = nullptr;// [max_layers][max_load_tiles][E]
-    uint32_t *load_ticket = nullptr;// [max_layers]
-    uint32_t *load_epoch = nullptr;// [max_layers]
+    uint64_t *load_tick = nullptr; // [max_layers] {epoch:32 | ticket:32}
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
-    uint32_t *rr_ticket = nullptr; // [max_layers]
-    uint32_t *rr_epoch = nullptr;  // [max_layers]
+    uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
 
     size_t plan_lds = 0;
     size_t reroute_lds = 0;
@@ -64,6 +62,12 @@ struct ue_ctx {
     float **d_master_g = nullptr;
     void **d_spare_w = nullptr;
     float **d_spare_g = nullptr;
+
+    // Kernel timing (off unless ue_set_timing enabled it).
+    static constexpr int kMaxEvents = 8;
+    bool timing = false;
+    hipEvent_t ev[kMaxEvents] = {};
+    int n_ev = 0;
 
     std::string err;
 };
@@ -80,6 +84,15 @@ hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
                           const int32_t *placement, int L, int64_t A,
                           int32_t *phys, int32_t *rank_counts, int32_t *perm,
                           int32_t *inv_perm, int32_t *faults, hipStream_t s);
+// Reroute that takes each tile's expert prefix from the load kernel's
+// published words instead of its own lookback (the routing must be the one
+// the immediately preceding launch_load counted).
+hipError_t launch_reroute_after_load(const ue_ctx &c, const int32_t *routing,
+                                     const int32_t *placement, int L,
+                                     int64_t A, int32_t *phys,
+                                     int32_t *rank_counts, int32_t *perm,
+                                     int32_t *inv_perm, int32_t *faults,
+                                     hipStream_t s);
 hipError_t launch_weight_sync(const ue_ctx &c, const int32_t *rep_off,
                               const int32_t *rep_buf, int n_experts,
                               hipStream_t s);
@@ -92,7 +105,9 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
 
 size_t load_lds_bytes(int E);
 size_t plan_lds_bytes(int E, int R, int P);
-size_t reroute_lds_bytes(int E, int R, int P);
+size_t reroute_lds_bytes(int E, int R, int P, int k);
+// Words per expert bitmap of the reroute's ranking (0: ranks by matching).
+int reroute_bitmap_words(int E, int k);
 // Raise the dynamic LDS limit of a kernel that needs more than 64 KiB.
 hipError_t plan_prepare(size_t lds_bytes);
 hipError_t reroute_prepare(size_t lds_bytes);
@@ -208,6 +223,7 @@ constexpr uint32_t kFlagPrefix = 2;
 constexpr uint32_t kFlagPoison = 3;
 constexpr uint32_t kValueMask = 0x3FFFFFFFu;
 constexpr int32_t kPoisonBit = 0x40000000;   // reported in fault counts
+constexpr int kLookbackWindow = 8;           // predecessors polled at once
 
 __device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint32_t flag,
                                                uint32_t value) {
@@ -236,30 +252,50 @@ __device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
             excl[b] = 0;
             continue;
         }
+        // Poll a window of kLookbackWindow predecessors per round trip (the
+        // loads are independent), then fold them in from the nearest one:
+        // add AGG values until a PREFIX; a word not yet published restarts
+        // the next window at that tile.
         uint32_t acc = 0;
-        bool bad = false;
+        bool bad = false, done = false;
         int t = tile - 1;
         uint32_t spins = 0;
-        while (true) {
-            const uint64_t v =
-                atomic_load_agent(st + static_cast<int64_t>(t) * nbins + b);
-            const uint32_t flag = static_cast<uint32_t>(v >> 30) & 3u;
-            if (static_cast<uint32_t>(v >> 32) != epoch || flag == 0) {
+        while (!done) {
+            uint64_t v[kLookbackWindow];
+#pragma unroll
+            for (int i = 0; i < kLookbackWindow; ++i)
+                v[i] = (t - i >= 0) ? atomic_load_agent(
+                                          st + static_cast<int64_t>(t - i) * nbins + b)
+                                    : 0;
+            bool stalled = false;
+#pragma unroll
+            for (int i = 0; i < kLookbackWindow; ++i) {
+                if (done || stalled) continue;
+                const uint32_t flag = static_cast<uint32_t>(v[i] >> 30) & 3u;
+                if (static_cast<uint32_t>(v[i] >> 32) != epoch || flag == 0) {
+                    stalled = true;          // resume at tile t (not consumed)
+                    continue;
+                }
+                acc += static_cast<uint32_t>(v[i]) & kValueMask;
+                if (flag == kFlagPoison) {
+                    bad = true;
+                    done = true;
+                } else if (flag == kFlagPrefix || t == 0) {
+                    done = true;
+                } else {
+                    --t;
+                }
+            }
+            if (done) break;
+            if (stalled) {
                 if (++spins > spin_limit) {
                     bad = true;
                     break;
                 }
-                __builtin_amdgcn_s_sleep(2);
-                continue;
+                __builtin_amdgcn_s_sleep(1);
+            } else {
+                spins = 0;
             }
-            acc += static_cast<uint32_t>(v) & kValueMask;
-            if (flag == kFlagPoison) {
-                bad = true;
-                break;
-            }
-            if (flag == kFlagPrefix || t == 0) break;
-            --t;
-            spins = 0;
         }
         atomic_store_agent(mine + b,
                            pack_state(epoch, bad ? kFlagPoison : kFlagPrefix,
@@ -270,19 +306,30 @@ __device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
     return poisoned;
 }
 
-// Tile ticket and call epoch of one launch over one layer. Tickets come
-// from atomicInc with wrap-around at tiles-1, so a complete launch leaves the
-// counter at zero without any reset. Every workgroup reads the epoch before
-// it takes its ticket; the holder of the last ticket then stores the new
-// epoch, after every other workgroup of the launch has read the old one.
-__device__ __forceinline__ void take_ticket(uint32_t *ticket, uint32_t *epoch,
-                                            int tiles, uint32_t &my_ticket,
+// Tile ticket and call epoch of one launch over one layer, from one 64-bit
+// word {epoch:32 | ticket:32} with one atomic: the old value gives this
+// workgroup's ticket and the epoch of the previous call. The holder of the
+// last ticket adds 2^32 - tiles, which carries the ticket count (then equal
+// to tiles) into the epoch: the word returns to {epoch + 1 | 0} after every
+// other workgroup of the launch has taken its ticket and so read the old
+// epoch. The call's own epoch is the old one plus one.
+__device__ __forceinline__ void take_ticket(uint64_t *tick, int tiles,
+                                            uint32_t &my_ticket,
                                             uint32_t &my_epoch) {
-    const uint32_t e = atomic_load_agent(epoch) + 1u;
-    const uint32_t t = atomicInc(ticket, static_cast<uint32_t>(tiles - 1));
-    if (t == static_cast<uint32_t>(tiles - 1)) atomic_store_agent(epoch, e);
+    const uint64_t v = atomicAdd(reinterpret_cast<unsigned long long *>(tick),
+                                 1ull);
+    const uint32_t t = static_cast<uint32_t>(v);
+    if (t == static_cast<uint32_t>(tiles - 1))
+        atomicAdd(reinterpret_cast<unsigned long long *>(tick),
+                  (1ull << 32) - static_cast<uint64_t>(tiles));
     my_ticket = t;
-    my_epoch = e;
+    my_epoch = static_cast<uint32_t>(v >> 32) + 1u;
+}
+
+// Epoch of the latest completed launch over a layer (read by a later
+// kernel, after that launch finished).
+__device__ __forceinline__ uint32_t last_epoch(const uint64_t *tick) {
+    return static_cast<uint32_t>(atomic_load_agent(tick) >> 32);
 }
 
 }  // namespace ue

@@ -22,15 +22,21 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_rebalance(ctx, routing, with_inv=True):
-    """load -> plan -> reroute on the device; returns numpy copies."""
+def gpu_rebalance(ctx, routing, with_inv=True, fused=False):
+    """load -> plan -> reroute on the device, as three calls or as one
+    ue_rebalance call; returns numpy copies."""
     dev = ctx.device
     r = routing.to(dev)
     L = r.shape[0]
     invalid = torch.full((L,), -7, dtype=torch.int32, device=dev)
-    counts = ue.ue_load(ctx, r, invalid=invalid)
-    placement = ue.ue_plan(ctx, counts)
-    out = ue.ue_reroute(ctx, r, placement, with_inv=with_inv)
+    if fused:
+        out = ue.ue_rebalance(ctx, r, invalid=invalid, with_inv=with_inv)
+        counts, placement = out.pop("counts"), out.pop("placement")
+        out.pop("invalid")
+    else:
+        counts = ue.ue_load(ctx, r, invalid=invalid)
+        placement = ue.ue_plan(ctx, counts)
+        out = ue.ue_reroute(ctx, r, placement, with_inv=with_inv)
     torch.cuda.synchronize(dev)
     f = ctx.placement_fields(placement)
     res = dict(counts=counts.cpu().numpy(), invalid=invalid.cpu().numpy(),

@@ -70,17 +70,72 @@ def test_random_instances():
         compare_with_oracle(res, routing, E, R, S)
 
 
+@pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
-def test_configs_full_size(name):
-    """Every routing workload at its full size, every layer, bit-exact."""
+def test_configs_full_size(name, fused):
+    """Every routing workload at its full size, every layer, bit-exact, as
+    three calls and as one ue_rebalance call."""
     cfg = W.CONFIGS[name]
-    say("full size", name)
+    say("full size", name, "fused" if fused else "calls")
     routing = W.make_routing(cfg, device=DEV)
     ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
                    cfg.layers)
-    res = gpu_rebalance(ctx, routing)
+    res = gpu_rebalance(ctx, routing, fused=fused)
     compare_with_oracle(res, routing.cpu().numpy(), cfg.experts, cfg.ranks,
                         cfg.spare)
+
+
+def test_fused_equals_calls_random():
+    """ue_rebalance gives the same bits as ue_load + ue_plan + ue_reroute on
+    random shapes (ragged tails, k not dividing the tile, repeated calls
+    with changing sizes on one context), and matches the oracle."""
+    rng = np.random.default_rng(17)
+    ctx = make_ctx(96, 8, 2, 8, 9000, 3)
+    for it in range(12):
+        T = int(rng.choice([0, 1, 100, 4095, 4096, 4097, 9000]))
+        L = int(rng.integers(1, 4))
+        k = 8
+        routing = np.stack([pins.random_routing(rng, T, 96, k,
+                                                float(rng.uniform(0, 2.5)))
+                            for _ in range(L)])
+        say(f"fused vs calls {it}: T={T} L={L}")
+        a = gpu_rebalance(ctx, torch.from_numpy(routing), fused=True)
+        b = gpu_rebalance(ctx, torch.from_numpy(routing), fused=False)
+        for key in ("counts", "invalid", "placement", "phys", "perm",
+                    "inv_perm", "rank_counts", "faults"):
+            assert np.array_equal(a[key], b[key]), key
+        compare_with_oracle(a, routing, 96, 8, 2)
+
+
+def test_duplicate_expert_in_token():
+    """Top-k never repeats an expert within a token, but the path must stay
+    exact if a token does (those tiles rank by matching lanes)."""
+    rng = np.random.default_rng(21)
+    E, R, S, k, T = 64, 8, 2, 8, 5000
+    routing = pins.random_routing(rng, T, E, k, 1.2)
+    routing[10, 3] = routing[10, 5]
+    routing[4500, 0] = routing[4500, 7]
+    say("duplicates")
+    ctx = make_ctx(E, R, S, k, T)
+    for fused in (False, True):
+        res = gpu_rebalance(ctx, torch.from_numpy(routing[None]), fused=fused)
+        compare_with_oracle(res, routing[None], E, R, S)
+
+
+def test_kernel_times():
+    cfg = W.CONFIGS["tiny"]
+    routing = W.make_routing(cfg, device=DEV)
+    ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens)
+    say("kernel times")
+    with pytest.raises(ue.UEError):
+        ue.ue_kernel_times(ctx)
+    ue.ue_set_timing(ctx, True)
+    ue.ue_rebalance(ctx, routing)
+    t = ue.ue_kernel_times(ctx)
+    assert len(t) == 3 and all(v > 0 for v in t)
+    ue.ue_load(ctx, routing)
+    assert len(ue.ue_kernel_times(ctx)) == 1
+    ue.ue_set_timing(ctx, False)
 
 
 def test_invalid_ids_and_faults():
