@@ -249,6 +249,13 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--only", choices=["rebalance", "large_ep", "stream",
+                                       "gather"], default=None,
+                    help="run one measurement (for profiling); prints its "
+                         "JSON object instead of the contract line")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="with --only: also run a 1 GiB device copy, the "
+                         "reference for scaling byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} given); "
@@ -261,6 +268,30 @@ def main():
     from moe_expert_load_ue_amd import workloads as W
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only:
+        res = {}
+        if args.only == "rebalance":
+            cfg, rb, ms, phases, _ = bench_rebalance(ue, W, dev, args.steps,
+                                                     args.warmup)
+            res = {"ms_per_step": ms,
+                   "kernel_us": {k: v * 1000 for k, v in phases.items()}}
+        elif args.only == "large_ep":
+            res = bench_large_ep(ue, W, dev)
+        elif args.only == "stream":
+            res = bench_stream(ue, W, dev)
+        elif args.only == "gather":
+            res = bench_gather(ue, W, dev)
+        if args.calib_copy:
+            n = (1 << 30) // 4
+            src = torch.ones(n, dtype=torch.float32, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            res["calib_copy_bytes_each_way"] = n * 4
+        print(json.dumps(res), flush=True)
+        return
 
     cfg, rb, ms, phases, ms_one = bench_rebalance(ue, W, dev, args.steps,
                                                   args.warmup)
