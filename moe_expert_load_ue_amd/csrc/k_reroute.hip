@@ -57,8 +57,7 @@ struct RerouteArgs {
     int32_t *phys, *perm, *inv_perm;
     uint64_t *state;           // [max_layers][max_tiles][E] own lookback
     uint64_t *tick;            // [max_layers] own ticket and epoch
-    const uint64_t *load_state;// the load kernel's words (after-load mode)
-    const uint64_t *load_tick; // the load kernel's ticket and epoch
+    const int32_t *tile_prefix;// [max_layers][max_tiles][E] from the load
     int32_t *rank_counts, *faults;
 };
 
@@ -79,10 +78,10 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
     return a > 2 * kRerouteTile ? a : 2 * kRerouteTile;
 }
 
-// kAfterLoad: the tile is blockIdx.x and the count of each expert in
-// earlier tiles is the inclusive prefix the load kernel published for the
-// previous tile (checked against that launch's epoch); otherwise the tile
-// comes from the ticket and the prefix from this kernel's own lookback.
+// kAfterLoad: the count of each expert in earlier tiles is the per-tile
+// prefix the load kernel just wrote, tiles do not depend on each other and
+// workgroup blockIdx.x takes tile blockIdx.x. Otherwise the workgroup takes
+// one tile by ticket and finds the prefix by lookback.
 template <bool kAfterLoad>
 __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     extern __shared__ int32_t lds[];
@@ -116,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     if (kAfterLoad) {
         if (tid == 0) {
             s_ticket = blockIdx.x;
-            s_epoch = last_epoch(g.load_tick + layer);
+            s_epoch = 0;
         }
     } else if (tid == 0) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
@@ -139,11 +138,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const bool bitmap = W > 0;
     int32_t *bm = area;                    // [E][Wp] token bitmaps
     int32_t *bpre = area + E * Wp;         // [E][Wp] popcount prefixes
-    if (bitmap)
-        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = 0;
     __syncthreads();
-    const int tile = static_cast<int>(s_ticket);
-    if (tile >= g.tiles) return;    // only after a corrupted earlier launch
+    if (static_cast<int>(s_ticket) >= g.tiles)
+        return;    // only after a corrupted earlier launch
     // capacity prefix of each replica within its expert, from LDS
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
@@ -155,19 +152,38 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         }
     }
     const uint32_t epoch = s_epoch;
+    const int tile = static_cast<int>(s_ticket);
     const int64_t base = static_cast<int64_t>(layer) * g.A;
     const int64_t tile0 = static_cast<int64_t>(tile) * kRerouteTile;
     const int64_t a0 = tile0 + static_cast<int64_t>(w) * 64 * kRerouteItems +
                        lane;
 
+    // global reads first: the tile's ids and, after a load, its prefixes
     int32_t ids[kRerouteItems];
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
         const int64_t a = a0 + 64 * i;
-        const int id = (a < g.A) ? __builtin_nontemporal_load(g.routing + base + a)
-                                 : -1;
-        ids[i] = static_cast<uint32_t>(id) < static_cast<uint32_t>(E) ? id : -1;
+        ids[i] = (a < g.A) ? __builtin_nontemporal_load(g.routing + base + a)
+                           : -1;
     }
+    constexpr int kPerThread = kMaxExperts / kBlock;
+    int32_t pre_reg[kPerThread];
+    if (kAfterLoad) {
+        const int32_t *tp = g.tile_prefix +
+                            (static_cast<int64_t>(layer) * g.max_tiles + tile) * E;
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int e = tid + q * kBlock;
+            pre_reg[q] = e < E ? tp[e] : 0;
+        }
+    }
+    if (bitmap)
+        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = 0;
+#pragma unroll
+    for (int i = 0; i < kRerouteItems; ++i)
+        ids[i] = static_cast<uint32_t>(ids[i]) < static_cast<uint32_t>(E) ? ids[i]
+                                                                          : -1;
+    __syncthreads();
 
     // ---- 1. ranks within the tile ------------------------------------------
     int32_t rank[kRerouteItems];
@@ -229,7 +245,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = tid; i < kWaves * E; i += kBlock) whist[i] = 0;
         __syncthreads();
         int32_t *my_hist = whist + w * E;
-        int32_t lead[kRerouteItems];
+        // rank[i] packs the leader's count before the round (13 bits, a
+        // tile holds at most 4096 items), the rank below (6 bits) and the
+        // leader lane (6 bits) until the leaders' counts are fetched
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
@@ -240,13 +258,14 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             if (valid && below == 0)
                 old = atomicAdd(&my_hist[id], __builtin_popcountll(peers));
             const int leader = peers ? __builtin_ctzll(peers) : lane;
-            rank[i] = old;
-            lead[i] = leader | static_cast<int>(below << 6);
+            rank[i] = (old & 0x1FFF) | static_cast<int>(below << 13) |
+                      (leader << 19);
         }
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
-            const int before = __shfl(rank[i], lead[i] & 63, 64);
-            rank[i] = before + (lead[i] >> 6);
+            const int pk = rank[i];
+            const int before = __shfl(pk, (pk >> 19) & 63, 64) & 0x1FFF;
+            rank[i] = before + ((pk >> 13) & 63);
         }
         __syncthreads();
         for (int e = tid; e < E; e += kBlock) {
@@ -286,19 +305,10 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     // ---- 3. count of each expert in earlier tiles ---------------------------
     bool bad = false;
     if (kAfterLoad) {
-        const uint64_t *lst =
-            g.load_state + static_cast<int64_t>(layer) * g.max_tiles * E +
-            static_cast<int64_t>(tile - 1) * E;
-        for (int e = tid; e < E; e += kBlock) {
-            int v = 0;
-            if (tile > 0) {
-                const uint64_t word = lst[e];
-                const uint32_t flag = static_cast<uint32_t>(word >> 30) & 3u;
-                bad |= static_cast<uint32_t>(word >> 32) != epoch ||
-                       flag != kFlagPrefix;
-                v = static_cast<int>(static_cast<uint32_t>(word) & kValueMask);
-            }
-            tbase[e] = v;
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int e = tid + q * kBlock;
+            if (e < E) tbase[e] = pre_reg[q];
         }
     } else {
         uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
@@ -330,7 +340,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     __syncthreads();
     int32_t *stage_a = area;
     int32_t *stage_pos = area + kRerouteTile;
-#pragma unroll
+    // partly unrolled: fully unrolled, the sixteen items' addresses and
+    // stores keep too many registers live and halve the waves per SIMD
+#pragma unroll 4
     for (int i = 0; i < kRerouteItems; ++i) {
         const int64_t a = a0 + 64 * i;
         if (a >= g.A) continue;
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
-    if (tile != g.tiles - 1) return;
+    if (tile == g.tiles - 1) {
     // Assignments j in [lo, top) of a replica land at slot_off + (j - lo);
     // those whose position falls outside [0, A) (a plan made for other
     // counts) are faults like those beyond the expert's capacity.
@@ -404,6 +416,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     if (tid == 0 && g.faults)
         g.faults[layer] = static_cast<int32_t>(g.A - tot_valid + tot_over) |
                           (poisoned ? kPoisonBit : 0);
+    }
 }
 
 // Largest number of tokens that kRerouteTile consecutive assignments touch.
@@ -453,7 +466,7 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.k = c.k;
     g.ebits = c.ebits;
     g.tiles = tiles;
-    g.max_tiles = after_load ? c.max_load_tiles : c.max_rr_tiles;
+    g.max_tiles = c.max_rr_tiles;
     g.bm_words = reroute_bitmap_words(c.E, c.k);
     g.spin_limit = 1u << 22;
     g.lds_bytes = static_cast<uint32_t>(c.reroute_lds);
@@ -463,13 +476,16 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.inv_perm = inv_perm;
     g.state = c.scan_state;
     g.tick = c.rr_tick;
-    g.load_state = c.load_state;
-    g.load_tick = c.load_tick;
+    g.tile_prefix = c.tile_prefix;
     g.rank_counts = rank_counts;
     g.faults = faults;
-    if (after_load)
+    if (after_load) {
+        // one tile per workgroup: the hardware then overlaps one tile's
+        // tail with the next tile's loads on the same CU, which a
+        // persistent workgroup looping over tiles cannot
         hipLaunchKernelGGL(k_reroute<true>, dim3(tiles, L), dim3(kBlock),
                            c.reroute_lds, s, g);
+    }
     else
         hipLaunchKernelGGL(k_reroute<false>, dim3(tiles, L), dim3(kBlock),
                            c.reroute_lds, s, g);

@@ -154,10 +154,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     const int Lmax = cfg->max_layers;
     int64_t rr_tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
     if (rr_tiles < 1) rr_tiles = 1;
-    int64_t ld_tiles = (A + ue::kLoadTile - 1) / ue::kLoadTile;
-    if (ld_tiles < 1) ld_tiles = 1;
+    const int64_t ld_groups = (rr_tiles + ue::kLoadGroup - 1) / ue::kLoadGroup;
     c->max_rr_tiles = static_cast<int>(rr_tiles);
-    c->max_load_tiles = static_cast<int>(ld_tiles);
+    c->max_load_groups = static_cast<int>(ld_groups);
 
     // Workspace carve-up, each piece 256-byte aligned.
     size_t off = 0;
@@ -166,8 +165,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         off = round_up(off + bytes, 256);
         return o;
     };
-    const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_tiles * E);
+    const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_groups * E);
     const size_t o_ltick = take(sizeof(uint64_t) * Lmax);
+    const size_t o_tprefix = take(sizeof(int32_t) * Lmax * rr_tiles * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
     c->ws_bytes = off;
@@ -186,6 +186,7 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     char *b = static_cast<char *>(c->ws);
     c->load_state = reinterpret_cast<uint64_t *>(b + o_lstate);
     c->load_tick = reinterpret_cast<uint64_t *>(b + o_ltick);
+    c->tile_prefix = reinterpret_cast<int32_t *>(b + o_tprefix);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
     *out = c;

@@ -25,6 +25,7 @@ constexpr int kRerouteItems = 16;
 constexpr int kRerouteTile = kBlock * kRerouteItems;
 constexpr int kLoadItems = kRerouteItems;
 constexpr int kLoadTile = kRerouteTile;
+constexpr int kLoadGroup = 4;        // tiles counted by one load workgroup
 
 }  // namespace ue
 
@@ -44,9 +45,10 @@ struct ue_ctx {
     // launch and epochs only grow, so nothing is cleared between calls.
     void *ws = nullptr;
     size_t ws_bytes = 0;
-    int max_load_tiles = 0;        // load tiles of the largest layer
-    uint64_t *load_state = nullptr;// [max_layers][max_load_tiles][E]
+    int max_load_groups = 0;       // load tile groups of the largest layer
+    uint64_t *load_state = nullptr;// [max_layers][max_load_groups][E]
     uint64_t *load_tick = nullptr; // [max_layers] {epoch:32 | ticket:32}
+    int32_t *tile_prefix = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
 
@@ -111,6 +113,7 @@ int reroute_bitmap_words(int E, int k);
 // Raise the dynamic LDS limit of a kernel that needs more than 64 KiB.
 hipError_t plan_prepare(size_t lds_bytes);
 hipError_t reroute_prepare(size_t lds_bytes);
+// Reroute workgroups that can be resident on one CU with this much LDS.
 
 // ---------------------------------------------------------------------
 // wave64 helpers
