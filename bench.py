@@ -221,24 +221,57 @@ def bench_gather(ue, W, dev):
     return res
 
 
-def cpu_baseline(W, routing_layers=4):
-    """The oracle as it stands on a bounded sample of the same workload:
-    the first ``routing_layers`` layers of the dsv3 routing (same seeds),
-    load + plan + reroute per layer, single thread."""
-    import numpy as np
+def cpu_baseline(routing, cfg, min_seconds=10.0):
+    """The oracle as it stands, single thread, on a bounded sample of the
+    same workload: the bench's own dsv3 routing (copied to the host),
+    load + plan + reroute of every layer, repeated until at least
+    ``min_seconds`` of CPU work have been timed."""
     import oracle
-    cfg = W.CONFIGS["dsv3"]
-    r = W.make_routing(cfg, device="cpu", layers=routing_layers).numpy()
-    t0 = time.perf_counter()
-    oracle.rebalance(r, cfg.experts, cfg.ranks, cfg.spare)
-    dt = time.perf_counter() - t0
-    n = routing_layers * cfg.assignments
+    r = routing.cpu().numpy()
+    L = r.shape[0]
+    passes, dt = 0, 0.0
+    while dt < min_seconds:
+        t0 = time.perf_counter()
+        oracle.rebalance(r, cfg.experts, cfg.ranks, cfg.spare)
+        dt += time.perf_counter() - t0
+        passes += 1
+    n = passes * L * cfg.assignments
     return {"value": n / dt, "unit": "assignments/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"{routing_layers} of 58 dsv3 layers "
-                      f"({n} assignments), load+plan+reroute, "
-                      f"{dt:.2f} s on one host thread of {os.cpu_count()}",
-            "seconds": round(dt, 3)}
+            "sample": f"{passes} passes over all {L} dsv3 layers "
+                      f"({n} assignments), load+plan+reroute, {dt:.1f} s "
+                      f"on one host thread of {os.cpu_count()}",
+            "seconds": round(dt, 2)}
+
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                            "profiles", "k_reroute_dsv3_traffic.json")
+KERNEL_SOURCES = ("moe_expert_load_ue_amd/csrc/k_reroute.hip",
+                  "moe_expert_load_ue_amd/csrc/ue_internal.h")
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the reroute from calibrated FETCH_SIZE and
+    WRITE_SIZE counters, or None when the kernel's sources changed since
+    the counters were taken (the file records their digest)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != kernel_source_digest():
+        return None
+    return rec["read_bytes"] + rec["write_bytes"]
 
 
 def main():
@@ -248,7 +281,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-layers", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--only", choices=["rebalance", "large_ep", "stream",
                                        "gather"], default=None,
                     help="run one measurement (for profiling); prints its "
@@ -332,10 +365,11 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "k_reroute",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "algorithmic_bytes_per_launch": rr_bytes},
         "imbalance": imbalance(rb, cfg),
     }
+    routing_host = rb.routing.cpu()
     del rb
     torch.cuda.empty_cache()
     if not args.no_extra:
@@ -347,7 +381,8 @@ def main():
         line["gather"] = bench_gather(ue, W, dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        line["cpu_baseline"] = cpu_baseline(W, args.cpu_layers)
+        line["cpu_baseline"] = cpu_baseline(routing_host, cfg,
+                                            args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
