@@ -9,7 +9,9 @@
 // every token), so a tile's histogram is kept as kSub interleaved copies,
 // bin e of copy c at e * kSub + c, and lane l adds into copy l mod kSub:
 // lanes of a wave that hold the same id hit kSub different banks, which
-// bounds the serialisation of an LDS atomic at 64 / kSub lanes. Groups then
+// bounds the serialisation of an LDS atomic at 64 / kSub lanes. Tiles
+// alternate between two such histograms, so one tile is counted while the
+// previous one is summed and cleared, with one barrier per tile. Groups then
 // combine their histograms with the decoupled lookback of ue_internal.h;
 // the group with the last ticket ends with the inclusive prefix over the
 // whole layer, which is the layer's counts. Every group also writes, for
@@ -24,7 +26,7 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kSub = 8;   // interleaved histogram copies
+constexpr int kSub = 8;   // interleaved histogram copies (two 16-byte reads)
 
 struct LoadArgs {
     const int32_t *routing;
@@ -45,9 +47,9 @@ __device__ __forceinline__ void count_one(int id, int E, int sub,
 }
 
 __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
-    extern __shared__ int32_t lds[];
-    int32_t *hist = lds;                   // [E][kSub] one tile's counts
-    int32_t *cnt = lds + kSub * g.E;       // [kLoadGroup][E] per tile
+    extern __shared__ __align__(16) int32_t lds[];
+    int32_t *hist = lds;                   // [2][E][kSub] alternating tiles
+    int32_t *cnt = lds + 2 * kSub * g.E;   // [kLoadGroup][E] per tile
     int32_t *gcnt = cnt + kLoadGroup * g.E;// [E] the group's counts
     int32_t *excl = gcnt + g.E;            // [E] counts of earlier groups
     __shared__ uint32_t s_ticket, s_epoch;
@@ -58,6 +60,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     const int tid = threadIdx.x;
     const int sub = tid & (kSub - 1);
     if (tid == 0) take_ticket(g.tick + layer, g.groups, s_ticket, s_epoch);
+    for (int i = tid; i < 2 * kSub * E; i += kBlock) hist[i] = 0;
     __syncthreads();
     const int grp = static_cast<int>(s_ticket);
     if (grp >= g.groups) return;    // only after a corrupted earlier launch
@@ -80,31 +83,34 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     }
 #pragma unroll
     for (int s = 0; s < kLoadGroup; ++s) {
-        for (int i = tid; i < kSub * E; i += kBlock) hist[i] = 0;
-        __syncthreads();
+        int32_t *h = hist + (s & 1) * kSub * E;
         if (full[s]) {
 #pragma unroll
             for (int i = 0; i < kLoadItems / 4; ++i) {
-                count_one(r[s][i].x, E, sub, hist);
-                count_one(r[s][i].y, E, sub, hist);
-                count_one(r[s][i].z, E, sub, hist);
-                count_one(r[s][i].w, E, sub, hist);
+                count_one(r[s][i].x, E, sub, h);
+                count_one(r[s][i].y, E, sub, h);
+                count_one(r[s][i].z, E, sub, h);
+                count_one(r[s][i].w, E, sub, h);
             }
         } else {
             const int64_t t0 = static_cast<int64_t>(tile_first + s) * kLoadTile;
             const int64_t t1 = (t0 + kLoadTile < g.A) ? t0 + kLoadTile : g.A;
             for (int64_t a = t0 + tid; a < t1; a += kBlock)
-                count_one(src[a], E, sub, hist);
+                count_one(src[a], E, sub, h);
         }
         __syncthreads();
+        // sum and clear this tile's copies while the next tile is counted
+        // into the other histogram; the barrier after that count orders
+        // the clearing before this histogram's next use
         for (int e = tid; e < E; e += kBlock) {
-            int c = 0;
-#pragma unroll
-            for (int k = 0; k < kSub; ++k) c += hist[e * kSub + k];
-            cnt[s * E + e] = c;
+            i32x4 *b = reinterpret_cast<i32x4 *>(h + e * kSub);
+            const i32x4 u = b[0], v = b[1];
+            cnt[s * E + e] = u.x + u.y + u.z + u.w + v.x + v.y + v.z + v.w;
+            b[0] = i32x4{0, 0, 0, 0};
+            b[1] = i32x4{0, 0, 0, 0};
         }
-        __syncthreads();   // hist is cleared again for the next tile
     }
+    __syncthreads();
     for (int e = tid; e < E; e += kBlock) {
         int c = 0;
         for (int s = 0; s < kLoadGroup; ++s) c += cnt[s * E + e];
@@ -147,7 +153,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
 }  // namespace
 
 size_t load_lds_bytes(int E) {
-    return sizeof(int32_t) * (kSub + kLoadGroup + 2) * static_cast<size_t>(E);
+    return sizeof(int32_t) * (2 * kSub + kLoadGroup + 2) * static_cast<size_t>(E);
 }
 
 hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,

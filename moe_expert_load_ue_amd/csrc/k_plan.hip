@@ -208,8 +208,12 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     const int32_t *cin = counts + static_cast<int64_t>(layer) * E;
     int32_t *out = placement + static_cast<int64_t>(layer) * lay.words;
     PlanLds s = carve(lds, E, R, P);
-    // the carve-up must fit the launch's LDS (checked, not assumed)
-    if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) return;
+    // the carve-up must fit the launch's LDS (checked, not assumed); a
+    // mismatch marks the block (exhausted = -1) rather than pass silently
+    if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) {
+        if (tid == 0) out[lay.exhausted] = -1;
+        return;
+    }
 
     // ---- A. loads, quota, candidates ----------------------------------
     int part = 0;

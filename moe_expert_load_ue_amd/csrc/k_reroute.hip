@@ -39,6 +39,7 @@
 //      beyond an expert's capacity or outside [0, T*k).
 // No fences and no global atomics on data.
 #include <algorithm>
+#include <type_traits>
 
 #include "ue_internal.h"
 
@@ -48,7 +49,7 @@ namespace {
 struct RerouteArgs {
     const int32_t *routing;
     const int32_t *placement;
-    int64_t A;                 // assignments per layer
+    int32_t A;                 // assignments per layer (< 2^30)
     int E, R, NS, P, k, ebits, tiles, max_tiles;
     int bm_words;              // words per expert bitmap (0: no bitmap path)
     uint32_t spin_limit;       // bound on one lookback wait
@@ -61,35 +62,61 @@ struct RerouteArgs {
     int32_t *rank_counts, *faults;
 };
 
-// Bitmap path: bits of expert e live in words [e*Wp, e*Wp + W), with an odd
-// stride Wp so that neighbouring experts fall in other banks.
+// Element i of a per-layer array, with the byte offset formed in 32 bits
+// (every offset here is below 2^32 since T*k < 2^30): the address is then
+// a uniform 64-bit base plus one 32-bit register.
+template <typename T>
+__device__ __forceinline__ T *at(T *p, int i) {
+    using B = typename std::conditional<std::is_const<T>::value, const char,
+                                        char>::type;
+    return reinterpret_cast<T *>(reinterpret_cast<B *>(p) +
+                                 static_cast<uint32_t>(i) * sizeof(T));
+}
+
+// Bitmap path: expert e's token bitmap is words [e*Wp, e*Wp + W) of an
+// array of int2 {bits, popcount prefix}, with an odd stride Wp so that
+// neighbouring experts fall in other banks; one 8-byte read gives an item
+// both the word and the count of the bits before it.
 __host__ __device__ __forceinline__ int bm_stride(int W) { return W | 1; }
 
 // Largest region A (ints) the bitmap path may take; beyond it, the
 // configuration ranks by matching.
 constexpr int kBitmapBudget = 12288;
 
-// Size in ints of region A, shared in turn by the rank bitmaps and their
-// word prefixes (or the per-wave counters of the matching path) and by the
-// staged perm entries.
+// Size in ints of region A, shared in turn by the rank bitmaps (or the
+// per-wave counters of the matching path) and by the staged perm entries
+// (plus one dummy entry per thread); a multiple of 4 so that what follows
+// stays 16-byte aligned.
+static_assert(kRerouteTile <= 4096, "matching ranks are packed in 13 bits");
+
 __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
     int a = 2 * E * bm_stride(W);
     a = a > kWaves * E ? a : kWaves * E;
-    return a > 2 * kRerouteTile ? a : 2 * kRerouteTile;
+    a = a > 2 * (kRerouteTile + kBlock) ? a : 2 * (kRerouteTile + kBlock);
+    return (a + 3) & ~3;
 }
 
 // kAfterLoad: the count of each expert in earlier tiles is the per-tile
 // prefix the load kernel just wrote, tiles do not depend on each other and
 // workgroup blockIdx.x takes tile blockIdx.x. Otherwise the workgroup takes
-// one tile by ticket and finds the prefix by lookback.
+// one tile by ticket and finds the prefix by lookback. (A persistent grid
+// that loads the replica table once and loops over tiles measured no
+// faster: the hardware already overlaps one workgroup's table reads with
+// others' work.)
 template <bool kAfterLoad>
 __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
-    extern __shared__ int32_t lds[];
+    extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kWaves];
     __shared__ uint32_t s_ticket, s_epoch;
 
     const int E = g.E, P = g.P, R = g.R;
-    const int layer = blockIdx.y;
+    // after a load: launch order -> (layer, tile), contiguous per XCD, so
+    // that a tile's perm runs and its neighbour's share one L2
+    const int item = kAfterLoad
+        ? xcd_order(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y)
+        : 0;
+    const int layer = kAfterLoad ? item / static_cast<int>(gridDim.x)
+                                 : static_cast<int>(blockIdx.y);
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -97,26 +124,73 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int Wp = bm_stride(W);
 
     int32_t *area = lds;
-    int32_t *tcount = area + region_a_ints(E, W);
+    int4 *einfo = reinterpret_cast<int4 *>(area + region_a_ints(E, W));
+    int32_t *tcount = reinterpret_cast<int32_t *>(einfo + E);
     int32_t *torder = tcount + E;
     int32_t *tbase = torder + E;
-    int32_t *fslot = tbase + E;
-    int32_t *flim = fslot + E;
-    int32_t *fpos = flim + E;
-    int32_t *rep_off = fpos + E;
+    int32_t *rep_off = tbase + E;
     int32_t *rep_slot = rep_off + E + 1;
     int32_t *rep_lo = rep_slot + P;
     int32_t *rep_hi = rep_lo + P;
     int32_t *slot_off = rep_hi + P;
     int32_t *rank_hist = slot_off + P;
-    // the carve-up must fit the launch's LDS (checked, not assumed)
-    if (static_cast<size_t>(rank_hist + R - lds) * 4 > g.lds_bytes) return;
+    // the carve-up must fit the launch's LDS (checked, not assumed); a
+    // mismatch poisons the layer's fault count rather than pass silently
+    if (static_cast<size_t>(rank_hist + R - lds) * 4 > g.lds_bytes) {
+        if (tid == 0 && blockIdx.x == 0 && g.faults) g.faults[layer] = kPoisonBit;
+        return;
+    }
 
-    if (kAfterLoad) {
-        if (tid == 0) {
-            s_ticket = blockIdx.x;
-            s_epoch = 0;
+    // per-layer bases, uniform across the workgroup; items are then
+    // addressed by 32-bit offsets (A < 2^30)
+    const int64_t base = static_cast<int64_t>(layer) * g.A;
+    const int32_t *__restrict__ routing_l = g.routing + base;
+    int32_t *__restrict__ phys_l = g.phys + base;
+    int32_t *__restrict__ perm_l = g.perm + base;
+    int32_t *__restrict__ inv_l = g.inv_perm ? g.inv_perm + base : nullptr;
+    const int A = g.A;
+    constexpr int kPerThread = kMaxExperts / kBlock;
+    int32_t ids[kRerouteItems];
+    int32_t pre_reg[kPerThread];
+    int tile = 0;
+    int tile0 = 0, a0 = 0;
+    // the tile's ids (and, after a load, its prefixes): issued first so
+    // that their latency overlaps the placement table reads
+    // (a full tile loads unconditionally at immediate offsets; the ragged
+    // last tile clamps its reads into the layer and drops what lies beyond)
+    auto load_ids = [&](int t, int32_t *dst) {
+        const int first = t * kRerouteTile + w * 64 * kRerouteItems + lane;
+        if ((t + 1) * kRerouteTile <= A) {
+            const int32_t *src = at(routing_l, first);
+#pragma unroll
+            for (int i = 0; i < kRerouteItems; ++i)
+                dst[i] = __builtin_nontemporal_load(src + 64 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRerouteItems; ++i) {
+                const int a = first + 64 * i;
+                const int v = A > 0 ? __builtin_nontemporal_load(
+                                          at(routing_l, a < A ? a : A - 1))
+                                    : -1;
+                dst[i] = a < A ? v : -1;
+            }
         }
+    };
+    auto load_prefix = [&](int t, int32_t *dst) {
+        const int32_t *tp = g.tile_prefix +
+                            (static_cast<int64_t>(layer) * g.max_tiles + t) * E;
+#pragma unroll
+        for (int q = 0; q < kPerThread; ++q) {
+            const int e = tid + q * kBlock;
+            dst[q] = e < E ? tp[e] : 0;
+        }
+    };
+    if (kAfterLoad) {
+        tile = item % static_cast<int>(gridDim.x);
+        if (tile >= g.tiles) return;
+        load_ids(tile, ids);
+        load_prefix(tile, pre_reg);
+        if (tid == 0) s_epoch = 0;
     } else if (tid == 0) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
     }
@@ -136,11 +210,15 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         rep_hi[p] = cap > 0 ? cap : 0;     // capacity, until the prefix below
     }
     const bool bitmap = W > 0;
-    int32_t *bm = area;                    // [E][Wp] token bitmaps
-    int32_t *bpre = area + E * Wp;         // [E][Wp] popcount prefixes
+    int2 *bm = reinterpret_cast<int2 *>(area);   // [E][Wp] {bits, prefix}
+    if (bitmap)
+        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = int2{0, 0};
     __syncthreads();
-    if (static_cast<int>(s_ticket) >= g.tiles)
-        return;    // only after a corrupted earlier launch
+    if (!kAfterLoad) {
+        tile = static_cast<int>(s_ticket);
+        if (tile >= g.tiles) return;   // only after a corrupted earlier launch
+        load_ids(tile, ids);
+    }
     // capacity prefix of each replica within its expert, from LDS
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
@@ -152,38 +230,12 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         }
     }
     const uint32_t epoch = s_epoch;
-    const int tile = static_cast<int>(s_ticket);
-    const int64_t base = static_cast<int64_t>(layer) * g.A;
-    const int64_t tile0 = static_cast<int64_t>(tile) * kRerouteTile;
-    const int64_t a0 = tile0 + static_cast<int64_t>(w) * 64 * kRerouteItems +
-                       lane;
-
-    // global reads first: the tile's ids and, after a load, its prefixes
-    int32_t ids[kRerouteItems];
-#pragma unroll
-    for (int i = 0; i < kRerouteItems; ++i) {
-        const int64_t a = a0 + 64 * i;
-        ids[i] = (a < g.A) ? __builtin_nontemporal_load(g.routing + base + a)
-                           : -1;
-    }
-    constexpr int kPerThread = kMaxExperts / kBlock;
-    int32_t pre_reg[kPerThread];
-    if (kAfterLoad) {
-        const int32_t *tp = g.tile_prefix +
-                            (static_cast<int64_t>(layer) * g.max_tiles + tile) * E;
-#pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            const int e = tid + q * kBlock;
-            pre_reg[q] = e < E ? tp[e] : 0;
-        }
-    }
-    if (bitmap)
-        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = 0;
+    tile0 = tile * kRerouteTile;
+    a0 = tile0 + w * 64 * kRerouteItems + lane;
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i)
         ids[i] = static_cast<uint32_t>(ids[i]) < static_cast<uint32_t>(E) ? ids[i]
                                                                           : -1;
-    __syncthreads();
 
     // ---- 1. ranks within the tile ------------------------------------------
     int32_t rank[kRerouteItems];
@@ -192,36 +244,47 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         // token of item a0 + 64 i relative to the tile's first token,
         // stepped without a division per item
         const int k = g.k;
-        const int t_first = static_cast<int>(tile0 / k);
-        int tl = static_cast<int>(a0 / k) - t_first;
-        int rm = static_cast<int>(a0 % k);
+        const uint32_t uk = static_cast<uint32_t>(k);
+        const int t_first = static_cast<int>(static_cast<uint32_t>(tile0) / uk);
+        const uint32_t qa = static_cast<uint32_t>(a0) / uk;
+        int tl = static_cast<int>(qa) - t_first;
+        int rm = static_cast<int>(static_cast<uint32_t>(a0) - qa * uk);
         const int q64 = 64 / k, r64 = 64 % k;
+        // Branch-free: an id out of range ORs nothing into expert 0's
+        // word, so every lane issues the same instructions.
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             rank[i] = tl;                  // the token, until the read-back
-            if (id >= 0) {
-                const uint32_t bit = 1u << (tl & 31);
-                const uint32_t old = atomicOr(
-                    reinterpret_cast<uint32_t *>(&bm[id * Wp + (tl >> 5)]), bit);
-                dup |= (old & bit) != 0;
-            }
-            tl += q64;
+            const uint32_t bit = id >= 0 ? 1u << (tl & 31) : 0u;
+            const uint32_t old = atomicOr(
+                reinterpret_cast<uint32_t *>(area) +
+                    2 * ((id >= 0 ? id : 0) * Wp + (tl >> 5)),
+                bit);
+            dup |= (old & bit) != 0;
             rm += r64;
-            if (rm >= k) {
-                rm -= k;
-                ++tl;
-            }
+            const int carry = rm >= k;
+            rm -= carry ? k : 0;
+            tl += q64 + carry;
         }
     }
     const int use_match = !bitmap || __syncthreads_or(dup);
     if (!use_match) {
-        // prefix of popcounts over each expert's words; tile counts
+        // prefix of popcounts over each expert's words (read in batches so
+        // the reads overlap); tile counts
         for (int e = tid; e < E; e += kBlock) {
+            int2 *row = bm + e * Wp;
             int run = 0;
-            for (int i = 0; i < W; ++i) {
-                bpre[e * Wp + i] = run;
-                run += __builtin_popcount(static_cast<uint32_t>(bm[e * Wp + i]));
+            for (int i0 = 0; i0 < W; i0 += 8) {
+                uint32_t bits[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    bits[j] = i0 + j < W ? static_cast<uint32_t>(row[i0 + j].x) : 0u;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if (i0 + j < W) row[i0 + j].y = run;
+                    run += __builtin_popcount(bits[j]);
+                }
             }
             tcount[e] = run;
             torder[e] = run;
@@ -231,12 +294,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             const int tl = rank[i];
-            if (id >= 0) {
-                const int word = id * Wp + (tl >> 5);
-                const uint32_t below = (1u << (tl & 31)) - 1u;
-                rank[i] = bpre[word] + __builtin_popcount(
-                                           static_cast<uint32_t>(bm[word]) & below);
-            }
+            const int2 v = bm[(id >= 0 ? id : 0) * Wp + (tl >> 5)];
+            const uint32_t below = (1u << (tl & 31)) - 1u;
+            rank[i] = v.y + __builtin_popcount(static_cast<uint32_t>(v.x) & below);
         }
     } else {
         // matching path: ranks within rounds of 64 consecutive items
@@ -245,9 +305,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = tid; i < kWaves * E; i += kBlock) whist[i] = 0;
         __syncthreads();
         int32_t *my_hist = whist + w * E;
-        // rank[i] packs the leader's count before the round (13 bits, a
-        // tile holds at most 4096 items), the rank below (6 bits) and the
-        // leader lane (6 bits) until the leaders' counts are fetched
+        // rank[i] packs the leader's count before the round (13 bits; a
+        // tile holds kRerouteTile <= 4096 items), the rank below (6 bits)
+        // and the leader lane (6 bits) until the leaders' counts are fetched
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
@@ -317,9 +377,10 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int poisoned = __syncthreads_or(bad);
 
     // ---- 4. outputs ---------------------------------------------------------
-    // Per expert: the replica covering the tile's first assignment j0, the
-    // dispatch position of j0 and how many of the tile's assignments stay in
-    // that replica.
+    // Per expert, in one 16-byte word: the tile's first position in its
+    // (expert, j) order, how many of the tile's assignments stay in the
+    // replica covering the tile's first j, that replica's slot and the
+    // dispatch position of that first j.
     for (int e = tid; e < E; e += kBlock) {
         const int j0 = tbase[e];
         int q = -1, lim = 0, pos0 = 0;
@@ -333,58 +394,80 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 break;
             }
         }
-        fslot[e] = q;
-        flim[e] = q >= 0 ? lim : 0;
-        fpos[e] = pos0;
+        einfo[e] = int4{torder[e], q >= 0 ? lim : 0, q, pos0};
     }
     __syncthreads();
-    int32_t *stage_a = area;
-    int32_t *stage_pos = area + kRerouteTile;
-    // partly unrolled: fully unrolled, the sixteen items' addresses and
-    // stores keep too many registers live and halve the waves per SIMD
-#pragma unroll 4
+    // [tile] {a, pos} in (expert, j) order, then one dummy entry per thread
+    // that items without a valid id write to, so the stores need no branch
+    int2 *stage = reinterpret_cast<int2 *>(area);
+    const bool full_tile = tile0 + kRerouteTile <= A;
+    int32_t *phys_t = at(phys_l, a0);
+    int32_t *inv_t = inv_l ? at(inv_l, a0) : nullptr;
+    int p_out[kRerouteItems], pos_out[kRerouteItems], s_out[kRerouteItems];
+    bool slow = false;
+#pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
-        const int64_t a = a0 + 64 * i;
-        if (a >= g.A) continue;
         const int id = ids[i];
-        int p = -1, pos = -1;
-        if (id >= 0) {
-            const int jt = rank[i];                    // j within the tile
-            const int s = torder[id] + jt;             // tile (expert, j) order
-            if (jt < flim[id]) {
-                p = fslot[id];
-                pos = fpos[id] + jt;
-            } else {
-                const int j = tbase[id] + jt;
-                for (int r = rep_off[id]; r < rep_off[id + 1]; ++r) {
-                    if (j < rep_hi[r]) {
-                        if (j >= rep_lo[r] && rep_slot[r] >= 0) {
-                            p = rep_slot[r];
-                            pos = slot_off[p] + (j - rep_lo[r]);
-                        }
-                        break;
+        const int4 f = einfo[id >= 0 ? id : 0];
+        const int jt = rank[i];                        // j within the tile
+        const bool fast = id >= 0 && jt < f.y;
+        slow |= id >= 0 && !fast;
+        p_out[i] = fast ? f.z : -1;
+        pos_out[i] = fast ? f.w + jt : -1;
+        s_out[i] = id >= 0 ? f.x + jt : kRerouteTile + tid;
+    }
+    // Items past the replica covering the tile's first j (or faults) walk
+    // the expert's capacity prefixes; rare, so skipped per wave.
+    if (__ballot(slow) != 0) {
+#pragma unroll
+        for (int i = 0; i < kRerouteItems; ++i) {
+            const int id = ids[i];
+            if (id < 0 || p_out[i] >= 0) continue;
+            const int j = tbase[id] + rank[i];
+            for (int r = rep_off[id]; r < rep_off[id + 1]; ++r) {
+                if (j < rep_hi[r]) {
+                    if (j >= rep_lo[r] && rep_slot[r] >= 0) {
+                        p_out[i] = rep_slot[r];
+                        pos_out[i] = slot_off[p_out[i]] + (j - rep_lo[r]);
                     }
+                    break;
                 }
             }
-            if (p < 0 || pos < 0 || pos >= g.A) {
-                p = -1;
-                pos = -1;
-            }
-            stage_a[s] = static_cast<int32_t>(a);
-            stage_pos[s] = pos;
         }
-        __builtin_nontemporal_store(p, g.phys + base + a);
-        if (g.inv_perm) __builtin_nontemporal_store(pos, g.inv_perm + base + a);
+    }
+#pragma unroll
+    for (int i = 0; i < kRerouteItems; ++i) {
+        int p = p_out[i], pos = pos_out[i];
+        const bool ok = p >= 0 && pos >= 0 && pos < A;
+        p = ok ? p : -1;
+        pos = ok ? pos : -1;
+        stage[s_out[i]] = int2{a0 + 64 * i, pos};
+        p_out[i] = p;
+        pos_out[i] = pos;
+    }
+    if (full_tile) {
+#pragma unroll
+        for (int i = 0; i < kRerouteItems; ++i) {
+            __builtin_nontemporal_store(p_out[i], phys_t + 64 * i);
+            if (inv_t) __builtin_nontemporal_store(pos_out[i], inv_t + 64 * i);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRerouteItems; ++i) {
+            if (a0 + 64 * i >= A) continue;
+            __builtin_nontemporal_store(p_out[i], phys_t + 64 * i);
+            if (inv_t) __builtin_nontemporal_store(pos_out[i], inv_t + 64 * i);
+        }
     }
     __syncthreads();
     const int n_valid = torder[E - 1] + tcount[E - 1];
     for (int s = tid; s < n_valid; s += kBlock) {
-        const int pos = stage_pos[s];
-        if (pos >= 0) g.perm[base + pos] = stage_a[s];
+        const int2 v = stage[s];
+        if (v.y >= 0) *at(perm_l, v.y) = v.x;
     }
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
-    if (tile == g.tiles - 1) {
+    if (tile != g.tiles - 1) return;
     // Assignments j in [lo, top) of a replica land at slot_off + (j - lo);
     // those whose position falls outside [0, A) (a plan made for other
     // counts) are faults like those beyond the expert's capacity.
@@ -416,7 +499,6 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     if (tid == 0 && g.faults)
         g.faults[layer] = static_cast<int32_t>(g.A - tot_valid + tot_over) |
                           (poisoned ? kPoisonBit : 0);
-    }
 }
 
 // Largest number of tokens that kRerouteTile consecutive assignments touch.
@@ -432,10 +514,10 @@ int reroute_bitmap_words(int E, int k) {
 
 size_t reroute_lds_bytes(int E, int R, int P, int k) {
     const int W = reroute_bitmap_words(E, k);
-    // region A; tcount, torder, tbase, fslot, flim, fpos; rep_off (+1);
-    // four P-sized tables; the rank histogram
+    // region A; einfo (4 words per expert), tcount, torder, tbase;
+    // rep_off (+1); four P-sized tables; the rank histogram
     return sizeof(int32_t) * (static_cast<size_t>(region_a_ints(E, W)) +
-                              static_cast<size_t>(7) * E + 1 + 4 * P + R);
+                              static_cast<size_t>(8) * E + 1 + 4 * P + R);
 }
 
 hipError_t reroute_prepare(size_t lds_bytes) {
@@ -458,7 +540,7 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     RerouteArgs g;
     g.routing = routing;
     g.placement = placement;
-    g.A = A;
+    g.A = static_cast<int32_t>(A);   // the context bounds T*k below 2^30
     g.E = c.E;
     g.R = c.R;
     g.NS = c.NS;
@@ -480,9 +562,6 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.rank_counts = rank_counts;
     g.faults = faults;
     if (after_load) {
-        // one tile per workgroup: the hardware then overlaps one tile's
-        // tail with the next tile's loads on the same CU, which a
-        // persistent workgroup looping over tiles cannot
         hipLaunchKernelGGL(k_reroute<true>, dim3(tiles, L), dim3(kBlock),
                            c.reroute_lds, s, g);
     }

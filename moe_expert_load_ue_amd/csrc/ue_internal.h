@@ -21,11 +21,11 @@ constexpr int kWaves = kBlock / 64;
 // Routing tiles: kRerouteItems assignments per thread, processed as rounds
 // of 64 consecutive assignments per wave. The load kernel uses the same
 // tiles, so the per-tile prefixes it publishes serve the fused reroute.
-constexpr int kRerouteItems = 16;
+constexpr int kRerouteItems = 8;
 constexpr int kRerouteTile = kBlock * kRerouteItems;
 constexpr int kLoadItems = kRerouteItems;
 constexpr int kLoadTile = kRerouteTile;
-constexpr int kLoadGroup = 4;        // tiles counted by one load workgroup
+constexpr int kLoadGroup = 16384 / kLoadTile;   // tiles per load workgroup
 
 }  // namespace ue
 
@@ -121,6 +121,18 @@ hipError_t reroute_prepare(size_t lds_bytes);
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // Number of set bits of `mask` below this lane.
+// Workgroups are handed to the 8 XCDs round robin in launch order, and
+// each XCD has its own L2. Work item xcd_order(i, n) of n gives XCD i mod 8
+// one contiguous run of items, so neighbouring items (whose outputs share
+// cache lines) meet in the same L2. A bijection of [0, n) for any n.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_order(int i, int n) {
+    const int x = i % kXcds, k = i / kXcds;
+    const int q = n / kXcds, r = n % kXcds;
+    // XCD x receives q + (x < r) items; those of XCDs below x come first
+    return x * q + (x < r ? x : r) + k;
+}
+
 __device__ __forceinline__ uint32_t mask_rank(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi(
         static_cast<uint32_t>(mask >> 32),
