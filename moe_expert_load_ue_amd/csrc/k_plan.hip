@@ -16,10 +16,14 @@
 //   A. all 256 threads: counts and rank loads into LDS, the quota, the
 //      candidate list (compacted in id order, then ranked by comparison
 //      counting, which is exact and needs no sort network);
-//   B. wave 0 alone: the sequential spill loop. Each lane owns ranks
-//      lane, lane+64, ... and caches the smallest key (load << rbits | rank)
-//      among its eligible ranks; one DPP min-reduction per chunk picks the
-//      destination, and only the owner lane of that rank refreshes its key;
+//   B. wave 0 alone: the sequential spill loop, in scalar registers. The
+//      least-loaded eligible rank is the smaller of two minima: the next
+//      entry of the list of ranks eligible at the start, sorted once by
+//      (load, id) in part A (such a rank has received nothing yet, so its
+//      key is unchanged), and the smallest key among ranks that received a
+//      chunk and are still eligible, held by their owner lanes and reduced
+//      with DPP only while that set is non-empty (never with one spare slot
+//      per rank, where a destination fills its only slot);
 //   C. all threads: replica table (CSR) and slot tables by prefix sums.
 // Everything is integer and deterministic; the result does not depend on
 // scheduling.
@@ -29,7 +33,8 @@ namespace ue {
 namespace {
 
 struct PlanLds {
-    int32_t *cnt, *rem, *load, *nfree, *cand, *sorted, *first_rec, *nrec_e;
+    int32_t *cnt, *rem, *load, *cand, *sorted, *first_rec, *nrec_e;
+    int32_t *dkey, *dsorted, *smove;
     int32_t *rec_e, *rec_p, *rec_m, *slot_cap, *slot_exp, *rep_off;
 };
 
@@ -42,13 +47,15 @@ __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
     int32_t *p = base;
     s.cnt = p; p += E;
     s.rem = p; p += E;
-    s.cand = p; p += E;
+    s.cand = p; p += 2 * E;          // {rank << 16 | expert, count}
     s.sorted = p; p += E;
     s.first_rec = p; p += E;
     s.nrec_e = p; p += E;
     s.rep_off = p; p += E + 1;
     s.load = p; p += R;
-    s.nfree = p; p += R;
+    s.dkey = p; p += R;
+    s.dsorted = p; p += R;
+    s.smove = p; p += E;
     s.rec_e = p; p += P;
     s.rec_p = p; p += P;
     s.rec_m = p; p += P;
@@ -77,119 +84,174 @@ __device__ int block_scan_inplace(int32_t *data, int n, int *wsum) {
     return total;
 }
 
-// Per-lane register state of the ranks a lane owns (lane, lane+64, ...),
-// read and written with a wave-uniform slot index through unrolled selects.
-template <int RPL>
-struct RankRegs {
-    int load[RPL];
-    int nfree[RPL];
-
-    __device__ __forceinline__ int get_load(int k) const {
-        int v = 0;
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) v = (i == k) ? load[i] : v;
-        return v;
+// Entry c of an LDS list through a 64-entry window held one per lane:
+// readlane with a uniform index, one LDS read per 64 entries.
+struct ListWindow {
+    const int32_t *list;
+    int n, base, reg;
+    __device__ __forceinline__ void init(const int32_t *l, int count) {
+        list = l;
+        n = count;
+        base = 0;
+        const int lane = threadIdx.x & 63;
+        reg = lane < n ? list[lane] : -1;
     }
-    __device__ __forceinline__ int get_free(int k) const {
-        int v = 0;
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) v = (i == k) ? nfree[i] : v;
-        return v;
-    }
-    // smallest key (load << rbits | rank) among this lane's eligible ranks
-    __device__ __forceinline__ uint32_t key(int lane, int R, int Q,
-                                            int rbits) const {
-        uint32_t best = 0xFFFFFFFFu;
-#pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int r = lane + 64 * i;
-            const uint32_t k = (static_cast<uint32_t>(load[i]) << rbits) |
-                               static_cast<uint32_t>(r);
-            const bool ok = r < R && nfree[i] > 0 && load[i] < Q;
-            best = (ok && k < best) ? k : best;
+    __device__ __forceinline__ int get(int c) {
+        if (c - base >= 64) {
+            base = c & ~63;
+            const int i = base + (threadIdx.x & 63);
+            reg = i < n ? list[i] : -1;
         }
-        return best;
+        return __builtin_amdgcn_readlane(reg, c - base);
     }
 };
 
-// The spill loop, run by wave 0 alone. Everything that decides the next
-// step is wave-uniform: the candidate, its rank's load, the expert's
-// remainder and the reduced minimum key. Only the lane owning the chosen
-// destination changes its registers and refreshes its cached key.
+// Inclusive prefix sum over the wave with DPP (row shifts, then the row
+// broadcasts), saturating at 2^30: values are non-negative and below
+// 2^30, so no sum overflows and the saturating add stays associative.
+__device__ __forceinline__ uint32_t wave_sat_inclusive_sum(uint32_t x) {
+    constexpr uint32_t kCap = 1u << 30;
+    auto step = [&](uint32_t t) {
+        x = x + t;
+        x = x < kCap ? x : kCap;
+    };
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x111, 0xF, 0xF, false));  // row_shr:1
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x112, 0xF, 0xF, false));  // row_shr:2
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x114, 0xF, 0xF, false));  // row_shr:4
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x118, 0xF, 0xF, false));  // row_shr:8
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x142, 0xA, 0xF, false));  // row_bcast:15
+    step(__builtin_amdgcn_update_dpp(0u, x, 0x143, 0xC, 0xF, false));  // row_bcast:31
+    return x;
+}
+
+// The spill loop, run by wave 0 alone.
+//  - Candidate c (in order) moves A_c = min(count, its home rank's excess
+//    left by the rank's earlier candidates), found in part A; the loop
+//    only places those amounts, chunk by chunk, and stops the plan when no
+//    destination is left (exhausted).
+//  - dsorted holds the nd ranks eligible at the start as keys (load << rbits
+//    | rank), ascending: such a rank has all S spare slots free until it is
+//    first chosen, and the chunks of a run of such ranks are computed 64 at
+//    a time: lane j takes the j-th next rank, a saturating prefix sum of
+//    their headrooms (Q - load) finds the rank where the amount runs out,
+//    every rank before it is filled to Q and that rank takes the rest.
+//  - A rank left below Q with spare slots (only after taking the rest, and
+//    only with S > 1) is held by its owner lane (rank mod 64) as a key plus
+//    its free-slot count. Ranks of the list beyond the smallest held key
+//    wait while that rank takes one chunk on its own.
 template <int RPL>
-__device__ void spill_loop(PlanLds &s, int ncand, int R, int S, int N, int NS,
-                           int Q, int rbits, int &nrec_out,
+__device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
+                           int NS, int Q, int rbits, int &nrec_out,
                            int &exhausted_out) {
     const int lane = threadIdx.x & 63;
-    RankRegs<RPL> st;
+    uint32_t hkey[RPL];
+    int hfree[RPL];
 #pragma unroll
     for (int i = 0; i < RPL; ++i) {
-        const int r = lane + 64 * i;
-        st.load[i] = r < R ? s.load[r] : 0;
-        st.nfree[i] = r < R ? S : 0;
+        hkey[i] = 0xFFFFFFFFu;
+        hfree[i] = 0;
     }
-    uint32_t my_key = st.key(lane, R, Q, rbits);
+    uint32_t my_min = 0xFFFFFFFFu;
+    int h_count = 0;
+    // hold rank d (key k, f free slots) in its owner lane, or release it
+    auto hold = [&](int d, uint32_t k, int f) {
+        if (lane == (d & 63)) {
+            const int dk = d >> 6;
+            uint32_t b = 0xFFFFFFFFu;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                if (i == dk) {
+                    hkey[i] = k;
+                    hfree[i] = f;
+                }
+                b = hkey[i] < b ? hkey[i] : b;
+            }
+            my_min = b;
+        }
+    };
+    ListWindow cand, cmove;
+    cand.init(s.sorted, ncand);
+    cmove.init(s.smove, ncand);
     const uint32_t rmask = (1u << rbits) - 1u;
     const int max_rec = R * S;
-    int nrec = 0;
-    int exhausted = 0;
+    int di = 0, nrec = 0, exhausted = 0;
     for (int c = 0; c < ncand && !exhausted; ++c) {
-        const int e = __builtin_amdgcn_readfirstlane(s.sorted[c]);
-        const int r = e / N;
-        int Lr = __builtin_amdgcn_readlane(st.get_load(r >> 6), r & 63);
-        int rem_e = __builtin_amdgcn_readfirstlane(s.rem[e]);
-        const int first = nrec;
-        while (Lr > Q && rem_e > 0) {
-            // each chunk takes one spare slot: with all R*S taken no rank
-            // is eligible (this also bounds the loop whatever the keys hold)
-            const uint32_t best =
-                nrec < max_rec ? wave_min_u32(my_key) : 0xFFFFFFFFu;
-            if (best == 0xFFFFFFFFu) {
+        const int e = cand.get(c);
+        int rem = cmove.get(c);
+        while (rem > 0) {
+            const uint32_t kh = h_count > 0 ? wave_min_u32(my_min) : 0xFFFFFFFFu;
+            // the next list ranks below the smallest held key, within the
+            // spare slots left
+            const int idx = di + lane;
+            const uint32_t key = (idx < nd && nrec + lane < max_rec)
+                ? static_cast<uint32_t>(s.dsorted[idx]) : 0xFFFFFFFFu;
+            const bool valid = key < kh;
+            const int Ld = static_cast<int>(key >> rbits);
+            const int h = valid ? Q - Ld : 0;
+            const int pre = static_cast<int>(
+                wave_sat_inclusive_sum(static_cast<uint32_t>(h)));
+            const uint64_t hit = __ballot(valid && pre >= rem);
+            const int nv = hit ? __builtin_ctzll(hit) + 1
+                               : __builtin_popcountll(__ballot(valid));
+            // the sum before the hit lane is below rem, hence exact
+            const int before_hit =
+                (hit && nv >= 2) ? __builtin_amdgcn_readlane(pre, nv - 2) : 0;
+            if (lane < nv) {
+                // full headroom, except the rank where the amount runs out
+                const int m = (hit && lane == nv - 1) ? rem - before_hit : h;
+                const int d = static_cast<int>(key & rmask);
+                s.rec_e[nrec + lane] = e;
+                s.rec_p[nrec + lane] = d * NS + N;      // its first spare
+                s.rec_m[nrec + lane] = m;
+            }
+            if (nv > 0) {
+                if (hit) {
+                    const uint32_t lk = static_cast<uint32_t>(
+                        __builtin_amdgcn_readlane(static_cast<int>(key), nv - 1));
+                    const int m_last = rem - before_hit;
+                    const int Ld2 = static_cast<int>(lk >> rbits) + m_last;
+                    if (S > 1 && Ld2 < Q) {
+                        const int d = static_cast<int>(lk & rmask);
+                        hold(d, (static_cast<uint32_t>(Ld2) << rbits) |
+                                    static_cast<uint32_t>(d), S - 1);
+                        ++h_count;
+                    }
+                    rem = 0;
+                } else {
+                    rem -= __builtin_amdgcn_readlane(pre, nv - 1);
+                }
+                di += nv;
+                nrec += nv;
+            }
+            if (rem == 0 || nv == 64) continue;
+            // the run stopped before the amount: the smallest held rank
+            // takes one chunk, or nothing is left
+            if (kh == 0xFFFFFFFFu || nrec >= max_rec) {
                 exhausted = 1;
                 break;
             }
-            const int d = static_cast<int>(best & rmask);
-            const int Ld = static_cast<int>(best >> rbits);
-            int m = Lr - Q;
-            m = rem_e < m ? rem_e : m;
-            m = (Q - Ld) < m ? (Q - Ld) : m;
+            const int d = static_cast<int>(kh & rmask);
+            const int Lh = static_cast<int>(kh >> rbits);
             const int dk = d >> 6;
-            const int fr = __builtin_amdgcn_readlane(st.get_free(dk), d & 63);
-            const int p = d * NS + N + (S - fr);
+            int f = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) f = (i == dk) ? hfree[i] : f;
+            const int fr = __builtin_amdgcn_readlane(f, d & 63);
+            const int m = rem < Q - Lh ? rem : Q - Lh;
             if (lane == 0) {
                 s.rec_e[nrec] = e;
-                s.rec_p[nrec] = p;
+                s.rec_p[nrec] = d * NS + N + (S - fr);
                 s.rec_m[nrec] = m;
             }
             ++nrec;
-            rem_e -= m;
-            Lr -= m;
-            if (lane == (d & 63)) {
-#pragma unroll
-                for (int i = 0; i < RPL; ++i) {
-                    if (i == dk) {
-                        st.load[i] = Ld + m;
-                        st.nfree[i] -= 1;
-                    }
-                }
-                my_key = st.key(lane, R, Q, rbits);
-            }
+            rem -= m;
+            const bool again = fr > 1 && Lh + m < Q;
+            hold(d, again ? (static_cast<uint32_t>(Lh + m) << rbits) |
+                                static_cast<uint32_t>(d)
+                          : 0xFFFFFFFFu,
+                 fr - 1);
+            h_count -= again ? 0 : 1;
         }
-        if (lane == (r & 63)) {
-#pragma unroll
-            for (int i = 0; i < RPL; ++i)
-                if (i == (r >> 6)) st.load[i] = Lr;
-        }
-        if (lane == 0) {
-            s.rem[e] = rem_e;
-            s.first_rec[e] = first;
-            s.nrec_e[e] = nrec - first;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < RPL; ++i) {
-        const int r = lane + 64 * i;
-        if (r < R) s.load[r] = st.load[i];
     }
     nrec_out = nrec;
     exhausted_out = exhausted;
@@ -199,9 +261,9 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
     int P, int rbits, uint32_t lds_bytes, ue_placement_layout lay,
     int32_t *__restrict__ placement) {
-    extern __shared__ int32_t lds[];
+    extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kWaves];
-    __shared__ int s_ncand, s_nrec, s_exhausted, s_quota;
+    __shared__ int s_ncand, s_nd, s_nrec, s_exhausted, s_quota;
 
     const int layer = blockIdx.x;
     const int tid = threadIdx.x;
@@ -232,7 +294,6 @@ __global__ __launch_bounds__(kBlock) void k_plan(
         int l = 0;
         for (int i = 0; i < N; ++i) l += s.cnt[r * N + i];
         s.load[r] = l;
-        s.nfree[r] = S;
         out[lay.load_before + r] = l;
     }
     __syncthreads();
@@ -246,23 +307,64 @@ __global__ __launch_bounds__(kBlock) void k_plan(
         for (int e = b; e < e_end; ++e) local += (s.load[e / N] > Q);
         int n;
         int pos = block_exclusive_sum(local, wsum, n);
+        // packed (home rank << 16 | expert), E and R below 2^16, and the
+        // count beside it
+        int2 *cand2 = reinterpret_cast<int2 *>(s.cand);
         for (int e = b; e < e_end; ++e)
-            if (s.load[e / N] > Q) s.cand[pos++] = e;
+            if (s.load[e / N] > Q)
+                cand2[pos++] = int2{((e / N) << 16) | e, s.cnt[e]};
         if (tid == 0) s_ncand = n;
     }
     __syncthreads();
     const int ncand = s_ncand;
-    // rank each candidate by (count desc, id asc)
+    // rank each candidate by (count desc, id asc); the amount it moves is
+    // its count capped by the excess its home rank still has after the
+    // rank's earlier candidates (each of those moved min(count, excess))
+    const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
     for (int i = tid; i < ncand; i += kBlock) {
-        const int e = s.cand[i];
-        const int c = s.cnt[e];
-        int pos = 0;
+        const int2 me = cand2[i];
+        const int e = me.x & 0xFFFF;
+        const int r = me.x >> 16;
+        const int c = me.y;
+        int pos = 0, before = 0;
         for (int j = 0; j < ncand; ++j) {
-            const int f = s.cand[j];
-            const int cf = s.cnt[f];
-            pos += (cf > c) || (cf == c && f < e);
+            const int2 o = cand2[j];
+            const int f = o.x & 0xFFFF;
+            const bool earlier = (o.y > c) || (o.y == c && f < e);
+            pos += earlier;
+            before += (earlier && (o.x >> 16) == r) ? o.y : 0;
         }
+        const int excess = s.load[r] - Q;
+        const int left = excess - (before < excess ? before : excess);
         s.sorted[pos] = e;
+        s.smove[pos] = c < left ? c : left;
+    }
+    // ranks eligible at the start (a spare slot, load below quota), as keys
+    // (load << rbits | rank), compacted in rank order then placed by their
+    // rank among the keys (distinct, so the order is strict)
+    {
+        const int per = (R + kBlock - 1) / kBlock;
+        const int b = tid * per;
+        const int r_end = (b + per < R) ? b + per : R;
+        int local = 0;
+        for (int r = b; r < r_end; ++r) local += (S > 0 && s.load[r] < Q);
+        int n;
+        int pos = block_exclusive_sum(local, wsum, n);
+        for (int r = b; r < r_end; ++r)
+            if (S > 0 && s.load[r] < Q)
+                s.dkey[pos++] = static_cast<int32_t>(
+                    (static_cast<uint32_t>(s.load[r]) << rbits) |
+                    static_cast<uint32_t>(r));
+        if (tid == 0) s_nd = n;
+    }
+    __syncthreads();
+    const int nd = s_nd;
+    for (int i = tid; i < nd; i += kBlock) {
+        const uint32_t k = static_cast<uint32_t>(s.dkey[i]);
+        int pos = 0;
+        for (int j = 0; j < nd; ++j)
+            pos += static_cast<uint32_t>(s.dkey[j]) < k;
+        s.dsorted[pos] = static_cast<int32_t>(k);
     }
     __syncthreads();
 
@@ -270,13 +372,13 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     if (tid < 64) {
         int nrec = 0, exhausted = 0;
         switch ((R + 63) / 64) {
-            case 1: spill_loop<1>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
-            case 2: spill_loop<2>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 1: spill_loop<1>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 2: spill_loop<2>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
             case 3:
-            case 4: spill_loop<4>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 4: spill_loop<4>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
             case 5: case 6: case 7:
-            case 8: spill_loop<8>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
-            default: spill_loop<16>(s, ncand, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 8: spill_loop<8>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            default: spill_loop<16>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
         }
         if (tid == 0) {
             s_nrec = nrec;
@@ -286,8 +388,22 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     }
     __syncthreads();
 
-    // ---- C. replica table and slot tables --------------------------------
+    // per expert: chunks placed (records of one expert are consecutive),
+    // the first of them and the remainder kept by the master; per rank: the
+    // loads after the plan. Integer adds, so the order does not matter.
     const int nrec = s_nrec;
+    for (int i = tid; i < nrec; i += kBlock) {
+        const int e = s.rec_e[i];
+        const int m = s.rec_m[i];
+        if (i == 0 || s.rec_e[i - 1] != e) s.first_rec[e] = i;
+        atomicAdd(&s.nrec_e[e], 1);
+        atomicSub(&s.rem[e], m);
+        atomicSub(&s.load[e / N], m);
+        atomicAdd(&s.load[s.rec_p[i] / NS], m);
+    }
+    __syncthreads();
+
+    // ---- C. replica table and slot tables --------------------------------
     for (int e = tid; e < E; e += kBlock) s.rep_off[e] = 1 + s.nrec_e[e];
     __syncthreads();
     const int n_rep = block_scan_inplace(s.rep_off, E, wsum);
@@ -353,7 +469,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(
 }  // namespace
 
 size_t plan_lds_bytes(int E, int R, int P) {
-    return sizeof(int32_t) * (static_cast<size_t>(7) * E + 1 + 2 * R + 5 * P);
+    return sizeof(int32_t) * (static_cast<size_t>(9) * E + 1 + 3 * R + 5 * P);
 }
 
 hipError_t plan_prepare(size_t lds_bytes) {
