@@ -70,6 +70,30 @@ def test_random_instances():
         compare_with_oracle(res, routing, E, R, S)
 
 
+def test_many_spares_and_ranks():
+    """Several spare slots per rank (destinations that take more than one
+    chunk and stay eligible), ranks beyond one wave's lanes (R > 64), and
+    skew strong enough to exhaust the slots: the planner's held-rank path
+    against the oracle."""
+    rng = np.random.default_rng(1234)
+    shapes = [(128, 128, 3), (256, 128, 2), (96, 32, 8), (64, 16, 16),
+              (512, 256, 4), (200, 100, 5), (1024, 1024, 1), (1024, 64, 12)]
+    for it, (E, R, S) in enumerate(shapes):
+        if R * (E // R + S) > 4096:
+            continue
+        k = int(rng.integers(1, 9))
+        T = int(rng.choice([3000, 9000, 20000]))
+        L = 2
+        routing = np.stack([pins.random_routing(rng, T, E, k,
+                                                float(rng.uniform(0.8, 2.5)))
+                            for _ in range(L)])
+        say(f"spares {it}: E={E} R={R} S={S} k={k} T={T}")
+        ctx = make_ctx(E, R, S, k, T, L)
+        for fused in (False, True):
+            res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
+            compare_with_oracle(res, routing, E, R, S)
+
+
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
 def test_configs_full_size(name, fused):
