@@ -16,7 +16,8 @@
 // the group with the last ticket ends with the inclusive prefix over the
 // whole layer, which is the layer's counts. Every group also writes, for
 // each of its tiles, the count of each expert in all earlier tiles of the
-// layer: the fused reroute reads those instead of scanning again. No
+// layer (and the last group the layer's totals after the last tile): the
+// fused reroute reads those instead of scanning again. No
 // fence, no global atomics on data, no clearing launch; integer sums make
 // the result exact and order-independent.
 #include "ue_internal.h"
@@ -36,7 +37,7 @@ struct LoadArgs {
     uint32_t spin_limit;
     uint64_t *state;           // [max_layers][max_groups][E]
     uint64_t *tick;            // [max_layers]
-    int32_t *tile_prefix;      // [max_layers][max_tiles][E]
+    int32_t *tile_prefix;      // [max_layers][max_tiles + 1][E]
     int32_t *counts, *invalid;
 };
 
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     const int poisoned = __syncthreads_or(bad);
 
     // per tile of the group: count of each expert in all earlier tiles
-    int32_t *tp = g.tile_prefix + static_cast<int64_t>(layer) * g.max_tiles * E;
+    int32_t *tp = g.tile_prefix +
+                  static_cast<int64_t>(layer) * (g.max_tiles + 1) * E;
     for (int e = tid; e < E; e += kBlock) {
         int run = excl[e];
         for (int s = 0; s < kLoadGroup; ++s) {
@@ -141,6 +143,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     for (int e = tid; e < E; e += kBlock) {
         const int c = excl[e] + gcnt[e];
         out[e] = c;
+        tp[static_cast<int64_t>(g.tiles) * E + e] = c;   // row tiles: totals
         part += c;
     }
     int total;

@@ -58,7 +58,7 @@ struct RerouteArgs {
     int32_t *phys, *perm, *inv_perm;
     uint64_t *state;           // [max_layers][max_tiles][E] own lookback
     uint64_t *tick;            // [max_layers] own ticket and epoch
-    const int32_t *tile_prefix;// [max_layers][max_tiles][E] from the load
+    const int32_t *tile_prefix;// [max_layers][max_tiles + 1][E] from the load
     int32_t *rank_counts, *faults;
 };
 
@@ -73,26 +73,35 @@ __device__ __forceinline__ T *at(T *p, int i) {
                                  static_cast<uint32_t>(i) * sizeof(T));
 }
 
-// Bitmap path: expert e's token bitmap is words [e*Wp, e*Wp + W) of an
-// array of int2 {bits, popcount prefix}, with an odd stride Wp so that
-// neighbouring experts fall in other banks; one 8-byte read gives an item
-// both the word and the count of the bits before it.
+// Bitmap path: expert e's token bitmap is words [e*Wp, e*Wp + W), with an
+// odd stride Wp so that neighbouring experts fall in other banks; the
+// popcount prefix of each word (at most one tile's tokens, so 16 bits) sits
+// at the same index of a second, 16-bit array.
 __host__ __device__ __forceinline__ int bm_stride(int W) { return W | 1; }
 
-// Largest region A (ints) the bitmap path may take; beyond it, the
-// configuration ranks by matching.
-constexpr int kBitmapBudget = 12288;
+// Ints of the bitmap region (words, then the 16-bit prefixes).
+__host__ __device__ __forceinline__ int bitmap_ints(int E, int W) {
+    const int n = E * bm_stride(W);
+    return n + (n + 1) / 2;
+}
+
+// Largest bitmap region (ints); beyond it, the configuration ranks by
+// matching.
+constexpr int kBitmapBudget = 9216;
+
+// Staged perm entries: (assignment - tile start) | expert << 11, one per
+// item in the tile's (expert, j) order, then one dummy per thread.
+static_assert(kRerouteTile <= 2048, "staged entries keep 11 bits of position");
+static_assert(kMaxExperts <= (1 << 20), "staged entries keep the expert above");
 
 // Size in ints of region A, shared in turn by the rank bitmaps (or the
-// per-wave counters of the matching path) and by the staged perm entries
-// (plus one dummy entry per thread); a multiple of 4 so that what follows
-// stays 16-byte aligned.
-static_assert(kRerouteTile <= 4096, "matching ranks are packed in 13 bits");
-
+// per-wave counters of the matching path) and by the staged perm entries;
+// a multiple of 4 so that what follows stays 16-byte aligned. The rest of
+// the LDS (per-expert arrays and the replica table) follows it.
 __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
-    int a = 2 * E * bm_stride(W);
+    int a = W > 0 ? bitmap_ints(E, W) : 0;
     a = a > kWaves * E ? a : kWaves * E;
-    a = a > 2 * (kRerouteTile + kBlock) ? a : 2 * (kRerouteTile + kBlock);
+    a = a > kRerouteTile + kBlock ? a : kRerouteTile + kBlock;
     return (a + 3) & ~3;
 }
 
@@ -102,7 +111,7 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
 // one tile by ticket and finds the prefix by lookback. (A persistent grid
 // that loads the replica table once and loops over tiles measured no
 // faster: the hardware already overlaps one workgroup's table reads with
-// others' work.)
+// others' work, while the LDS per workgroup sets how many share a CU.)
 template <bool kAfterLoad>
 __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
@@ -130,8 +139,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     int32_t *tbase = torder + E;
     int32_t *rep_off = tbase + E;
     int32_t *rep_slot = rep_off + E + 1;
-    int32_t *rep_lo = rep_slot + P;
-    int32_t *rep_hi = rep_lo + P;
+    int32_t *rep_hi = rep_slot + P;   // capacity prefix: end of each replica
     int32_t *slot_off = rep_hi + P;
     int32_t *rank_hist = slot_off + P;
     // the carve-up must fit the launch's LDS (checked, not assumed); a
@@ -151,15 +159,24 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int A = g.A;
     constexpr int kPerThread = kMaxExperts / kBlock;
     int32_t ids[kRerouteItems];
-    int32_t pre_reg[kPerThread];
+    int32_t pre_reg[kPerThread], pre_next[kPerThread];
     int tile = 0;
-    int tile0 = 0, a0 = 0;
+    // Item i of a lane is assignment aL + 64 i: each step of a wave covers
+    // 64 consecutive assignments, so global reads and writes coalesce.
+    // (Spreading a step's tokens 32 apart, to keep a hot expert's bitmap
+    // ORs off one LDS word, measured slower: the accesses no longer
+    // coalesce.)
+    const int k = g.k;
+    auto lane_base = [&](int t) {
+        return t * kRerouteTile + w * 64 * kRerouteItems + lane;
+    };
+    int tile0 = 0, aL = 0;
     // the tile's ids (and, after a load, its prefixes): issued first so
     // that their latency overlaps the placement table reads
     // (a full tile loads unconditionally at immediate offsets; the ragged
     // last tile clamps its reads into the layer and drops what lies beyond)
     auto load_ids = [&](int t, int32_t *dst) {
-        const int first = t * kRerouteTile + w * 64 * kRerouteItems + lane;
+        const int first = lane_base(t);
         if ((t + 1) * kRerouteTile <= A) {
             const int32_t *src = at(routing_l, first);
 #pragma unroll
@@ -178,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     };
     auto load_prefix = [&](int t, int32_t *dst) {
         const int32_t *tp = g.tile_prefix +
-                            (static_cast<int64_t>(layer) * g.max_tiles + t) * E;
+                            (static_cast<int64_t>(layer) * (g.max_tiles + 1) + t) * E;
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             const int e = tid + q * kBlock;
@@ -190,6 +207,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         if (tile >= g.tiles) return;
         load_ids(tile, ids);
         load_prefix(tile, pre_reg);
+        load_prefix(tile + 1, pre_next);   // row tiles holds the totals
         if (tid == 0) s_epoch = 0;
     } else if (tid == 0) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
@@ -210,28 +228,49 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         rep_hi[p] = cap > 0 ? cap : 0;     // capacity, until the prefix below
     }
     const bool bitmap = W > 0;
-    int2 *bm = reinterpret_cast<int2 *>(area);   // [E][Wp] {bits, prefix}
+    uint32_t *bm = reinterpret_cast<uint32_t *>(area);          // [E][Wp]
+    uint16_t *bpre = reinterpret_cast<uint16_t *>(area + E * Wp);  // [E][Wp]
     if (bitmap)
-        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = int2{0, 0};
+        for (int i = tid; i < E * Wp; i += kBlock) bm[i] = 0u;
     __syncthreads();
     if (!kAfterLoad) {
         tile = static_cast<int>(s_ticket);
         if (tile >= g.tiles) return;   // only after a corrupted earlier launch
         load_ids(tile, ids);
     }
-    // capacity prefix of each replica within its expert, from LDS
+    // capacity prefix of each replica within its expert, from LDS; replica
+    // r of expert e then covers j in [r == rep_off[e] ? 0 : rep_hi[r-1],
+    // rep_hi[r])
     for (int e = tid; e < E; e += kBlock) {
         int run = 0;
         const int hi = rep_off[e + 1];
         for (int i = rep_off[e]; i < hi; ++i) {
-            rep_lo[i] = run;
             run += rep_hi[i];
             rep_hi[i] = run;
         }
     }
+    // Physical slot and dispatch position of assignment j of expert e, or
+    // -1 for both if no replica covers j (only a plan made for other counts
+    // leaves such assignments).
+    auto locate = [&](int e, int j, int &p, int &pos) {
+        p = -1;
+        pos = -1;
+        int lo = 0;
+        for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
+            const int hi = rep_hi[r];
+            if (j < hi) {
+                if (rep_slot[r] >= 0) {
+                    p = rep_slot[r];
+                    pos = slot_off[p] + (j - lo);
+                }
+                return;
+            }
+            lo = hi;
+        }
+    };
     const uint32_t epoch = s_epoch;
     tile0 = tile * kRerouteTile;
-    a0 = tile0 + w * 64 * kRerouteItems + lane;
+    aL = lane_base(tile);
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i)
         ids[i] = static_cast<uint32_t>(ids[i]) < static_cast<uint32_t>(E) ? ids[i]
@@ -241,62 +280,75 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     int32_t rank[kRerouteItems];
     int dup = 0;
     if (bitmap) {
-        // token of item a0 + 64 i relative to the tile's first token,
-        // stepped without a division per item
-        const int k = g.k;
+        // token of item i relative to the tile's first token, stepped
+        // without a division per item
         const uint32_t uk = static_cast<uint32_t>(k);
         const int t_first = static_cast<int>(static_cast<uint32_t>(tile0) / uk);
-        const uint32_t qa = static_cast<uint32_t>(a0) / uk;
+        const uint32_t qa = static_cast<uint32_t>(aL) / uk;
         int tl = static_cast<int>(qa) - t_first;
-        int rm = static_cast<int>(static_cast<uint32_t>(a0) - qa * uk);
+        int rm = static_cast<int>(static_cast<uint32_t>(aL) - qa * uk);
         const int q64 = 64 / k, r64 = 64 % k;
         // Branch-free: an id out of range ORs nothing into expert 0's
-        // word, so every lane issues the same instructions.
+        // word, so every lane issues the same instructions. After a load
+        // the OR returns nothing (a repeated expert shows up below as a
+        // popcount short of the load's count); otherwise the returned word
+        // shows a bit already set.
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             rank[i] = tl;                  // the token, until the read-back
             const uint32_t bit = id >= 0 ? 1u << (tl & 31) : 0u;
-            const uint32_t old = atomicOr(
-                reinterpret_cast<uint32_t *>(area) +
-                    2 * ((id >= 0 ? id : 0) * Wp + (tl >> 5)),
-                bit);
-            dup |= (old & bit) != 0;
+            uint32_t *word = bm + (id >= 0 ? id : 0) * Wp + (tl >> 5);
+            if (kAfterLoad) {
+                __hip_atomic_fetch_or(word, bit, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
+                const uint32_t old = atomicOr(word, bit);
+                dup |= (old & bit) != 0;
+            }
             rm += r64;
             const int carry = rm >= k;
             rm -= carry ? k : 0;
             tl += q64 + carry;
         }
     }
-    const int use_match = !bitmap || __syncthreads_or(dup);
+    if (kAfterLoad && bitmap) __syncthreads();
+    int use_match = !bitmap || (!kAfterLoad && __syncthreads_or(dup));
     if (!use_match) {
         // prefix of popcounts over each expert's words (read in batches so
-        // the reads overlap); tile counts
-        for (int e = tid; e < E; e += kBlock) {
-            int2 *row = bm + e * Wp;
+        // the reads overlap); tile counts, checked against the load's
+        for (int q = 0; q < kPerThread; ++q) {
+            const int e = tid + q * kBlock;
+            if (e >= E) break;
+            const uint32_t *row = bm + e * Wp;
+            uint16_t *prow = bpre + e * Wp;
             int run = 0;
             for (int i0 = 0; i0 < W; i0 += 8) {
                 uint32_t bits[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    bits[j] = i0 + j < W ? static_cast<uint32_t>(row[i0 + j].x) : 0u;
+                    bits[j] = i0 + j < W ? row[i0 + j] : 0u;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if (i0 + j < W) row[i0 + j].y = run;
+                    if (i0 + j < W) prow[i0 + j] = static_cast<uint16_t>(run);
                     run += __builtin_popcount(bits[j]);
                 }
             }
             tcount[e] = run;
             torder[e] = run;
+            if (kAfterLoad) dup |= run != pre_next[q] - pre_reg[q];
         }
-        __syncthreads();
+        if (kAfterLoad) use_match = __syncthreads_or(dup);
+        else __syncthreads();
+    }
+    if (!use_match) {
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             const int tl = rank[i];
-            const int2 v = bm[(id >= 0 ? id : 0) * Wp + (tl >> 5)];
+            const int word = (id >= 0 ? id : 0) * Wp + (tl >> 5);
             const uint32_t below = (1u << (tl & 31)) - 1u;
-            rank[i] = v.y + __builtin_popcount(static_cast<uint32_t>(v.x) & below);
+            rank[i] = bpre[word] + __builtin_popcount(bm[word] & below);
         }
     } else {
         // matching path: ranks within rounds of 64 consecutive items
@@ -382,28 +434,26 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     // replica covering the tile's first j, that replica's slot and the
     // dispatch position of that first j.
     for (int e = tid; e < E; e += kBlock) {
-        const int j0 = tbase[e];
-        int q = -1, lim = 0, pos0 = 0;
-        for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-            if (j0 < rep_hi[r]) {
-                if (j0 >= rep_lo[r] && rep_slot[r] >= 0) {
-                    q = rep_slot[r];
-                    lim = rep_hi[r] - j0;
-                    pos0 = slot_off[q] + (j0 - rep_lo[r]);
+        int q, pos0;
+        locate(e, tbase[e], q, pos0);
+        int lim = 0;
+        if (q >= 0) {
+            // the covering replica's end: the first capacity prefix above j0
+            for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
+                if (tbase[e] < rep_hi[r]) {
+                    lim = rep_hi[r] - tbase[e];
+                    break;
                 }
-                break;
             }
         }
-        einfo[e] = int4{torder[e], q >= 0 ? lim : 0, q, pos0};
+        einfo[e] = int4{torder[e], lim, q, pos0};
     }
     __syncthreads();
-    // [tile] {a, pos} in (expert, j) order, then one dummy entry per thread
-    // that items without a valid id write to, so the stores need no branch
-    int2 *stage = reinterpret_cast<int2 *>(area);
+    uint32_t *stage = reinterpret_cast<uint32_t *>(area);
     const bool full_tile = tile0 + kRerouteTile <= A;
-    int32_t *phys_t = at(phys_l, a0);
-    int32_t *inv_t = inv_l ? at(inv_l, a0) : nullptr;
-    int p_out[kRerouteItems], pos_out[kRerouteItems], s_out[kRerouteItems];
+    int32_t *phys_t = at(phys_l, aL);
+    int32_t *inv_t = inv_l ? at(inv_l, aL) : nullptr;
+    int p_out[kRerouteItems], pos_out[kRerouteItems];
     bool slow = false;
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
@@ -414,7 +464,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         slow |= id >= 0 && !fast;
         p_out[i] = fast ? f.z : -1;
         pos_out[i] = fast ? f.w + jt : -1;
-        s_out[i] = id >= 0 ? f.x + jt : kRerouteTile + tid;
+        stage[id >= 0 ? f.x + jt : kRerouteTile + tid] =
+            static_cast<uint32_t>(64 * i + aL - tile0) |
+            (static_cast<uint32_t>(id >= 0 ? id : 0) << 11);
     }
     // Items past the replica covering the tile's first j (or faults) walk
     // the expert's capacity prefixes; rare, so skipped per wave.
@@ -423,27 +475,14 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             if (id < 0 || p_out[i] >= 0) continue;
-            const int j = tbase[id] + rank[i];
-            for (int r = rep_off[id]; r < rep_off[id + 1]; ++r) {
-                if (j < rep_hi[r]) {
-                    if (j >= rep_lo[r] && rep_slot[r] >= 0) {
-                        p_out[i] = rep_slot[r];
-                        pos_out[i] = slot_off[p_out[i]] + (j - rep_lo[r]);
-                    }
-                    break;
-                }
-            }
+            locate(id, tbase[id] + rank[i], p_out[i], pos_out[i]);
         }
     }
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
-        int p = p_out[i], pos = pos_out[i];
-        const bool ok = p >= 0 && pos >= 0 && pos < A;
-        p = ok ? p : -1;
-        pos = ok ? pos : -1;
-        stage[s_out[i]] = int2{a0 + 64 * i, pos};
-        p_out[i] = p;
-        pos_out[i] = pos;
+        const bool ok = p_out[i] >= 0 && pos_out[i] >= 0 && pos_out[i] < A;
+        p_out[i] = ok ? p_out[i] : -1;
+        pos_out[i] = ok ? pos_out[i] : -1;
     }
     if (full_tile) {
 #pragma unroll
@@ -454,16 +493,24 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     } else {
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
-            if (a0 + 64 * i >= A) continue;
+            if (aL + 64 * i >= A) continue;
             __builtin_nontemporal_store(p_out[i], phys_t + 64 * i);
             if (inv_t) __builtin_nontemporal_store(pos_out[i], inv_t + 64 * i);
         }
     }
     __syncthreads();
+    // perm in the tile's (expert, j) order: each entry's dispatch position
+    // again from its expert's fast path (or the replica walk)
     const int n_valid = torder[E - 1] + tcount[E - 1];
-    for (int s = tid; s < n_valid; s += kBlock) {
-        const int2 v = stage[s];
-        if (v.y >= 0) *at(perm_l, v.y) = v.x;
+    for (int s2 = tid; s2 < n_valid; s2 += kBlock) {
+        const uint32_t v = stage[s2];
+        const int e = static_cast<int>(v >> 11);
+        const int4 f = einfo[e];
+        const int jt = s2 - f.x;
+        int p = f.z, pos = f.w + jt;
+        if (jt >= f.y) locate(e, tbase[e] + jt, p, pos);
+        if (p >= 0 && pos >= 0 && pos < A)
+            *at(perm_l, pos) = tile0 + static_cast<int>(v & 2047u);
     }
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
@@ -475,19 +522,21 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     for (int e = tid; e < E; e += kBlock) {
         const int total = tbase[e] + tcount[e];
         part_valid += total;
-        int placed = 0;
+        int placed = 0, lo = 0;
         for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-            const int lo = rep_lo[r], hi = rep_hi[r];
+            const int hi = rep_hi[r];
             const int top = total < hi ? total : hi;
-            if (top <= lo || rep_slot[r] < 0) continue;
-            const int64_t first = slot_off[rep_slot[r]];
-            const int64_t n = top - lo;
-            const int64_t lo_ok = first < 0 ? -first : 0;
-            const int64_t hi_ok = g.A - first < n ? g.A - first : n;
-            const int in_range =
-                hi_ok > lo_ok ? static_cast<int>(hi_ok - lo_ok) : 0;
-            if (in_range) atomicAdd(&rank_hist[rep_slot[r] / g.NS], in_range);
-            placed += in_range;
+            if (top > lo && rep_slot[r] >= 0) {
+                const int64_t first = slot_off[rep_slot[r]];
+                const int64_t n = top - lo;
+                const int64_t lo_ok = first < 0 ? -first : 0;
+                const int64_t hi_ok = g.A - first < n ? g.A - first : n;
+                const int in_range =
+                    hi_ok > lo_ok ? static_cast<int>(hi_ok - lo_ok) : 0;
+                if (in_range) atomicAdd(&rank_hist[rep_slot[r] / g.NS], in_range);
+                placed += in_range;
+            }
+            lo = hi;
         }
         part_over += total - placed;
     }
@@ -509,15 +558,15 @@ int tile_tokens(int k) { return (kRerouteTile - 1) / k + 2; }
 int reroute_bitmap_words(int E, int k) {
     const int W = (tile_tokens(k) + 31) / 32;
     // the bitmaps and their prefixes share region A with the staged perm
-    return 2 * E * bm_stride(W) <= kBitmapBudget ? W : 0;
+    return bitmap_ints(E, W) <= kBitmapBudget ? W : 0;
 }
 
 size_t reroute_lds_bytes(int E, int R, int P, int k) {
     const int W = reroute_bitmap_words(E, k);
     // region A; einfo (4 words per expert), tcount, torder, tbase;
-    // rep_off (+1); four P-sized tables; the rank histogram
+    // rep_off (+1); three P-sized tables; the rank histogram
     return sizeof(int32_t) * (static_cast<size_t>(region_a_ints(E, W)) +
-                              static_cast<size_t>(8) * E + 1 + 4 * P + R);
+                              static_cast<size_t>(8) * E + 1 + 3 * P + R);
 }
 
 hipError_t reroute_prepare(size_t lds_bytes) {

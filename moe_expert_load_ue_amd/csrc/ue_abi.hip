@@ -167,7 +167,8 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     };
     const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_groups * E);
     const size_t o_ltick = take(sizeof(uint64_t) * Lmax);
-    const size_t o_tprefix = take(sizeof(int32_t) * Lmax * rr_tiles * E);
+    // per-tile expert prefixes: one row per tile plus the totals
+    const size_t o_tprefix = take(sizeof(int32_t) * Lmax * (rr_tiles + 1) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
     c->ws_bytes = off;
