@@ -69,6 +69,8 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     const int32_t *src = g.routing + static_cast<int64_t>(layer) * g.A;
     const int tile_first = grp * kLoadGroup;
     // Issue the loads of every full tile of the group before counting.
+    // Plain (temporal) loads: the fused reroute reads the same routing
+    // right after, and finds it in the device-wide cache.
     i32x4 r[kLoadGroup][kLoadItems / 4];
     bool full[kLoadGroup];
 #pragma unroll
@@ -79,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
             const i32x4 *v = reinterpret_cast<const i32x4 *>(src + t0);
 #pragma unroll
             for (int i = 0; i < kLoadItems / 4; ++i)
-                r[s][i] = __builtin_nontemporal_load(v + i * kBlock + tid);
+                r[s][i] = v[i * kBlock + tid];
         }
     }
 #pragma unroll

@@ -174,21 +174,21 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     // the tile's ids (and, after a load, its prefixes): issued first so
     // that their latency overlaps the placement table reads
     // (a full tile loads unconditionally at immediate offsets; the ragged
-    // last tile clamps its reads into the layer and drops what lies beyond)
+    // last tile clamps its reads into the layer and drops what lies beyond;
+    // plain loads, since after the load kernel the routing sits in the
+    // device-wide cache)
     auto load_ids = [&](int t, int32_t *dst) {
         const int first = lane_base(t);
         if ((t + 1) * kRerouteTile <= A) {
             const int32_t *src = at(routing_l, first);
 #pragma unroll
             for (int i = 0; i < kRerouteItems; ++i)
-                dst[i] = __builtin_nontemporal_load(src + 64 * i);
+                dst[i] = src[64 * i];
         } else {
 #pragma unroll
             for (int i = 0; i < kRerouteItems; ++i) {
                 const int a = first + 64 * i;
-                const int v = A > 0 ? __builtin_nontemporal_load(
-                                          at(routing_l, a < A ? a : A - 1))
-                                    : -1;
+                const int v = A > 0 ? *at(routing_l, a < A ? a : A - 1) : -1;
                 dst[i] = a < A ? v : -1;
             }
         }
