@@ -1,5 +1,6 @@
 """Builds libue.so, the HIP library behind the C ABI in include/ue.h, for
-gfx950 with hipcc. Run as ``python -m moe_expert_load_ue_amd.build``."""
+gfx950 with hipcc, and the standalone HBM probe (csrc/hbm_probe.hip, not
+part of the library). Run as ``python -m moe_expert_load_ue_amd.build``."""
 from __future__ import annotations
 
 import os
@@ -11,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libue.so")
+PROBE = os.path.join(HERE, "hbm_probe")
 SOURCES = ["ue_abi.hip", "k_load.hip", "k_plan.hip", "k_reroute.hip",
            "k_stream.hip"]
 
@@ -43,5 +45,18 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_probe(verbose: bool = False) -> str:
+    tmp = PROBE + ".tmp"
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-o", tmp, os.path.join(CSRC, "hbm_probe.hip")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe(verbose="-v" in sys.argv))
