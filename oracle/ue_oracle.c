@@ -66,6 +66,11 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
 /* ---------------------------------------------------------------------- */
 /* Step 2. Quota plan for one layer.
  *
+ * policy 0: every chunk goes to the least-loaded eligible rank (the rule
+ * stated above). policy 1 (best fit): when that rank would be left with
+ * room to spare, the chunk goes to the eligible rank with the smallest
+ * headroom that still takes all of it, ties to the lowest id.
+ *
  * scalars[0] = quota Q
  * scalars[1] = exhausted (1 if an overloaded rank still had excess but no
  *              rank was left with a free spare slot and load < Q)
@@ -83,9 +88,10 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  *
  * Returns 0, or -1 if the shape is not one the slot model covers. */
 int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
-             int32_t *scalars, int32_t *rep_off, int32_t *rep_slot,
-             int32_t *rep_cap, int32_t *slot_expert, int32_t *slot_cap,
-             int32_t *slot_off, int32_t *load_before, int32_t *load_after)
+             int32_t policy, int32_t *scalars, int32_t *rep_off,
+             int32_t *rep_slot, int32_t *rep_cap, int32_t *slot_expert,
+             int32_t *slot_cap, int32_t *slot_off, int32_t *load_before,
+             int32_t *load_after)
 {
     if (E <= 0 || R <= 0 || S < 0 || E % R != 0)
         return -1;
@@ -162,6 +168,19 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
             int64_t m = load[r] - Q;
             if (rem[e] < m)
                 m = rem[e];
+            /* Policy 1, best fit: when the least-loaded rank could take
+             * the whole amount with room to spare, send it instead to the
+             * eligible rank whose headroom is the smallest that still
+             * holds it (the most loaded such rank; ties: lowest id). */
+            if (policy == 1 && m < Q - load[d]) {
+                int32_t b = d;
+                for (int32_t x = 0; x < R; ++x) {
+                    if (nfree[x] > 0 && load[x] < Q && Q - load[x] >= m &&
+                        load[x] > load[b])
+                        b = x;
+                }
+                d = b;
+            }
             if (Q - load[d] < m)
                 m = Q - load[d];
             /* lowest free spare slot of d */

@@ -49,7 +49,8 @@ def _eq(name, got, want):
 
 
 def check_golden(g):
-    pl = oracle.plan(np.asarray(g["counts"], np.int32), g["R"], g["S"])
+    pl = oracle.plan(np.asarray(g["counts"], np.int32), g["R"], g["S"],
+                     g.get("policy", 0))
     for key in ("quota", "exhausted", "residual", "n_rep"):
         assert pl[key] == g[key], f"{g['name']}: {key} {pl[key]} != {g[key]}"
     for key in ("load_before", "load_after", "rep_off", "slot_expert",
@@ -107,12 +108,12 @@ def check_load(routing, E):
     return counts[0]
 
 
-def check_plan(counts, R, S, A=None):
+def check_plan(counts, R, S, A=None, policy=0):
     counts = np.asarray(counts, np.int64)
     E = counts.size
     N, NS = E // R, E // R + S
     P = R * NS
-    pl = oracle.plan(counts.astype(np.int32), R, S)
+    pl = oracle.plan(counts.astype(np.int32), R, S, policy)
     Q = pl["quota"]
     total = int(counts.sum())
     A = total if A is None else A
@@ -188,7 +189,61 @@ def check_plan(counts, R, S, A=None):
     else:
         assert residual == 0 and after.max(initial=0) <= Q, \
             "every rank within quota whenever slots suffice"
+    check_choices(counts, R, S, policy, pl)
     return pl
+
+
+def check_choices(counts, R, S, policy, pl):
+    """Replays the plan's chunks in creation order (candidates by count
+    desc, id asc; each expert's replicas in table order) from the native
+    loads and checks every step against the rule: the destination is
+    eligible (a free spare slot, load below Q); under policy 0 it is the
+    least-loaded such rank (lowest id on ties); under policy 1 too, unless
+    the amount is below that rank's headroom, when it is the eligible rank
+    with the smallest headroom that holds the amount (lowest id on ties);
+    the chunk is min(source excess, expert remainder, headroom) and takes
+    the lowest free spare slot; an expert stops short only when no rank is
+    eligible, and then nothing moves after it."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    N, NS = E // R, E // R + S
+    Q = pl["quota"]
+    L = counts.reshape(R, N).sum(axis=1).astype(np.int64)
+    free = np.full(R, S)
+    cands = sorted((e for e in range(E) if L[e // N] > Q),
+                   key=lambda e: (-counts[e], e))
+    stopped = False
+    for e in cands:
+        chunks = [(int(pl["rep_slot"][i]), int(pl["rep_cap"][i]))
+                  for i in range(pl["rep_off"][e] + 1, pl["rep_off"][e + 1])]
+        if stopped:
+            assert not chunks, "nothing moves after the plan stops"
+            continue
+        r, rem = e // N, int(counts[e])
+        while L[r] > Q and rem > 0:
+            elig = [x for x in range(R) if free[x] > 0 and L[x] < Q]
+            if not elig:
+                assert not chunks, "a chunk placed with no eligible rank"
+                stopped = True
+                break
+            assert chunks, "an expert stopped while a rank was eligible"
+            p, m = chunks.pop(0)
+            d = p // NS
+            need = min(int(L[r] - Q), rem)
+            least = min(elig, key=lambda x: (L[x], x))
+            want = least
+            if policy == 1 and need < Q - L[least]:
+                fits = [x for x in elig if Q - L[x] >= need]
+                want = min(fits, key=lambda x: (Q - L[x], x))
+            assert d == want, f"expert {e}: chunk to rank {d}, rule says {want}"
+            assert m == min(need, int(Q - L[d])), "chunk size"
+            assert p == d * NS + N + (S - free[d]), "lowest free spare slot"
+            L[r] -= m
+            L[d] += m
+            free[d] -= 1
+            rem -= m
+        assert not chunks, f"expert {e}: more chunks than the rule places"
+    assert bool(pl["exhausted"]) == stopped, "exhausted flag"
 
 
 def check_reroute(routing, pl):
@@ -226,9 +281,9 @@ def check_reroute(routing, pl):
     return rr
 
 
-def check_instance(routing, E, R, S):
+def check_instance(routing, E, R, S, policy=0):
     counts = check_load(routing, E)
-    pl = check_plan(counts, R, S)
+    pl = check_plan(counts, R, S, policy=policy)
     check_reroute(routing, pl)
     return pl
 
@@ -364,12 +419,12 @@ def optimum_max_load(counts, R, S):
     return best
 
 
-def check_against_optimum(counts, R, S):
+def check_against_optimum(counts, R, S, policy=0):
     """Returns greedy / optimum. The greedy plan is one of the placements
     enumerated, so the optimum can never exceed it; every placement has a
     rank at or above ceil(total / R) = Q, so when slots suffice the greedy
     (which then ends with every rank <= Q) is optimal."""
-    pl = check_plan(counts, R, S)
+    pl = check_plan(counts, R, S, policy=policy)
     greedy = int(pl["load_after"].max(initial=0))
     opt = optimum_max_load(list(counts), R, S)
     assert opt <= greedy, "greedy beats the exhaustive optimum"

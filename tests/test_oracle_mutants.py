@@ -56,6 +56,10 @@ MUTANTS = {
     "quota counts experts": ("(total + R - 1) / R", "(total + E - 1) / E"),
     "no exhausted flag": ("exhausted = 1;\n                break;",
                           "break;"),
+    "best fit takes the most headroom": ("load[x] > load[b])",
+                                         "load[x] < load[b])"),
+    "best fit ties highest id": ("load[x] > load[b])", "load[x] >= load[b])"),
+    "best fit ignores the fit": ("Q - load[x] >= m &&", ""),
     "replica before master": ("rep_slot[n] = (e / N) * NS + (e % N);\n"
                               "        rep_cap[n] = (int32_t)rem[e];\n"
                               "        ++n;\n",
@@ -69,6 +73,8 @@ def run_all_pins():
     rng = np.random.default_rng(11)
     for _ in range(300):
         pins.check_instance(*pins.random_instance(rng))
+    for _ in range(300):
+        pins.check_instance(*pins.random_instance(rng), policy=1)
     pins.check_no_spares(np.random.default_rng(1))
     pins.check_one_rank(np.random.default_rng(2))
     pins.check_balanced()

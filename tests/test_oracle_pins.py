@@ -11,19 +11,21 @@ def test_golden(case):
     pins.check_golden(case)
 
 
-def test_invariants_random():
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+def test_invariants_random(policy):
     rng = np.random.default_rng(20260602)
     for _ in range(1500):
-        pins.check_instance(*pins.random_instance(rng))
+        pins.check_instance(*pins.random_instance(rng), policy=policy)
 
 
-def test_invariants_larger():
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+def test_invariants_larger(policy):
     rng = np.random.default_rng(7)
     for _ in range(40):
         routing, E, R, S = pins.random_instance(
             rng, max_ranks=32, max_native=8, max_spare=3, max_tokens=2000,
             max_k=8)
-        pins.check_instance(routing, E, R, S)
+        pins.check_instance(routing, E, R, S, policy=policy)
 
 
 def test_no_spares():
@@ -46,7 +48,8 @@ def test_invalid_ids():
     pins.check_invalid_ids()
 
 
-def test_brute_force_optimum():
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+def test_brute_force_optimum(policy):
     """Exhaustive optimum on tiny instances: greedy == optimum == Q whenever
     slots suffice; otherwise the optimum never exceeds greedy. The worst
     observed greedy/optimum ratio is reported."""
@@ -60,9 +63,9 @@ def test_brute_force_optimum():
         E = R * N
         counts = rng.integers(0, 9, size=E).astype(np.int32)
         counts[rng.integers(0, E)] += int(rng.integers(0, 12))
-        ratio = pins.check_against_optimum(counts, R, S)
+        ratio = pins.check_against_optimum(counts, R, S, policy)
         worst = max(worst, ratio)
         n_exhausted += ratio > 1.0
-    print(f"greedy/optimum worst {worst:.3f}; above optimum in "
+    print(f"policy {policy}: greedy/optimum worst {worst:.3f}; above optimum in "
           f"{n_exhausted}/60")
     assert worst <= 2.0
