@@ -48,12 +48,12 @@ class Rebalance:
     """Preallocated buffers and the one ABI call of a rebalance
     (ue_rebalance: load -> plan -> reroute on the stream)."""
 
-    def __init__(self, ue, cfg, routing, dev):
+    def __init__(self, ue, cfg, routing, dev, policy=0):
         import torch
         self.ue = ue
         L, T, k = routing.shape
         self.ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk,
-                              T, L, device=dev)
+                              T, L, device=dev, plan_policy=policy)
         self.routing = routing
         i32 = dict(dtype=torch.int32, device=dev)
         self.out = dict(counts=torch.empty((L, cfg.experts), **i32),
@@ -133,11 +133,22 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     return cfg, rb, ms, phases, ms_one
 
 
-def bench_large_ep(ue, W, dev):
+def bench_best_fit(ue, cfg, routing, dev, steps, warmup):
+    """The same rebalance under the best-fit planner rule: time and the
+    balance it reaches."""
+    rb = Rebalance(ue, cfg, routing, dev, policy=ue.PLAN_BEST_FIT)
+    ms = time_steps(rb.step, steps, warmup)
+    phases = phase_times(rb, max(steps, 10))
+    return {"us_per_rebalance": round(ms * 1000.0, 2),
+            "kernel_us": {k: round(v * 1000.0, 2) for k, v in phases.items()},
+            "imbalance": imbalance(rb, cfg)}
+
+
+def bench_large_ep(ue, W, dev, policy=0):
     import torch
     cfg = W.CONFIGS["large_ep"]
     routing = W.make_routing(cfg, device=dev)
-    rb = Rebalance(ue, cfg, routing, dev)
+    rb = Rebalance(ue, cfg, routing, dev, policy)
     for _ in range(20):
         rb.step()
     torch.cuda.synchronize()
@@ -152,6 +163,8 @@ def bench_large_ep(ue, W, dev):
     phases = phase_times(rb, 50)
     return {"workload": "large_ep: E=256 k=8 R=256 (1 native + 1 spare) "
                         "T=262144, 1 layer",
+            "planner": ("best fit" if policy == ue.PLAN_BEST_FIT
+                        else "least loaded"),
             "us_per_rebalance_p10_p50_p90": [round(t[reps // 10], 2),
                                              round(t[reps // 2], 2),
                                              round(t[9 * reps // 10], 2)],
@@ -369,12 +382,18 @@ def main():
                      "algorithmic_bytes_per_launch": rr_bytes},
         "imbalance": imbalance(rb, cfg),
     }
+    if not args.no_extra:
+        log("dsv3 under the best-fit planner")
+        line["best_fit"] = bench_best_fit(ue, cfg, rb.routing, dev,
+                                          args.steps, args.warmup)
     routing_host = rb.routing.cpu()
     del rb
     torch.cuda.empty_cache()
     if not args.no_extra:
         log("large_ep")
         line["large_ep"] = bench_large_ep(ue, W, dev)
+        line["large_ep_best_fit"] = bench_large_ep(ue, W, dev,
+                                                   ue.PLAN_BEST_FIT)
         log("stream")
         line["stream"] = bench_stream(ue, W, dev)
         log("gather")

@@ -65,7 +65,9 @@ typedef enum ue_status {
  *                      P = R*(N+S) <= 4096
  *   topk k             experts per token, 1..E
  *   max_tokens         largest T of any call (T*k < 2^30)
- *   max_layers         largest L (layers or microbatches) of any call      */
+ *   max_layers         largest L (layers or microbatches) of any call
+ *   plan_policy        destination rule of the planner (see ue_plan):
+ *                      UE_PLAN_LEAST_LOADED (0) or UE_PLAN_BEST_FIT (1)    */
 typedef struct ue_config {
     int32_t num_experts;
     int32_t num_ranks;
@@ -73,7 +75,15 @@ typedef struct ue_config {
     int32_t topk;
     int32_t max_tokens;
     int32_t max_layers;
+    int32_t plan_policy;
 } ue_config;
+
+enum {
+    UE_PLAN_LEAST_LOADED = 0,  /* every chunk to the least-loaded rank     */
+    UE_PLAN_BEST_FIT = 1       /* a chunk the least-loaded rank would not
+                                  fill goes to the eligible rank with the
+                                  smallest headroom that holds it          */
+};
 
 typedef struct ue_ctx ue_ctx;
 
@@ -147,6 +157,10 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
  *   least-loaded rank (ties: lowest id) that has a free spare slot and load
  *   < Q; chunk = min(source excess, expert remainder, destination
  *   headroom); with no such rank the plan stops (exhausted = 1).
+ *   Under UE_PLAN_BEST_FIT, when the amount left (min of source excess and
+ *   expert remainder) is below the least-loaded rank's headroom, it goes
+ *   whole to the eligible rank with the smallest headroom >= the amount
+ *   (ties: lowest id) instead.
  *   counts     device, int32 [L, E] (e.g. from ue_load)
  *   placement  device, L blocks of ue_placement_bytes() bytes, out
  * Fully on the device; nothing returns to the host. */

@@ -39,7 +39,10 @@ class ue_config(ctypes.Structure):
                 ("spare_per_rank", ctypes.c_int32),
                 ("topk", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32),
-                ("max_layers", ctypes.c_int32)]
+                ("max_layers", ctypes.c_int32),
+                ("plan_policy", ctypes.c_int32)]
+
+PLAN_LEAST_LOADED, PLAN_BEST_FIT = 0, 1
 
 
 PLACEMENT_FIELDS = ("words", "quota", "exhausted", "residual", "n_rep",
@@ -132,17 +135,18 @@ class Context:
 
     def __init__(self, num_experts: int, num_ranks: int, spare_per_rank: int,
                  topk: int, max_tokens: int, max_layers: int = 1,
-                 device=None):
+                 device=None, plan_policy: int = PLAN_LEAST_LOADED):
         self.device = torch.device(device if device is not None else
                                    f"cuda:{torch.cuda.current_device()}")
         self.E, self.R, self.S = int(num_experts), int(num_ranks), int(
             spare_per_rank)
         self.k, self.max_tokens = int(topk), int(max_tokens)
         self.max_layers = int(max_layers)
+        self.plan_policy = int(plan_policy)
         self.N = self.E // self.R if self.R else 0
         self.P = self.R * (self.N + self.S)
         cfg = ue_config(self.E, self.R, self.S, self.k, self.max_tokens,
-                        self.max_layers)
+                        self.max_layers, self.plan_policy)
         h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             rc = library().ue_create(ctypes.byref(cfg), ctypes.byref(h))
@@ -216,9 +220,10 @@ class Context:
 
 
 def ue_create(num_experts, num_ranks, spare_per_rank, topk, max_tokens,
-              max_layers=1, device=None) -> Context:
+              max_layers=1, device=None, plan_policy=PLAN_LEAST_LOADED
+              ) -> Context:
     return Context(num_experts, num_ranks, spare_per_rank, topk, max_tokens,
-                   max_layers, device)
+                   max_layers, device, plan_policy)
 
 
 def ue_destroy(ctx: Context):

@@ -11,6 +11,11 @@
 //   free spare slot of the least-loaded rank (ties: lowest id) that has a
 //   free spare slot and load < Q; chunk = min(source excess, expert
 //   remainder, destination headroom); no such rank stops the plan.
+//   A second rule (best fit, chosen per context) differs in one step: when
+//   the amount left (min of source excess and expert remainder) is below
+//   the least-loaded rank's headroom, it goes whole to the eligible rank
+//   with the smallest headroom that still holds it (ties: lowest id), so
+//   partly filled ranks close up instead of many ranks each taking a bit.
 //
 // Layout of the work:
 //   A. all 256 threads: counts and rank loads into LDS, the quota, the
@@ -139,10 +144,17 @@ __device__ __forceinline__ uint32_t wave_sat_inclusive_sum(uint32_t x) {
 //    only with S > 1) is held by its owner lane (rank mod 64) as a key plus
 //    its free-slot count. Ranks of the list beyond the smallest held key
 //    wait while that rank takes one chunk on its own.
+//  - Best fit: when the rest is below the headroom of the rank that would
+//    take it (always the least-loaded eligible one), it goes instead to the
+//    eligible rank with the smallest headroom that holds it, ties to the
+//    lowest id: a forward search of the list (from where the run stopped)
+//    and a reduction over held ranks. A list entry taken this way is marked
+//    gone (bit b of lane l: entry 64 b + l) and skipped when the run gets
+//    there.
 template <int RPL>
 __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
-                           int NS, int Q, int rbits, int &nrec_out,
-                           int &exhausted_out) {
+                           int NS, int Q, int rbits, bool best_fit,
+                           int &nrec_out, int &exhausted_out) {
     const int lane = threadIdx.x & 63;
     uint32_t hkey[RPL];
     int hfree[RPL];
@@ -152,6 +164,7 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
         hfree[i] = 0;
     }
     uint32_t my_min = 0xFFFFFFFFu;
+    uint32_t dgone = 0;
     int h_count = 0;
     // hold rank d (key k, f free slots) in its owner lane, or release it
     auto hold = [&](int d, uint32_t k, int f) {
@@ -169,81 +182,181 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
             my_min = b;
         }
     };
-    ListWindow cand, cmove;
-    cand.init(s.sorted, ncand);
-    cmove.init(s.smove, ncand);
+    auto held_free = [&](int d) {
+        const int dk = d >> 6;
+        int f = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) f = (i == dk) ? hfree[i] : f;
+        return __builtin_amdgcn_readlane(f, d & 63);
+    };
     const uint32_t rmask = (1u << rbits) - 1u;
     const int max_rec = R * S;
     int di = 0, nrec = 0, exhausted = 0;
+    // whether list entry idx (any idx, per lane) was taken out of order
+    auto is_gone = [&](int idx, bool in) {
+        const uint32_t w = static_cast<uint32_t>(
+            __shfl(static_cast<int>(dgone), idx & 63, 64));
+        return in && ((w >> ((idx >> 6) & 31)) & 1u) != 0;
+    };
+    auto record = [&](int e, int d, int fr, int m) {
+        if (lane == 0) {
+            s.rec_e[nrec] = e;
+            s.rec_p[nrec] = d * NS + N + (S - fr);
+            s.rec_m[nrec] = m;
+        }
+        ++nrec;
+    };
+    // Place `need` whole on the eligible rank with the smallest headroom
+    // >= need (the most loaded one with load <= Q - need; ties: lowest id),
+    // among list entries from `from` on and held ranks.
+    auto place_best_fit = [&](int e, int need, int from) {
+        const int thr = Q - need;
+        int bestL = -1, bestIdx = -1;
+        for (int x0 = from; x0 < nd; x0 += 64) {
+            const int idx = x0 + lane;
+            const bool in = idx < nd;
+            const uint32_t key = in ? static_cast<uint32_t>(s.dsorted[idx])
+                                    : 0xFFFFFFFFu;
+            const bool g = is_gone(idx, in);
+            const int L = static_cast<int>(key >> rbits);
+            const bool q = in && !g && L <= thr;
+            const uint64_t bq = __ballot(q);
+            if (bq) {
+                const int last = 63 - __builtin_clzll(bq);
+                const int Lw = __builtin_amdgcn_readlane(L, last);
+                const uint64_t eq = __ballot(q && L == Lw);
+                if (Lw > bestL) {
+                    bestL = Lw;
+                    bestIdx = x0 + __builtin_ctzll(eq);
+                }
+            }
+            if (__ballot(in && !g && L > thr)) break;   // sorted: no more
+        }
+        // held ranks: (load + 1) << rbits | (rmask - id), largest wins
+        uint32_t hb = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            if (hkey[i] == 0xFFFFFFFFu) continue;
+            const uint32_t L = hkey[i] >> rbits;
+            const uint32_t id = hkey[i] & rmask;
+            const uint32_t enc = ((L + 1u) << rbits) | (rmask - id);
+            if (static_cast<int>(L) <= thr && enc > hb) hb = enc;
+        }
+        const uint32_t hbest = h_count > 0 ? ~wave_min_u32(~hb) : 0u;
+        const int Lh = static_cast<int>(hbest >> rbits) - 1;
+        const int idh = static_cast<int>(rmask - (hbest & rmask));
+        const int idd = bestIdx >= 0
+            ? static_cast<int>(static_cast<uint32_t>(s.dsorted[bestIdx]) & rmask)
+            : 0;
+        const bool from_held = hbest != 0u &&
+            (bestIdx < 0 || Lh > bestL || (Lh == bestL && idh < idd));
+        if ((!from_held && bestIdx < 0) || nrec >= max_rec) {
+            exhausted = 1;           // cannot happen with a consistent state
+            return;
+        }
+        int d, Ld, fr;
+        if (from_held) {
+            d = idh;
+            Ld = Lh;
+            fr = held_free(d);
+            hold(d, 0xFFFFFFFFu, 0);
+            --h_count;
+        } else {
+            d = idd;
+            Ld = bestL;
+            fr = S;
+            if (lane == (bestIdx & 63)) dgone |= 1u << (bestIdx >> 6);
+        }
+        record(e, d, fr, need);
+        if (fr > 1 && Ld + need < Q) {
+            hold(d, (static_cast<uint32_t>(Ld + need) << rbits) |
+                        static_cast<uint32_t>(d), fr - 1);
+            ++h_count;
+        }
+    };
+    ListWindow cand, cmove;
+    cand.init(s.sorted, ncand);
+    cmove.init(s.smove, ncand);
     for (int c = 0; c < ncand && !exhausted; ++c) {
         const int e = cand.get(c);
         int rem = cmove.get(c);
-        while (rem > 0) {
+        while (rem > 0 && !exhausted) {
             const uint32_t kh = h_count > 0 ? wave_min_u32(my_min) : 0xFFFFFFFFu;
             // the next list ranks below the smallest held key, within the
-            // spare slots left
+            // spare slots left; entries taken out of order are skipped
             const int idx = di + lane;
-            const uint32_t key = (idx < nd && nrec + lane < max_rec)
-                ? static_cast<uint32_t>(s.dsorted[idx]) : 0xFFFFFFFFu;
-            const bool valid = key < kh;
+            const bool in = idx < nd;
+            const uint32_t key = in ? static_cast<uint32_t>(s.dsorted[idx])
+                                    : 0xFFFFFFFFu;
+            const bool g = is_gone(idx, in);
+            const bool ok = in && !g && key < kh;
+            const int cr = static_cast<int>(mask_rank(__ballot(ok)));
+            const bool valid = ok && nrec + cr < max_rec;
+            const uint64_t stops = __ballot(!valid && !g);
+            const int stop = stops ? __builtin_ctzll(stops) : 64;
+            const bool run = valid && lane < stop;
             const int Ld = static_cast<int>(key >> rbits);
-            const int h = valid ? Q - Ld : 0;
+            const int h = run ? Q - Ld : 0;
             const int pre = static_cast<int>(
                 wave_sat_inclusive_sum(static_cast<uint32_t>(h)));
-            const uint64_t hit = __ballot(valid && pre >= rem);
-            const int nv = hit ? __builtin_ctzll(hit) + 1
-                               : __builtin_popcountll(__ballot(valid));
+            const uint64_t hit = __ballot(run && pre >= rem);
+            const int hl = hit ? __builtin_ctzll(hit) : stop;
             // the sum before the hit lane is below rem, hence exact
-            const int before_hit =
-                (hit && nv >= 2) ? __builtin_amdgcn_readlane(pre, nv - 2) : 0;
-            if (lane < nv) {
-                // full headroom, except the rank where the amount runs out
-                const int m = (hit && lane == nv - 1) ? rem - before_hit : h;
+            const int before =
+                hl >= 1 ? __builtin_amdgcn_readlane(pre, hl - 1) : 0;
+            const int need = rem - before;
+            const bool bf = hit && best_fit &&
+                            need < __builtin_amdgcn_readlane(h, hl);
+            // lanes placed now: full headroom before the hit lane, the rest
+            // on the hit lane (unless best fit sends it elsewhere)
+            const bool put = run && (lane < hl || (hit && lane == hl && !bf));
+            const uint64_t puts = __ballot(put);
+            if (put) {
+                const int m = lane == hl ? need : h;
                 const int d = static_cast<int>(key & rmask);
-                s.rec_e[nrec + lane] = e;
-                s.rec_p[nrec + lane] = d * NS + N;      // its first spare
-                s.rec_m[nrec + lane] = m;
+                const int at = nrec + static_cast<int>(mask_rank(puts));
+                s.rec_e[at] = e;
+                s.rec_p[at] = d * NS + N;      // its first spare
+                s.rec_m[at] = m;
             }
-            if (nv > 0) {
-                if (hit) {
+            nrec += __builtin_popcountll(puts);
+            if (hit) {
+                di += hl + (bf ? 0 : 1);
+                if (bf) {
+                    place_best_fit(e, need, di);
+                } else {
                     const uint32_t lk = static_cast<uint32_t>(
-                        __builtin_amdgcn_readlane(static_cast<int>(key), nv - 1));
-                    const int m_last = rem - before_hit;
-                    const int Ld2 = static_cast<int>(lk >> rbits) + m_last;
+                        __builtin_amdgcn_readlane(static_cast<int>(key), hl));
+                    const int Ld2 = static_cast<int>(lk >> rbits) + need;
                     if (S > 1 && Ld2 < Q) {
                         const int d = static_cast<int>(lk & rmask);
                         hold(d, (static_cast<uint32_t>(Ld2) << rbits) |
                                     static_cast<uint32_t>(d), S - 1);
                         ++h_count;
                     }
-                    rem = 0;
-                } else {
-                    rem -= __builtin_amdgcn_readlane(pre, nv - 1);
                 }
-                di += nv;
-                nrec += nv;
+                rem = 0;
+                continue;
             }
-            if (rem == 0 || nv == 64) continue;
-            // the run stopped before the amount: the smallest held rank
-            // takes one chunk, or nothing is left
+            rem = need;                    // what the full chunks left
+            di += stop;
+            if (stop == 64) continue;
+            // the run stopped before the amount: the smallest held rank is
+            // now the least-loaded eligible one, or nothing is left
             if (kh == 0xFFFFFFFFu || nrec >= max_rec) {
                 exhausted = 1;
                 break;
             }
             const int d = static_cast<int>(kh & rmask);
             const int Lh = static_cast<int>(kh >> rbits);
-            const int dk = d >> 6;
-            int f = 0;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) f = (i == dk) ? hfree[i] : f;
-            const int fr = __builtin_amdgcn_readlane(f, d & 63);
-            const int m = rem < Q - Lh ? rem : Q - Lh;
-            if (lane == 0) {
-                s.rec_e[nrec] = e;
-                s.rec_p[nrec] = d * NS + N + (S - fr);
-                s.rec_m[nrec] = m;
+            if (best_fit && rem < Q - Lh) {
+                place_best_fit(e, rem, di);
+                rem = 0;
+                continue;
             }
-            ++nrec;
+            const int fr = held_free(d);
+            const int m = rem < Q - Lh ? rem : Q - Lh;
+            record(e, d, fr, m);
             rem -= m;
             const bool again = fr > 1 && Lh + m < Q;
             hold(d, again ? (static_cast<uint32_t>(Lh + m) << rbits) |
@@ -259,7 +372,7 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
 
 __global__ __launch_bounds__(kBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
-    int P, int rbits, uint32_t lds_bytes, ue_placement_layout lay,
+    int P, int rbits, int policy, uint32_t lds_bytes, ue_placement_layout lay,
     int32_t *__restrict__ placement) {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kWaves];
@@ -370,15 +483,16 @@ __global__ __launch_bounds__(kBlock) void k_plan(
 
     // ---- B. sequential spill loop on wave 0 ------------------------------
     if (tid < 64) {
+        const bool best_fit = policy == UE_PLAN_BEST_FIT;
         int nrec = 0, exhausted = 0;
         switch ((R + 63) / 64) {
-            case 1: spill_loop<1>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
-            case 2: spill_loop<2>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 1: spill_loop<1>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
+            case 2: spill_loop<2>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
             case 3:
-            case 4: spill_loop<4>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 4: spill_loop<4>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
             case 5: case 6: case 7:
-            case 8: spill_loop<8>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
-            default: spill_loop<16>(s, ncand, nd, R, S, N, NS, Q, rbits, nrec, exhausted); break;
+            case 8: spill_loop<8>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
+            default: spill_loop<16>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
         }
         if (tid == 0) {
             s_nrec = nrec;
@@ -482,6 +596,7 @@ hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        int32_t *placement, hipStream_t s) {
     hipLaunchKernelGGL(k_plan, dim3(L), dim3(kBlock), c.plan_lds, s, counts,
                        c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
+                       static_cast<int>(c.cfg.plan_policy),
                        static_cast<uint32_t>(c.plan_lds), c.lay, placement);
     return hipGetLastError();
 }

@@ -83,7 +83,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
               S = cfg->spare_per_rank, k = cfg->topk;
     if (E < 1 || E > ue::kMaxExperts || R < 1 || E % R != 0 || S < 0 ||
         S > ue::kMaxSpare || k < 1 || k > E || cfg->max_tokens < 0 ||
-        cfg->max_layers < 1)
+        cfg->max_layers < 1 ||
+        (cfg->plan_policy != UE_PLAN_LEAST_LOADED &&
+         cfg->plan_policy != UE_PLAN_BEST_FIT))
         return UE_EUNSUPPORTED;
     const int N = E / R, NS = N + S;
     const int64_t P = static_cast<int64_t>(R) * NS;

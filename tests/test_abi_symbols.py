@@ -43,3 +43,13 @@ def test_status_names():
     lib = ue.library()
     for code, name in ue.STATUS.items():
         assert lib.ue_status_name(code).decode() == name
+
+
+def test_config_struct_matches_header():
+    """The ctypes mirror of ue_config has the header's fields in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct ue_config \{(.*?)\} ue_config;", text,
+                     flags=re.S).group(1)
+    fields = re.findall(r"int32_t\s+(\w+);", body)
+    assert [f for f, _ in ue.ue_config._fields_] == fields
+    assert ctypes.sizeof(ue.ue_config) == 4 * len(fields)

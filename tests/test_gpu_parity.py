@@ -14,8 +14,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def make_ctx(E, R, S, k, T, L=1):
-    return ue.Context(E, R, S, k, max(T, 1), L, device=DEV)
+def make_ctx(E, R, S, k, T, L=1, policy=ue.PLAN_LEAST_LOADED):
+    return ue.Context(E, R, S, k, max(T, 1), L, device=DEV,
+                      plan_policy=policy)
 
 
 @pytest.mark.parametrize("case", [g for g in pins.golden_cases()
@@ -23,7 +24,8 @@ def make_ctx(E, R, S, k, T, L=1):
 def test_golden_cases(case):
     say("golden", case["name"])
     routing = np.asarray(case["routing"], np.int32)[None]
-    ctx = make_ctx(case["E"], case["R"], case["S"], case["k"], case["T"])
+    ctx = make_ctx(case["E"], case["R"], case["S"], case["k"], case["T"],
+                   policy=case.get("policy", 0))
     res = gpu_rebalance(ctx, torch.from_numpy(routing))
     for key in ("phys", "perm", "inv_perm", "rank_counts"):
         assert res[key].reshape(-1).tolist() == case[key], key
@@ -33,7 +35,8 @@ def test_golden_cases(case):
 def test_golden_planner_only():
     for case in pins.golden_cases():
         say("golden plan", case["name"])
-        ctx = make_ctx(case["E"], case["R"], case["S"], 1, 1)
+        ctx = make_ctx(case["E"], case["R"], case["S"], 1, 1,
+                       policy=case.get("policy", 0))
         counts = torch.tensor(case["counts"], dtype=torch.int32,
                               device=DEV)[None]
         f = ctx.placement_fields(ue.ue_plan(ctx, counts))
@@ -47,10 +50,11 @@ def test_golden_planner_only():
         assert f["rep_cap"][0, :n].tolist() == case["rep_cap"]
 
 
-def test_random_instances():
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+def test_random_instances(policy):
     """Seeded random shapes: tiny to several tiles with ragged tails, skew
     from uniform to extreme, S = 0..3, one to four layers."""
-    rng = np.random.default_rng(99)
+    rng = np.random.default_rng(99 + policy)
     for it in range(60):
         R = int(rng.integers(1, 17))
         N = int(rng.integers(1, 9))
@@ -64,18 +68,20 @@ def test_random_instances():
         skew = float(rng.uniform(0, 3))
         routing = np.stack([pins.random_routing(rng, T, E, k, skew)
                             for _ in range(L)])
-        say(f"random {it}: E={E} R={R} S={S} k={k} T={T} L={L}")
-        ctx = make_ctx(E, R, S, k, T, L)
+        say(f"random {it}: E={E} R={R} S={S} k={k} T={T} L={L} "
+            f"policy={policy}")
+        ctx = make_ctx(E, R, S, k, T, L, policy)
         res = gpu_rebalance(ctx, torch.from_numpy(routing))
         compare_with_oracle(res, routing, E, R, S)
 
 
-def test_many_spares_and_ranks():
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+def test_many_spares_and_ranks(policy):
     """Several spare slots per rank (destinations that take more than one
     chunk and stay eligible), ranks beyond one wave's lanes (R > 64), and
     skew strong enough to exhaust the slots: the planner's held-rank path
     against the oracle."""
-    rng = np.random.default_rng(1234)
+    rng = np.random.default_rng(1234 + policy)
     shapes = [(128, 128, 3), (256, 128, 2), (96, 32, 8), (64, 16, 16),
               (512, 256, 4), (200, 100, 5), (1024, 1024, 1), (1024, 64, 12)]
     for it, (E, R, S) in enumerate(shapes):
@@ -87,23 +93,24 @@ def test_many_spares_and_ranks():
         routing = np.stack([pins.random_routing(rng, T, E, k,
                                                 float(rng.uniform(0.8, 2.5)))
                             for _ in range(L)])
-        say(f"spares {it}: E={E} R={R} S={S} k={k} T={T}")
-        ctx = make_ctx(E, R, S, k, T, L)
+        say(f"spares {it}: E={E} R={R} S={S} k={k} T={T} policy={policy}")
+        ctx = make_ctx(E, R, S, k, T, L, policy)
         for fused in (False, True):
             res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
             compare_with_oracle(res, routing, E, R, S)
 
 
+@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
-def test_configs_full_size(name, fused):
+def test_configs_full_size(name, fused, policy):
     """Every routing workload at its full size, every layer, bit-exact, as
-    three calls and as one ue_rebalance call."""
+    three calls and as one ue_rebalance call, under both planner rules."""
     cfg = W.CONFIGS[name]
-    say("full size", name, "fused" if fused else "calls")
+    say("full size", name, "fused" if fused else "calls", "policy", policy)
     routing = W.make_routing(cfg, device=DEV)
     ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
-                   cfg.layers)
+                   cfg.layers, policy)
     res = gpu_rebalance(ctx, routing, fused=fused)
     compare_with_oracle(res, routing.cpu().numpy(), cfg.experts, cfg.ranks,
                         cfg.spare)
@@ -258,3 +265,5 @@ def test_refusals_leave_outputs_untouched():
     for bad in ((63, 8, 1, 8), (2048, 8, 1, 8), (64, 8, 100, 8), (64, 8, 1, 65)):
         with pytest.raises(ue.UEError):
             ue.Context(*bad, 100, 1, device=DEV)
+    with pytest.raises(ue.UEError):
+        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=2)
