@@ -133,6 +133,96 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     return cfg, rb, ms, phases, ms_one
 
 
+def stale_rank_loads(slot_expert, slot_cap, counts_new, N, NS, R):
+    """Rank loads when plans made from other counts are applied to
+    ``counts_new`` [L, E]: each expert's new count is split over the slots
+    the old plan gave it in proportion to their old capacities (an expert
+    the old plan saw no tokens of stays whole on its native slot). Slot
+    tables are [L, P] (slot_expert -1: unused). Returns float64 [L, R]."""
+    import torch
+    L, P = slot_expert.shape
+    E = counts_new.shape[1]
+    dev = counts_new.device
+    se = slot_expert.long()
+    used = se >= 0
+    e_of = torch.where(used, se, torch.zeros_like(se))
+    cap = torch.where(used, slot_cap.double(), torch.zeros_like(se,
+                                                               dtype=torch.float64))
+    tot = torch.zeros((L, E), dtype=torch.float64, device=dev)
+    tot.scatter_add_(1, e_of, cap)
+    t = torch.gather(tot, 1, e_of)
+    native = (torch.arange(P, device=dev) % NS < N)[None, :].expand(L, P)
+    share = torch.where(t > 0, cap / t.clamp(min=1.0),
+                        native.to(torch.float64))
+    share = torch.where(used, share, torch.zeros_like(share))
+    load = torch.gather(counts_new.double(), 1, e_of) * share
+    rank = (torch.arange(P, device=dev) // NS)[None, :].expand(L, P)
+    out = torch.zeros((L, R), dtype=torch.float64, device=dev)
+    out.scatter_add_(1, rank, load)
+    return out
+
+
+def _spread(x):
+    import numpy as np
+    x = np.asarray(x, dtype=np.float64)
+    return [round(float(np.min(x)), 4), round(float(np.median(x)), 4),
+            round(float(np.max(x)), 4)]
+
+
+def bench_stale(ue, W, dev):
+    """Max/mean rank load when each plan comes from earlier loads instead of
+    the exact current ones: the previous microbatch's plan and the plan of
+    the summed earlier microbatches under the pipeline workload's drift,
+    and the previous step's plan of the same dsv3 layer (same distribution,
+    fresh tokens). Plans are made by the library; only the split of the
+    new counts over the old plan's slots is evaluated here."""
+    import torch
+    out = {}
+    cfg = W.CONFIGS["pipeline"]
+    routing = W.make_routing(cfg, device=dev)
+    rb = Rebalance(ue, cfg, routing, dev)
+    rb.step()
+    ctx = rb.ctx
+    counts = rb.out["counts"]
+    f = ctx.placement_fields(rb.placement)
+    mean = counts.sum(1).double() / cfg.ranks
+    cum = torch.cumsum(counts, 0, dtype=torch.int32)[:-1].contiguous()
+    hist = ctx.placement_fields(ue.ue_plan(ctx, cum))
+    N, NS = ctx.N, ctx.N + ctx.S
+    prev = stale_rank_loads(f["slot_expert"][:-1], f["slot_cap"][:-1],
+                            counts[1:], N, NS, cfg.ranks)
+    summed = stale_rank_loads(hist["slot_expert"], hist["slot_cap"],
+                              counts[1:], N, NS, cfg.ranks)
+    m1 = mean[1:]
+    out["pipeline_drift"] = {
+        "microbatches": "1..15 (each planned from earlier ones)",
+        "no_rebalance": _spread((f["load_before"][1:].max(1).values / m1).cpu()),
+        "exact_load": _spread((f["load_after"][1:].max(1).values / m1).cpu()),
+        "previous_microbatch_plan": _spread((prev.max(1).values / m1).cpu()),
+        "summed_history_plan": _spread((summed.max(1).values / m1).cpu()),
+    }
+    del rb, routing
+    cfg = W.CONFIGS["dsv3"]
+    r0 = W.make_routing(cfg, device=dev)
+    r1 = W.make_routing(cfg, device=dev, step=1)
+    ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
+                     cfg.layers, device=dev)
+    old = ctx.placement_fields(ue.ue_plan(ctx, ue.ue_load(ctx, r0)))
+    c1 = ue.ue_load(ctx, r1)
+    now = ctx.placement_fields(ue.ue_plan(ctx, c1))
+    mean = c1.sum(1).double() / cfg.ranks
+    st = stale_rank_loads(old["slot_expert"], old["slot_cap"], c1, ctx.N,
+                          ctx.N + ctx.S, cfg.ranks)
+    out["dsv3_next_step"] = {
+        "layers": "58 (plan of the same layer one step earlier)",
+        "no_rebalance": _spread((now["load_before"].max(1).values / mean).cpu()),
+        "exact_load": _spread((now["load_after"].max(1).values / mean).cpu()),
+        "previous_step_plan": _spread((st.max(1).values / mean).cpu()),
+    }
+    torch.cuda.synchronize()
+    return out
+
+
 def bench_best_fit(ue, cfg, routing, dev, steps, warmup):
     """The same rebalance under the best-fit planner rule: time and the
     balance it reaches."""
@@ -295,7 +385,7 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", choices=["rebalance", "large_ep", "stream",
+    ap.add_argument("--only", choices=["rebalance", "large_ep", "stale", "stream",
                                        "gather"], default=None,
                     help="run one measurement (for profiling); prints its "
                          "JSON object instead of the contract line")
@@ -326,6 +416,8 @@ def main():
             res = bench_large_ep(ue, W, dev)
         elif args.only == "stream":
             res = bench_stream(ue, W, dev)
+        elif args.only == "stale":
+            res = bench_stale(ue, W, dev)
         elif args.only == "gather":
             res = bench_gather(ue, W, dev)
         if args.calib_copy:
@@ -398,6 +490,8 @@ def main():
         line["stream"] = bench_stream(ue, W, dev)
         log("gather")
         line["gather"] = bench_gather(ue, W, dev)
+        log("stale plans")
+        line["stale_plan"] = bench_stale(ue, W, dev)
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(routing_host, cfg,

@@ -171,11 +171,13 @@ def layer_setup(cfg: RoutingConfig | str, layer: int, device="cpu"):
 
 def make_routing(cfg: RoutingConfig | str, device="cpu",
                  layers: int | None = None,
-                 tokens: int | None = None) -> torch.Tensor:
+                 tokens: int | None = None, step: int = 0) -> torch.Tensor:
     """Routing tensor int32 ``[L, T, k]`` for a named configuration.
 
     ``layers``/``tokens`` may shrink the workload (same recipe, fewer layers
-    or tokens) for fast tests."""
+    or tokens) for fast tests. ``step`` > 0 gives the same layers at a later
+    training step: the same exponent, expert order and hot set per layer
+    (the same distribution), with fresh token draws."""
     if isinstance(cfg, str):
         cfg = CONFIGS[cfg]
     L = cfg.layers if layers is None else int(layers)
@@ -188,6 +190,8 @@ def make_routing(cfg: RoutingConfig | str, device="cpu",
             pass                    # one stream continues across layers
         else:
             g, s, order, hot = layer_setup(cfg, layer, device)
+            if step:
+                g = _gen(device, seed_of(p["seed"], (int(step) << 20) + layer))
         if cfg.kind == "hot":
             out[layer] = hot_layer(T, k, s, hot, order, p["p_hot"], g)
         else:

@@ -73,6 +73,26 @@ def test_dsv3_layers_nonstationary():
     assert len(set(tops)) > 1, "independent permutations per layer"
 
 
+def test_later_step_same_distribution():
+    """A later step redraws the tokens of each layer from the same
+    distribution: different routing, the same expert order (the hottest
+    experts agree), a close count profile."""
+    for name in ("dsv3", "large_ep", "tiny"):
+        cfg = W.CONFIGS[name]
+        a = W.make_routing(cfg, layers=2, tokens=8192)
+        b = W.make_routing(cfg, layers=2, tokens=8192, step=1)
+        _valid(b, cfg.experts, cfg.topk)
+        assert not torch.equal(a, b), name
+        assert torch.equal(b, W.make_routing(cfg, layers=2, tokens=8192,
+                                             step=1)), name
+        for layer in range(2):
+            ca = np.bincount(a[layer].numpy().ravel(), minlength=cfg.experts)
+            cb = np.bincount(b[layer].numpy().ravel(), minlength=cfg.experts)
+            assert np.argmax(ca) == np.argmax(cb), name
+            tv = 0.5 * np.abs(ca / ca.sum() - cb / cb.sum()).sum()
+            assert tv < 0.05, (name, tv)
+
+
 def test_pipeline_drift():
     cfg = W.CONFIGS["pipeline"]
     s = W.layer_exponents(cfg)
