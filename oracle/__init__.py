@@ -62,7 +62,8 @@ def load_library(path: str):
     lib.orc_load.argtypes = [i32p, ctypes.c_int64, ctypes.c_int32, i32p]
     lib.orc_plan.restype = ctypes.c_int
     lib.orc_plan.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32,
-                             ctypes.c_int32, ctypes.c_int32] + [i32p] * 9
+                             ctypes.c_int32, ctypes.c_int32,
+                             ctypes.c_int32] + [i32p] * 9
     lib.orc_reroute.restype = ctypes.c_int64
     lib.orc_reroute.argtypes = [i32p, ctypes.c_int64, ctypes.c_int32,
                                 ctypes.c_int32, ctypes.c_int32] + [i32p] * 8
@@ -113,10 +114,11 @@ def load(routing: np.ndarray, n_experts: int):
 
 
 def plan(counts: np.ndarray, n_ranks: int, n_spare: int,
-         policy: int = 0) -> dict:
+         policy: int = 0, quota_mode: int = 0) -> dict:
     """Quota plan for one layer from its ``counts`` (int32 ``[E]``).
     ``policy`` 0: least-loaded destination; 1: best fit for a chunk the
-    least-loaded rank would not fill."""
+    least-loaded rank would not fill. ``quota_mode`` 0: Q = ceil(total /
+    R); 1: the lowest of 64 raised quotas at which nothing is left."""
     c = np.ascontiguousarray(counts, dtype=np.int32).reshape(-1)
     E, R, S = c.size, int(n_ranks), int(n_spare)
     if E % R != 0:
@@ -133,7 +135,8 @@ def plan(counts: np.ndarray, n_ranks: int, n_spare: int,
         load_before=np.zeros(R, np.int32),
         load_after=np.zeros(R, np.int32),
     )
-    rc = _get().orc_plan(c, E, R, S, int(policy), out["scalars"],
+    rc = _get().orc_plan(c, E, R, S, int(policy), int(quota_mode),
+                         out["scalars"],
                          out["rep_off"],
                          out["rep_slot"], out["rep_cap"], out["slot_expert"],
                          out["slot_cap"], out["slot_off"], out["load_before"],
@@ -142,7 +145,8 @@ def plan(counts: np.ndarray, n_ranks: int, n_spare: int,
         raise ValueError("oracle plan refused the shape")
     q, exhausted, residual, n_rep = (int(v) for v in out["scalars"])
     out.update(quota=q, exhausted=exhausted, residual=residual, n_rep=n_rep,
-               E=E, R=R, S=S, N=E // R, P=P, policy=int(policy))
+               E=E, R=R, S=S, N=E // R, P=P, policy=int(policy),
+               quota_mode=int(quota_mode))
     return out
 
 
@@ -163,7 +167,7 @@ def reroute(routing: np.ndarray, pl: dict, perm_fill: int = -1) -> dict:
 
 
 def rebalance(routing: np.ndarray, n_experts: int, n_ranks: int,
-              n_spare: int, policy: int = 0) -> list:
+              n_spare: int, policy: int = 0, quota_mode: int = 0) -> list:
     """load -> plan -> reroute for every layer of ``routing [L, T, k]``."""
     r = np.ascontiguousarray(routing, dtype=np.int32)
     if r.ndim <= 2:
@@ -173,7 +177,7 @@ def rebalance(routing: np.ndarray, n_experts: int, n_ranks: int,
     r = r.reshape(r.shape[0], -1)
     res = []
     for layer in range(r.shape[0]):
-        pl = plan(counts[layer], n_ranks, n_spare, policy)
+        pl = plan(counts[layer], n_ranks, n_spare, policy, quota_mode)
         rr = reroute(r[layer], pl)
         pl.update(rr)
         pl["counts"] = counts[layer]

@@ -35,6 +35,9 @@
  *    the replica whose capacity prefix covers j (master first, then replicas
  *    in creation order);
  *    the dispatch permutation is the stable counting sort by physical slot.
+ *  Two variants, each one step different (see Step 2): best fit for a
+ *  remainder the least-loaded rank would not fill, and a quota search that
+ *  raises Q in small steps until the plan is no longer exhausted.
  *
  * Everything is integer; there is nothing to round.
  */
@@ -71,7 +74,17 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  * room to spare, the chunk goes to the eligible rank with the smallest
  * headroom that still takes all of it, ties to the lowest id.
  *
- * scalars[0] = quota Q
+ * quota_mode 0: Q = ceil(sum(counts) / R). quota_mode 1 (quota search):
+ * with one spare slot a rank takes one chunk, so a chunk that leaves a
+ * destination part full wastes the rest of its headroom, while the ranks
+ * below Q0 = ceil(sum / R) hold, together, only the sources' excess plus
+ * less than R of slack; the plan at Q0 then almost always stops with
+ * excess left. The search raises the quota in steps of ceil(Q0 / 256) and
+ * keeps the lowest of Q0, Q0 + step, ..., Q0 + 63 step at which nothing is
+ * left (the scheduler is quota-driven; the pages do not say how the quota
+ * is set). With none, Q0 stands.
+ *
+ * scalars[0] = quota Q (the one used)
  * scalars[1] = exhausted (1 if an overloaded rank still had excess but no
  *              rank was left with a free spare slot and load < Q)
  * scalars[2] = residual = sum over ranks of max(0, load_after - Q)
@@ -87,43 +100,23 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  * slot_off the exclusive prefix sum of slot_cap (P+1 entries).
  *
  * Returns 0, or -1 if the shape is not one the slot model covers. */
-int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
-             int32_t policy, int32_t *scalars, int32_t *rep_off,
-             int32_t *rep_slot, int32_t *rep_cap, int32_t *slot_expert,
-             int32_t *slot_cap, int32_t *slot_off, int32_t *load_before,
-             int32_t *load_after)
+/* One greedy pass at quota Q: native loads, candidates, spill loop. Fills
+ * load, rem, nfree and the spill records; returns 1 if the plan stopped
+ * with excess left (exhausted), else 0. */
+static int greedy_at(const int32_t *counts, int32_t E, int32_t R, int32_t S,
+                     int32_t policy, int64_t Q, int64_t *load, int64_t *rem,
+                     int32_t *nfree, int32_t *cand, int32_t *rec_e,
+                     int32_t *rec_p, int64_t *rec_m, int32_t *nrec_out)
 {
-    if (E <= 0 || R <= 0 || S < 0 || E % R != 0)
-        return -1;
-    const int32_t N = E / R;       /* native experts per rank */
-    const int32_t NS = N + S;      /* physical slots per rank */
-    const int32_t P = R * NS;      /* physical slots in total */
-
-    int64_t *load = calloc((size_t)R, sizeof(int64_t));
-    int64_t *rem = calloc((size_t)E, sizeof(int64_t));
-    int32_t *nfree = calloc((size_t)R, sizeof(int32_t));
-    int32_t *cand = calloc((size_t)E, sizeof(int32_t));
-    /* spill records in creation order: expert, slot, amount */
-    int32_t *rec_e = calloc((size_t)(R * S + 1), sizeof(int32_t));
-    int32_t *rec_p = calloc((size_t)(R * S + 1), sizeof(int32_t));
-    int64_t *rec_m = calloc((size_t)(R * S + 1), sizeof(int64_t));
-    if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m) {
-        free(load); free(rem); free(nfree); free(cand);
-        free(rec_e); free(rec_p); free(rec_m);
-        return -1;
+    const int32_t N = E / R;
+    const int32_t NS = N + S;
+    for (int32_t r = 0; r < R; ++r) {
+        load[r] = 0;
+        nfree[r] = S;
     }
-
-    /* Quota and rank loads under the native placement. */
-    int64_t total = 0;
     for (int32_t e = 0; e < E; ++e) {
-        total += counts[e];
         load[e / N] += counts[e];
         rem[e] = counts[e];
-    }
-    const int64_t Q = (total + R - 1) / R;
-    for (int32_t r = 0; r < R; ++r) {
-        load_before[r] = (int32_t)load[r];
-        nfree[r] = S;
     }
 
     /* Candidates: experts of overloaded ranks, heaviest first (count desc,
@@ -195,6 +188,67 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
             nfree[d] -= 1;
         }
     }
+    *nrec_out = nrec;
+    return exhausted;
+}
+
+int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
+             int32_t policy, int32_t quota_mode, int32_t *scalars,
+             int32_t *rep_off, int32_t *rep_slot, int32_t *rep_cap,
+             int32_t *slot_expert, int32_t *slot_cap, int32_t *slot_off,
+             int32_t *load_before, int32_t *load_after)
+{
+    if (E <= 0 || R <= 0 || S < 0 || E % R != 0)
+        return -1;
+    const int32_t N = E / R;       /* native experts per rank */
+    const int32_t NS = N + S;      /* physical slots per rank */
+    const int32_t P = R * NS;      /* physical slots in total */
+
+    int64_t *load = calloc((size_t)R, sizeof(int64_t));
+    int64_t *rem = calloc((size_t)E, sizeof(int64_t));
+    int32_t *nfree = calloc((size_t)R, sizeof(int32_t));
+    int32_t *cand = calloc((size_t)E, sizeof(int32_t));
+    /* spill records in creation order: expert, slot, amount */
+    int32_t *rec_e = calloc((size_t)(R * S + 1), sizeof(int32_t));
+    int32_t *rec_p = calloc((size_t)(R * S + 1), sizeof(int32_t));
+    int64_t *rec_m = calloc((size_t)(R * S + 1), sizeof(int64_t));
+    if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m) {
+        free(load); free(rem); free(nfree); free(cand);
+        free(rec_e); free(rec_p); free(rec_m);
+        return -1;
+    }
+
+    /* Plain quota and the native rank loads. */
+    int64_t total = 0;
+    for (int32_t e = 0; e < E; ++e)
+        total += counts[e];
+    const int64_t Q0 = (total + R - 1) / R;
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t l = 0;
+        for (int32_t i = 0; i < N; ++i)
+            l += counts[r * N + i];
+        load_before[r] = (int32_t)l;
+    }
+
+    /* Quota search (quota_mode 1): the quotas Q0 + j * ceil(Q0 / 256),
+     * j = 0 .. 63, are tried in increasing order, and the first at which
+     * the greedy pass places every excess is kept; if none does, the plain
+     * quota Q0 stands. */
+    int64_t Q = Q0;
+    int32_t nrec = 0;
+    if (quota_mode == 1) {
+        const int64_t step = (Q0 + 255) / 256;
+        for (int32_t j = 0; j < 64; ++j) {
+            const int64_t M = Q0 + j * step;
+            if (!greedy_at(counts, E, R, S, policy, M, load, rem, nfree, cand,
+                           rec_e, rec_p, rec_m, &nrec)) {
+                Q = M;
+                break;
+            }
+        }
+    }
+    const int exhausted = greedy_at(counts, E, R, S, policy, Q, load, rem,
+                                    nfree, cand, rec_e, rec_p, rec_m, &nrec);
 
     /* Replica table: master first (keeps what was not spilled), then the
      * spilled replicas in creation order. */

@@ -50,7 +50,7 @@ def _eq(name, got, want):
 
 def check_golden(g):
     pl = oracle.plan(np.asarray(g["counts"], np.int32), g["R"], g["S"],
-                     g.get("policy", 0))
+                     g.get("policy", 0), g.get("quota_mode", 0))
     for key in ("quota", "exhausted", "residual", "n_rep"):
         assert pl[key] == g[key], f"{g['name']}: {key} {pl[key]} != {g[key]}"
     for key in ("load_before", "load_after", "rep_off", "slot_expert",
@@ -108,16 +108,70 @@ def check_load(routing, E):
     return counts[0]
 
 
-def check_plan(counts, R, S, A=None, policy=0):
+def exhausts_at(counts, R, S, policy, Q):
+    """Runs the planning rule at quota Q from scratch and says whether it
+    stops with excess left: candidates by count desc, id asc; each chunk to
+    the least-loaded rank with a free spare and load below Q (lowest id on
+    ties), or under policy 1 to the eligible rank with the smallest headroom
+    that holds a remainder the least-loaded rank would not fill."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    N = E // R
+    L = counts.reshape(R, N).sum(axis=1).astype(np.int64)
+    free = np.full(R, S)
+    for e in sorted((e for e in range(E) if L[e // N] > Q),
+                    key=lambda e: (-counts[e], e)):
+        r, rem = e // N, int(counts[e])
+        while L[r] > Q and rem > 0:
+            elig = [x for x in range(R) if free[x] > 0 and L[x] < Q]
+            if not elig:
+                return True
+            need = min(int(L[r] - Q), rem)
+            d = min(elig, key=lambda x: (L[x], x))
+            if policy == 1 and need < Q - L[d]:
+                d = min((x for x in elig if Q - L[x] >= need),
+                        key=lambda x: (Q - L[x], x))
+            m = min(need, int(Q - L[d]))
+            L[r] -= m
+            L[d] += m
+            free[d] -= 1
+            rem -= m
+    return False
+
+
+def check_quota(counts, R, S, policy, quota_mode, pl):
+    """Quota 0: ceil(total / R). Quota search: one of Q0 + j ceil(Q0/256),
+    j < 64; every lower one exhausts when the rule is run on its own; the
+    kept one does not, unless none of the 64 works, and then Q0 stands."""
+    total = int(np.asarray(counts, np.int64).sum())
+    Q0 = -(-total // R)
+    Q = pl["quota"]
+    if quota_mode == 0:
+        assert Q == Q0, "quota is ceil(total / ranks)"
+        return
+    step = -(-Q0 // 256)
+    grid = [Q0 + j * step for j in range(64)]
+    assert Q in grid, "the quota is one of the searched steps"
+    for M in grid[:grid.index(Q)]:
+        assert exhausts_at(counts, R, S, policy, M), \
+            f"quota {M} below the kept {Q} would place everything"
+    if pl["exhausted"]:
+        assert Q == Q0, "with no step that places everything, Q0 stands"
+        assert all(exhausts_at(counts, R, S, policy, M) for M in grid)
+    else:
+        assert not exhausts_at(counts, R, S, policy, Q)
+
+
+def check_plan(counts, R, S, A=None, policy=0, quota_mode=0):
     counts = np.asarray(counts, np.int64)
     E = counts.size
     N, NS = E // R, E // R + S
     P = R * NS
-    pl = oracle.plan(counts.astype(np.int32), R, S, policy)
+    pl = oracle.plan(counts.astype(np.int32), R, S, policy, quota_mode)
     Q = pl["quota"]
     total = int(counts.sum())
     A = total if A is None else A
-    assert Q == -(-total // R), "quota is ceil(total / ranks)"
+    check_quota(counts, R, S, policy, quota_mode, pl)
     assert pl["P"] == P and pl["N"] == N
 
     rep_off, rep_slot, rep_cap = pl["rep_off"], pl["rep_slot"], pl["rep_cap"]
@@ -281,9 +335,9 @@ def check_reroute(routing, pl):
     return rr
 
 
-def check_instance(routing, E, R, S, policy=0):
+def check_instance(routing, E, R, S, policy=0, quota_mode=0):
     counts = check_load(routing, E)
-    pl = check_plan(counts, R, S, policy=policy)
+    pl = check_plan(counts, R, S, policy=policy, quota_mode=quota_mode)
     check_reroute(routing, pl)
     return pl
 
@@ -419,16 +473,20 @@ def optimum_max_load(counts, R, S):
     return best
 
 
-def check_against_optimum(counts, R, S, policy=0):
+def check_against_optimum(counts, R, S, policy=0, quota_mode=0):
     """Returns greedy / optimum. The greedy plan is one of the placements
     enumerated, so the optimum can never exceed it; every placement has a
-    rank at or above ceil(total / R) = Q, so when slots suffice the greedy
-    (which then ends with every rank <= Q) is optimal."""
-    pl = check_plan(counts, R, S, policy=policy)
+    rank at or above ceil(total / R) = Q0, so when slots suffice at Q0 the
+    greedy (which then ends with every rank <= Q0) is optimal; a raised
+    quota that places everything bounds the greedy's maximum."""
+    pl = check_plan(counts, R, S, policy=policy, quota_mode=quota_mode)
     greedy = int(pl["load_after"].max(initial=0))
     opt = optimum_max_load(list(counts), R, S)
+    Q0 = -(-int(np.sum(counts)) // R)
     assert opt <= greedy, "greedy beats the exhaustive optimum"
-    assert opt >= pl["quota"], "no placement beats the quota"
+    assert opt >= Q0, "no placement beats the quota"
     if not pl["exhausted"]:
-        assert greedy == opt == pl["quota"]
+        assert greedy <= pl["quota"]
+        if pl["quota"] == Q0:
+            assert greedy == opt == Q0
     return greedy / opt if opt else 1.0

@@ -60,6 +60,14 @@ MUTANTS = {
                                          "load[x] < load[b])"),
     "best fit ties highest id": ("load[x] > load[b])", "load[x] >= load[b])"),
     "best fit ignores the fit": ("Q - load[x] >= m &&", ""),
+    "search keeps the last quota that works": ("Q = M;\n                break;",
+                                               "Q = M;"),
+    "search step rounds down": ("(Q0 + 255) / 256", "Q0 / 256"),
+    "search skips the plain quota": ("for (int32_t j = 0; j < 64; ++j)",
+                                     "for (int32_t j = 1; j < 64; ++j)"),
+    "plan made at the plain quota": (
+        "const int exhausted = greedy_at(counts, E, R, S, policy, Q, load,",
+        "const int exhausted = greedy_at(counts, E, R, S, policy, Q0, load,"),
     "replica before master": ("rep_slot[n] = (e / N) * NS + (e % N);\n"
                               "        rep_cap[n] = (int32_t)rem[e];\n"
                               "        ++n;\n",
@@ -75,6 +83,11 @@ def run_all_pins():
         pins.check_instance(*pins.random_instance(rng))
     for _ in range(300):
         pins.check_instance(*pins.random_instance(rng), policy=1)
+    for _ in range(150):
+        pins.check_instance(*pins.random_instance(rng), quota_mode=1)
+    for _ in range(150):
+        pins.check_instance(*pins.random_instance(rng), policy=1,
+                            quota_mode=1)
     pins.check_no_spares(np.random.default_rng(1))
     pins.check_one_rank(np.random.default_rng(2))
     pins.check_balanced()

@@ -11,21 +11,44 @@ def test_golden(case):
     pins.check_golden(case)
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
-def test_invariants_random(policy):
-    rng = np.random.default_rng(20260602)
-    for _ in range(1500):
-        pins.check_instance(*pins.random_instance(rng), policy=policy)
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1)]
+RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
+            "best_fit_search"]
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
-def test_invariants_larger(policy):
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_invariants_random(policy, quota_mode):
+    rng = np.random.default_rng(20260602 + quota_mode)
+    for _ in range(1500 if quota_mode == 0 else 600):
+        pins.check_instance(*pins.random_instance(rng), policy=policy,
+                            quota_mode=quota_mode)
+
+
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_invariants_larger(policy, quota_mode):
     rng = np.random.default_rng(7)
     for _ in range(40):
         routing, E, R, S = pins.random_instance(
             rng, max_ranks=32, max_native=8, max_spare=3, max_tokens=2000,
             max_k=8)
-        pins.check_instance(routing, E, R, S, policy=policy)
+        pins.check_instance(routing, E, R, S, policy=policy,
+                            quota_mode=quota_mode)
+
+
+def test_quota_search_large_quota():
+    """Quotas in the thousands (steps of ceil(Q0/256) > 1): the kept quota
+    is on the grid and every lower step exhausts, for both rules."""
+    rng = np.random.default_rng(8)
+    for it in range(12):
+        R = int(rng.choice([4, 8, 16]))
+        N = int(rng.integers(1, 5))
+        E = R * N
+        k = int(min(E, 4))
+        routing = pins.random_routing(rng, 6000, E, k, float(rng.uniform(0.8, 2)))
+        for policy in (0, 1):
+            pl = pins.check_instance(routing, E, R, 1, policy=policy,
+                                     quota_mode=1)
+            assert pl["quota"] >= 256     # the step is above one token here
 
 
 def test_no_spares():
@@ -48,8 +71,8 @@ def test_invalid_ids():
     pins.check_invalid_ids()
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
-def test_brute_force_optimum(policy):
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_brute_force_optimum(policy, quota_mode):
     """Exhaustive optimum on tiny instances: greedy == optimum == Q whenever
     slots suffice; otherwise the optimum never exceeds greedy. The worst
     observed greedy/optimum ratio is reported."""
@@ -63,9 +86,9 @@ def test_brute_force_optimum(policy):
         E = R * N
         counts = rng.integers(0, 9, size=E).astype(np.int32)
         counts[rng.integers(0, E)] += int(rng.integers(0, 12))
-        ratio = pins.check_against_optimum(counts, R, S, policy)
+        ratio = pins.check_against_optimum(counts, R, S, policy, quota_mode)
         worst = max(worst, ratio)
         n_exhausted += ratio > 1.0
-    print(f"policy {policy}: greedy/optimum worst {worst:.3f}; above optimum in "
+    print(f"policy {policy} quota {quota_mode}: greedy/optimum worst {worst:.3f}; above optimum in "
           f"{n_exhausted}/60")
     assert worst <= 2.0
