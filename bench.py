@@ -48,12 +48,13 @@ class Rebalance:
     """Preallocated buffers and the one ABI call of a rebalance
     (ue_rebalance: load -> plan -> reroute on the stream)."""
 
-    def __init__(self, ue, cfg, routing, dev, policy=0):
+    def __init__(self, ue, cfg, routing, dev, policy=0, quota_mode=0):
         import torch
         self.ue = ue
         L, T, k = routing.shape
         self.ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk,
-                              T, L, device=dev, plan_policy=policy)
+                              T, L, device=dev, plan_policy=policy,
+                              quota_mode=quota_mode)
         self.routing = routing
         i32 = dict(dtype=torch.int32, device=dev)
         self.out = dict(counts=torch.empty((L, cfg.experts), **i32),
@@ -169,7 +170,7 @@ def _spread(x):
             round(float(np.max(x)), 4)]
 
 
-def bench_stale(ue, W, dev):
+def bench_stale(ue, W, dev, policy=0, quota_mode=0):
     """Max/mean rank load when each plan comes from earlier loads instead of
     the exact current ones: the previous microbatch's plan and the plan of
     the summed earlier microbatches under the pipeline workload's drift,
@@ -180,7 +181,7 @@ def bench_stale(ue, W, dev):
     out = {}
     cfg = W.CONFIGS["pipeline"]
     routing = W.make_routing(cfg, device=dev)
-    rb = Rebalance(ue, cfg, routing, dev)
+    rb = Rebalance(ue, cfg, routing, dev, policy, quota_mode)
     rb.step()
     ctx = rb.ctx
     counts = rb.out["counts"]
@@ -206,7 +207,8 @@ def bench_stale(ue, W, dev):
     r0 = W.make_routing(cfg, device=dev)
     r1 = W.make_routing(cfg, device=dev, step=1)
     ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
-                     cfg.layers, device=dev)
+                     cfg.layers, device=dev, plan_policy=policy,
+                     quota_mode=quota_mode)
     old = ctx.placement_fields(ue.ue_plan(ctx, ue.ue_load(ctx, r0)))
     c1 = ue.ue_load(ctx, r1)
     now = ctx.placement_fields(ue.ue_plan(ctx, c1))
@@ -223,10 +225,15 @@ def bench_stale(ue, W, dev):
     return out
 
 
-def bench_best_fit(ue, cfg, routing, dev, steps, warmup):
-    """The same rebalance under the best-fit planner rule: time and the
-    balance it reaches."""
-    rb = Rebalance(ue, cfg, routing, dev, policy=ue.PLAN_BEST_FIT)
+# planner rules besides the default: (destination rule, quota mode)
+RULES = {"best_fit": (1, 0), "least_loaded_search": (0, 1),
+         "best_fit_search": (1, 1)}
+
+
+def bench_rule(ue, cfg, routing, dev, steps, warmup, policy, quota_mode):
+    """The same rebalance under another planner rule: time and the balance
+    it reaches."""
+    rb = Rebalance(ue, cfg, routing, dev, policy, quota_mode)
     ms = time_steps(rb.step, steps, warmup)
     phases = phase_times(rb, max(steps, 10))
     return {"us_per_rebalance": round(ms * 1000.0, 2),
@@ -234,11 +241,11 @@ def bench_best_fit(ue, cfg, routing, dev, steps, warmup):
             "imbalance": imbalance(rb, cfg)}
 
 
-def bench_large_ep(ue, W, dev, policy=0):
+def bench_large_ep(ue, W, dev, policy=0, quota_mode=0):
     import torch
     cfg = W.CONFIGS["large_ep"]
     routing = W.make_routing(cfg, device=dev)
-    rb = Rebalance(ue, cfg, routing, dev, policy)
+    rb = Rebalance(ue, cfg, routing, dev, policy, quota_mode)
     for _ in range(20):
         rb.step()
     torch.cuda.synchronize()
@@ -254,7 +261,8 @@ def bench_large_ep(ue, W, dev, policy=0):
     return {"workload": "large_ep: E=256 k=8 R=256 (1 native + 1 spare) "
                         "T=262144, 1 layer",
             "planner": ("best fit" if policy == ue.PLAN_BEST_FIT
-                        else "least loaded"),
+                        else "least loaded") +
+                       (", quota search" if quota_mode else ""),
             "us_per_rebalance_p10_p50_p90": [round(t[reps // 10], 2),
                                              round(t[reps // 2], 2),
                                              round(t[9 * reps // 10], 2)],
@@ -417,7 +425,8 @@ def main():
         elif args.only == "stream":
             res = bench_stream(ue, W, dev)
         elif args.only == "stale":
-            res = bench_stale(ue, W, dev)
+            res = {name: bench_stale(ue, W, dev, pol, qm) for name, (pol, qm)
+                   in [("least_loaded", (0, 0))] + list(RULES.items())}
         elif args.only == "gather":
             res = bench_gather(ue, W, dev)
         if args.calib_copy:
@@ -475,23 +484,28 @@ def main():
         "imbalance": imbalance(rb, cfg),
     }
     if not args.no_extra:
-        log("dsv3 under the best-fit planner")
-        line["best_fit"] = bench_best_fit(ue, cfg, rb.routing, dev,
-                                          args.steps, args.warmup)
+        line["rules"] = {}
+        for name, (pol, qm) in RULES.items():
+            log(f"dsv3 under planner rule {name}")
+            line["rules"][name] = bench_rule(ue, cfg, rb.routing, dev,
+                                             args.steps, args.warmup, pol, qm)
     routing_host = rb.routing.cpu()
     del rb
     torch.cuda.empty_cache()
     if not args.no_extra:
         log("large_ep")
         line["large_ep"] = bench_large_ep(ue, W, dev)
-        line["large_ep_best_fit"] = bench_large_ep(ue, W, dev,
-                                                   ue.PLAN_BEST_FIT)
+        line["large_ep_rules"] = {
+            name: bench_large_ep(ue, W, dev, pol, qm)
+            for name, (pol, qm) in RULES.items()}
         log("stream")
         line["stream"] = bench_stream(ue, W, dev)
         log("gather")
         line["gather"] = bench_gather(ue, W, dev)
         log("stale plans")
-        line["stale_plan"] = bench_stale(ue, W, dev)
+        line["stale_plan"] = {
+            "least_loaded": bench_stale(ue, W, dev),
+            "best_fit_search": bench_stale(ue, W, dev, *RULES["best_fit_search"])}
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(routing_host, cfg,

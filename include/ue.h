@@ -67,7 +67,9 @@ typedef enum ue_status {
  *   max_tokens         largest T of any call (T*k < 2^30)
  *   max_layers         largest L (layers or microbatches) of any call
  *   plan_policy        destination rule of the planner (see ue_plan):
- *                      UE_PLAN_LEAST_LOADED (0) or UE_PLAN_BEST_FIT (1)    */
+ *                      UE_PLAN_LEAST_LOADED (0) or UE_PLAN_BEST_FIT (1)
+ *   quota_mode         how the planner sets the quota (see ue_plan):
+ *                      UE_QUOTA_FIXED (0) or UE_QUOTA_SEARCH (1)           */
 typedef struct ue_config {
     int32_t num_experts;
     int32_t num_ranks;
@@ -76,6 +78,7 @@ typedef struct ue_config {
     int32_t max_tokens;
     int32_t max_layers;
     int32_t plan_policy;
+    int32_t quota_mode;
 } ue_config;
 
 enum {
@@ -83,6 +86,12 @@ enum {
     UE_PLAN_BEST_FIT = 1       /* a chunk the least-loaded rank would not
                                   fill goes to the eligible rank with the
                                   smallest headroom that holds it          */
+};
+
+enum {
+    UE_QUOTA_FIXED = 0,        /* Q = ceil(sum(counts) / R)                 */
+    UE_QUOTA_SEARCH = 1        /* the lowest of Q0 + j*ceil(Q0/256), j < 64,
+                                  at which nothing is left over (else Q0)   */
 };
 
 typedef struct ue_ctx ue_ctx;
@@ -161,6 +170,10 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
  *   expert remainder) is below the least-loaded rank's headroom, it goes
  *   whole to the eligible rank with the smallest headroom >= the amount
  *   (ties: lowest id) instead.
+ *   Under UE_QUOTA_SEARCH the plan above is made at the quotas
+ *   Q0 + j*ceil(Q0/256), j = 0..63 (Q0 = ceil(sum(counts)/R)), in order,
+ *   and the first that leaves nothing over is kept; with none, Q0 stands.
+ *   The placement's quota field holds the quota used.
  *   counts     device, int32 [L, E] (e.g. from ue_load)
  *   placement  device, L blocks of ue_placement_bytes() bytes, out
  * Fully on the device; nothing returns to the host. */

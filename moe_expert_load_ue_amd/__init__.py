@@ -40,9 +40,11 @@ class ue_config(ctypes.Structure):
                 ("topk", ctypes.c_int32),
                 ("max_tokens", ctypes.c_int32),
                 ("max_layers", ctypes.c_int32),
-                ("plan_policy", ctypes.c_int32)]
+                ("plan_policy", ctypes.c_int32),
+                ("quota_mode", ctypes.c_int32)]
 
 PLAN_LEAST_LOADED, PLAN_BEST_FIT = 0, 1
+QUOTA_FIXED, QUOTA_SEARCH = 0, 1
 
 
 PLACEMENT_FIELDS = ("words", "quota", "exhausted", "residual", "n_rep",
@@ -135,7 +137,8 @@ class Context:
 
     def __init__(self, num_experts: int, num_ranks: int, spare_per_rank: int,
                  topk: int, max_tokens: int, max_layers: int = 1,
-                 device=None, plan_policy: int = PLAN_LEAST_LOADED):
+                 device=None, plan_policy: int = PLAN_LEAST_LOADED,
+                 quota_mode: int = QUOTA_FIXED):
         self.device = torch.device(device if device is not None else
                                    f"cuda:{torch.cuda.current_device()}")
         self.E, self.R, self.S = int(num_experts), int(num_ranks), int(
@@ -143,10 +146,11 @@ class Context:
         self.k, self.max_tokens = int(topk), int(max_tokens)
         self.max_layers = int(max_layers)
         self.plan_policy = int(plan_policy)
+        self.quota_mode = int(quota_mode)
         self.N = self.E // self.R if self.R else 0
         self.P = self.R * (self.N + self.S)
         cfg = ue_config(self.E, self.R, self.S, self.k, self.max_tokens,
-                        self.max_layers, self.plan_policy)
+                        self.max_layers, self.plan_policy, self.quota_mode)
         h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             rc = library().ue_create(ctypes.byref(cfg), ctypes.byref(h))
@@ -220,10 +224,10 @@ class Context:
 
 
 def ue_create(num_experts, num_ranks, spare_per_rank, topk, max_tokens,
-              max_layers=1, device=None, plan_policy=PLAN_LEAST_LOADED
-              ) -> Context:
+              max_layers=1, device=None, plan_policy=PLAN_LEAST_LOADED,
+              quota_mode=QUOTA_FIXED) -> Context:
     return Context(num_experts, num_ranks, spare_per_rank, topk, max_tokens,
-                   max_layers, device, plan_policy)
+                   max_layers, device, plan_policy, quota_mode)
 
 
 def ue_destroy(ctx: Context):

@@ -39,7 +39,7 @@ namespace {
 
 struct PlanLds {
     int32_t *cnt, *rem, *load, *cand, *sorted, *first_rec, *nrec_e;
-    int32_t *dkey, *dsorted, *smove;
+    int32_t *dkey, *dsorted, *scount, *slimit;
     int32_t *rec_e, *rec_p, *rec_m, *slot_cap, *slot_exp, *rep_off;
 };
 
@@ -60,7 +60,8 @@ __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
     s.load = p; p += R;
     s.dkey = p; p += R;
     s.dsorted = p; p += R;
-    s.smove = p; p += E;
+    s.scount = p; p += E;
+    s.slimit = p; p += E;
     s.rec_e = p; p += P;
     s.rec_p = p; p += P;
     s.rec_m = p; p += P;
@@ -69,17 +70,45 @@ __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
     return s;
 }
 
+// The planner runs 16 waves per layer: phases A and C use them all, and
+// the quota search runs one greedy pass per wave.
+constexpr int kPlanBlock = 1024;
+constexpr int kPlanWaves = kPlanBlock / 64;
+// Quota search: quotas Q0 + j * ceil(Q0 / kQuotaGrain), j < kQuotaSteps.
+constexpr int kQuotaSteps = 64;
+constexpr int kQuotaGrain = 256;
+static_assert(kQuotaSteps % kPlanWaves == 0, "whole rounds of passes");
+
+// Exclusive prefix sum of one value per thread over the planner's block;
+// the block total goes to `total`. Contains barriers: every thread calls it.
+__device__ __forceinline__ int plan_block_sum(int v, int *wsum, int &total) {
+    const int w = threadIdx.x >> 6;
+    const int x = wave_inclusive_sum(v);
+    if (lane_id() == 63) wsum[w] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < kPlanWaves; ++i) {
+        const int t = wsum[i];
+        before += (i < w) ? t : 0;
+        total += t;
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
 // Exclusive scan of `n` ints in place in LDS (n up to a few thousand);
 // returns the total. Every thread must call it.
 __device__ int block_scan_inplace(int32_t *data, int n, int *wsum) {
     const int tid = threadIdx.x;
-    const int per = (n + kBlock - 1) / kBlock;
+    const int per = (n + kPlanBlock - 1) / kPlanBlock;
     const int b = tid * per;
     const int e = (b + per < n) ? b + per : n;
     int local = 0;
     for (int i = b; i < e; ++i) local += data[i];
     int total;
-    int run = block_exclusive_sum(local, wsum, total);
+    int run = plan_block_sum(local, wsum, total);
     for (int i = b; i < e; ++i) {
         const int v = data[i];
         data[i] = run;
@@ -129,14 +158,18 @@ __device__ __forceinline__ uint32_t wave_sat_inclusive_sum(uint32_t x) {
     return x;
 }
 
-// The spill loop, run by wave 0 alone.
+// The spill loop at quota Q, run by one wave. With `write` it records the
+// chunks in LDS; without, it only finds whether the plan runs out (the
+// quota search runs it so, one quota per wave).
 //  - Candidate c (in order) moves A_c = min(count, its home rank's excess
-//    left by the rank's earlier candidates), found in part A; the loop
-//    only places those amounts, chunk by chunk, and stops the plan when no
-//    destination is left (exhausted).
-//  - dsorted holds the nd ranks eligible at the start as keys (load << rbits
-//    | rank), ascending: such a rank has all S spare slots free until it is
-//    first chosen, and the chunks of a run of such ranks are computed 64 at
+//    over Q left by the rank's earlier candidates) = clamp(limit_c - Q, 0,
+//    count_c), where limit_c = rank load - counts of the rank's earlier
+//    candidates (part A); the loop only places those amounts, chunk by
+//    chunk, and stops the plan when no destination is left (exhausted).
+//  - dsorted holds ranks with a spare slot as keys (load << rbits | rank),
+//    ascending; the nd of them below Q are eligible at the start. Such a
+//    rank has all S spare slots free until it is first chosen, and the
+//    chunks of a run of such ranks are computed 64 at
 //    a time: lane j takes the j-th next rank, a saturating prefix sum of
 //    their headrooms (Q - load) finds the rank where the amount runs out,
 //    every rank before it is filled to Q and that rank takes the rest.
@@ -152,10 +185,21 @@ __device__ __forceinline__ uint32_t wave_sat_inclusive_sum(uint32_t x) {
 //    gone (bit b of lane l: entry 64 b + l) and skipped when the run gets
 //    there.
 template <int RPL>
-__device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
-                           int NS, int Q, int rbits, bool best_fit,
-                           int &nrec_out, int &exhausted_out) {
+__device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
+                           int N, int NS, int Q, int rbits, bool best_fit,
+                           bool write, int &nrec_out, int &exhausted_out) {
     const int lane = threadIdx.x & 63;
+    // list entries below Q (a prefix: the list is ascending)
+    int nd = 0;
+    {
+        const uint32_t qkey = static_cast<uint32_t>(Q) << rbits;
+        for (int x0 = 0; x0 < nd_all; x0 += 64) {
+            const int idx = x0 + lane;
+            const bool below = idx < nd_all &&
+                               static_cast<uint32_t>(s.dsorted[idx]) < qkey;
+            nd += __builtin_popcountll(__ballot(below));
+        }
+    }
     uint32_t hkey[RPL];
     int hfree[RPL];
 #pragma unroll
@@ -199,7 +243,7 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
         return in && ((w >> ((idx >> 6) & 31)) & 1u) != 0;
     };
     auto record = [&](int e, int d, int fr, int m) {
-        if (lane == 0) {
+        if (write && lane == 0) {
             s.rec_e[nrec] = e;
             s.rec_p[nrec] = d * NS + N + (S - fr);
             s.rec_m[nrec] = m;
@@ -274,12 +318,15 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
             ++h_count;
         }
     };
-    ListWindow cand, cmove;
+    ListWindow cand, ccount, climit;
     cand.init(s.sorted, ncand);
-    cmove.init(s.smove, ncand);
+    ccount.init(s.scount, ncand);
+    climit.init(s.slimit, ncand);
     for (int c = 0; c < ncand && !exhausted; ++c) {
         const int e = cand.get(c);
-        int rem = cmove.get(c);
+        const int cnt = ccount.get(c);
+        const int over = climit.get(c) - Q;
+        int rem = over <= 0 ? 0 : (cnt < over ? cnt : over);
         while (rem > 0 && !exhausted) {
             const uint32_t kh = h_count > 0 ? wave_min_u32(my_min) : 0xFFFFFFFFu;
             // the next list ranks below the smallest held key, within the
@@ -311,7 +358,7 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
             // on the hit lane (unless best fit sends it elsewhere)
             const bool put = run && (lane < hl || (hit && lane == hl && !bf));
             const uint64_t puts = __ballot(put);
-            if (put) {
+            if (write && put) {
                 const int m = lane == hl ? need : h;
                 const int d = static_cast<int>(key & rmask);
                 const int at = nrec + static_cast<int>(mask_rank(puts));
@@ -370,12 +417,31 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd, int R, int S, int N,
     exhausted_out = exhausted;
 }
 
-__global__ __launch_bounds__(kBlock) void k_plan(
+// One greedy pass at quota Q by the calling wave, dispatched on the number
+// of ranks each lane may hold.
+__device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
+                           int N, int NS, int Q, int rbits, bool best_fit,
+                           bool write, int &nrec, int &exhausted) {
+    nrec = 0;
+    exhausted = 0;
+    switch ((R + 63) / 64) {
+        case 1: spill_loop<1>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+        case 2: spill_loop<2>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+        case 3:
+        case 4: spill_loop<4>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+        case 5: case 6: case 7:
+        case 8: spill_loop<8>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+        default: spill_loop<16>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+    }
+}
+
+__global__ __launch_bounds__(kPlanBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
-    int P, int rbits, int policy, uint32_t lds_bytes, ue_placement_layout lay,
-    int32_t *__restrict__ placement) {
+    int P, int rbits, int policy, int quota_mode, uint32_t lds_bytes,
+    ue_placement_layout lay, int32_t *__restrict__ placement) {
     extern __shared__ __align__(16) int32_t lds[];
-    __shared__ int wsum[kWaves];
+    __shared__ int wsum[kPlanWaves];
+    __shared__ int s_works[kPlanWaves];
     __shared__ int s_ncand, s_nd, s_nrec, s_exhausted, s_quota;
 
     const int layer = blockIdx.x;
@@ -392,7 +458,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(
 
     // ---- A. loads, quota, candidates ----------------------------------
     int part = 0;
-    for (int e = tid; e < E; e += kBlock) {
+    for (int e = tid; e < E; e += kPlanBlock) {
         const int c = cin[e];
         s.cnt[e] = c;
         s.rem[e] = c;
@@ -401,9 +467,13 @@ __global__ __launch_bounds__(kBlock) void k_plan(
         part += c;
     }
     int total;
-    block_exclusive_sum(part, wsum, total);   // barrier: cnt visible
-    const int Q = (total + R - 1) / R;
-    for (int r = tid; r < R; r += kBlock) {
+    plan_block_sum(part, wsum, total);   // barrier: cnt visible
+    const int Q0 = (total + R - 1) / R;
+    const bool search = quota_mode == UE_QUOTA_SEARCH;
+    const int step = (Q0 + kQuotaGrain - 1) / kQuotaGrain;
+    // highest quota any pass may use: ranks below it can be destinations
+    const int Qmax = search ? Q0 + (kQuotaSteps - 1) * step : Q0;
+    for (int r = tid; r < R; r += kPlanBlock) {
         int l = 0;
         for (int i = 0; i < N; ++i) l += s.cnt[r * N + i];
         s.load[r] = l;
@@ -411,30 +481,32 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     }
     __syncthreads();
 
-    // candidates in id order: experts whose home rank is above quota
+    // candidates in id order: experts whose home rank is above Q0 (above
+    // any quota tried, a superset of each pass's candidates)
     {
-        const int per = (E + kBlock - 1) / kBlock;
+        const int per = (E + kPlanBlock - 1) / kPlanBlock;
         const int b = tid * per;
         const int e_end = (b + per < E) ? b + per : E;
         int local = 0;
-        for (int e = b; e < e_end; ++e) local += (s.load[e / N] > Q);
+        for (int e = b; e < e_end; ++e) local += (s.load[e / N] > Q0);
         int n;
-        int pos = block_exclusive_sum(local, wsum, n);
+        int pos = plan_block_sum(local, wsum, n);
         // packed (home rank << 16 | expert), E and R below 2^16, and the
         // count beside it
         int2 *cand2 = reinterpret_cast<int2 *>(s.cand);
         for (int e = b; e < e_end; ++e)
-            if (s.load[e / N] > Q)
+            if (s.load[e / N] > Q0)
                 cand2[pos++] = int2{((e / N) << 16) | e, s.cnt[e]};
         if (tid == 0) s_ncand = n;
     }
     __syncthreads();
     const int ncand = s_ncand;
-    // rank each candidate by (count desc, id asc); the amount it moves is
-    // its count capped by the excess its home rank still has after the
-    // rank's earlier candidates (each of those moved min(count, excess))
+    // rank each candidate by (count desc, id asc); at quota Q it moves its
+    // count capped by the excess its home rank still has after the rank's
+    // earlier candidates (each of those moved min(count, excess)), i.e.
+    // clamp(limit - Q, 0, count) with limit = rank load - their counts
     const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
-    for (int i = tid; i < ncand; i += kBlock) {
+    for (int i = tid; i < ncand; i += kPlanBlock) {
         const int2 me = cand2[i];
         const int e = me.x & 0xFFFF;
         const int r = me.x >> 16;
@@ -447,24 +519,23 @@ __global__ __launch_bounds__(kBlock) void k_plan(
             pos += earlier;
             before += (earlier && (o.x >> 16) == r) ? o.y : 0;
         }
-        const int excess = s.load[r] - Q;
-        const int left = excess - (before < excess ? before : excess);
         s.sorted[pos] = e;
-        s.smove[pos] = c < left ? c : left;
+        s.scount[pos] = c;
+        s.slimit[pos] = s.load[r] - before;
     }
-    // ranks eligible at the start (a spare slot, load below quota), as keys
-    // (load << rbits | rank), compacted in rank order then placed by their
-    // rank among the keys (distinct, so the order is strict)
+    // ranks that can receive at some quota tried (a spare slot, load below
+    // Qmax), as keys (load << rbits | rank), compacted in rank order then
+    // placed by their rank among the keys (distinct, so the order is strict)
     {
-        const int per = (R + kBlock - 1) / kBlock;
+        const int per = (R + kPlanBlock - 1) / kPlanBlock;
         const int b = tid * per;
         const int r_end = (b + per < R) ? b + per : R;
         int local = 0;
-        for (int r = b; r < r_end; ++r) local += (S > 0 && s.load[r] < Q);
+        for (int r = b; r < r_end; ++r) local += (S > 0 && s.load[r] < Qmax);
         int n;
-        int pos = block_exclusive_sum(local, wsum, n);
+        int pos = plan_block_sum(local, wsum, n);
         for (int r = b; r < r_end; ++r)
-            if (S > 0 && s.load[r] < Q)
+            if (S > 0 && s.load[r] < Qmax)
                 s.dkey[pos++] = static_cast<int32_t>(
                     (static_cast<uint32_t>(s.load[r]) << rbits) |
                     static_cast<uint32_t>(r));
@@ -472,7 +543,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     }
     __syncthreads();
     const int nd = s_nd;
-    for (int i = tid; i < nd; i += kBlock) {
+    for (int i = tid; i < nd; i += kPlanBlock) {
         const uint32_t k = static_cast<uint32_t>(s.dkey[i]);
         int pos = 0;
         for (int j = 0; j < nd; ++j)
@@ -481,24 +552,41 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     }
     __syncthreads();
 
-    // ---- B. sequential spill loop on wave 0 ------------------------------
-    if (tid < 64) {
-        const bool best_fit = policy == UE_PLAN_BEST_FIT;
-        int nrec = 0, exhausted = 0;
-        switch ((R + 63) / 64) {
-            case 1: spill_loop<1>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
-            case 2: spill_loop<2>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
-            case 3:
-            case 4: spill_loop<4>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
-            case 5: case 6: case 7:
-            case 8: spill_loop<8>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
-            default: spill_loop<16>(s, ncand, nd, R, S, N, NS, Q, rbits, best_fit, nrec, exhausted); break;
+    const bool best_fit = policy == UE_PLAN_BEST_FIT;
+    const int wave = tid >> 6;
+    // ---- B. greedy passes. Quota search: rounds of one pass per wave over
+    // the quotas in order; the first round with a quota that leaves nothing
+    // over ends the search, and the lowest such quota of that round is kept
+    // (every lower one was tried); with none, Q0 stands. Then wave 0 makes
+    // the plan at the chosen quota and records it. One call site keeps the
+    // pass inlined once.
+    int Q = Q0;
+    int j0 = 0;
+    bool rec = !search;
+#pragma unroll 1
+    while (true) {
+        int nrec_w = 0, exh_w = 0;
+        if (!rec || wave == 0)
+            spill_pass(s, ncand, nd, R, S, N, NS,
+                       rec ? Q : Q0 + (j0 + wave) * step, rbits, best_fit,
+                       rec, nrec_w, exh_w);
+        if (rec) {
+            if (tid == 0) {
+                s_nrec = nrec_w;
+                s_exhausted = exh_w;
+                s_quota = Q;
+            }
+            break;
         }
-        if (tid == 0) {
-            s_nrec = nrec;
-            s_exhausted = exhausted;
-            s_quota = Q;
-        }
+        if ((tid & 63) == 0) s_works[wave] = !exh_w;
+        __syncthreads();
+        int first = -1;
+        for (int w = kPlanWaves - 1; w >= 0; --w)
+            if (s_works[w]) first = w;
+        __syncthreads();
+        if (first >= 0) Q = Q0 + (j0 + first) * step;
+        j0 += kPlanWaves;
+        rec = first >= 0 || j0 >= kQuotaSteps;
     }
     __syncthreads();
 
@@ -506,7 +594,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     // the first of them and the remainder kept by the master; per rank: the
     // loads after the plan. Integer adds, so the order does not matter.
     const int nrec = s_nrec;
-    for (int i = tid; i < nrec; i += kBlock) {
+    for (int i = tid; i < nrec; i += kPlanBlock) {
         const int e = s.rec_e[i];
         const int m = s.rec_m[i];
         if (i == 0 || s.rec_e[i - 1] != e) s.first_rec[e] = i;
@@ -518,10 +606,10 @@ __global__ __launch_bounds__(kBlock) void k_plan(
     __syncthreads();
 
     // ---- C. replica table and slot tables --------------------------------
-    for (int e = tid; e < E; e += kBlock) s.rep_off[e] = 1 + s.nrec_e[e];
+    for (int e = tid; e < E; e += kPlanBlock) s.rep_off[e] = 1 + s.nrec_e[e];
     __syncthreads();
     const int n_rep = block_scan_inplace(s.rep_off, E, wsum);
-    for (int e = tid; e < E; e += kBlock) {
+    for (int e = tid; e < E; e += kPlanBlock) {
         const int base = s.rep_off[e];
         out[lay.rep_off + e] = base;
         out[lay.rep_slot + base] = (e / N) * NS + (e % N);
@@ -534,43 +622,43 @@ __global__ __launch_bounds__(kBlock) void k_plan(
         }
     }
     if (tid == 0) out[lay.rep_off + E] = n_rep;
-    for (int i = n_rep + tid; i < P; i += kBlock) {
+    for (int i = n_rep + tid; i < P; i += kPlanBlock) {
         out[lay.rep_slot + i] = -1;
         out[lay.rep_cap + i] = 0;
     }
-    for (int p = tid; p < P; p += kBlock) {
+    for (int p = tid; p < P; p += kPlanBlock) {
         s.slot_cap[p] = 0;
         s.slot_exp[p] = -1;
     }
     __syncthreads();
-    for (int e = tid; e < E; e += kBlock) {
+    for (int e = tid; e < E; e += kPlanBlock) {
         const int p = (e / N) * NS + (e % N);
         s.slot_exp[p] = e;
         s.slot_cap[p] = s.rem[e];
     }
-    for (int i = tid; i < nrec; i += kBlock) {
+    for (int i = tid; i < nrec; i += kPlanBlock) {
         s.slot_exp[s.rec_p[i]] = s.rec_e[i];
         s.slot_cap[s.rec_p[i]] = s.rec_m[i];
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kBlock) {
+    for (int p = tid; p < P; p += kPlanBlock) {
         out[lay.slot_expert + p] = s.slot_exp[p];
         out[lay.slot_cap + p] = s.slot_cap[p];
     }
     __syncthreads();
     const int slot_total = block_scan_inplace(s.slot_cap, P, wsum);
-    for (int p = tid; p < P; p += kBlock) out[lay.slot_off + p] = s.slot_cap[p];
+    for (int p = tid; p < P; p += kPlanBlock) out[lay.slot_off + p] = s.slot_cap[p];
     int resid = 0;
-    for (int r = tid; r < R; r += kBlock) {
+    for (int r = tid; r < R; r += kPlanBlock) {
         const int l = s.load[r];
         out[lay.load_after + r] = l;
-        resid += (l > Q) ? (l - Q) : 0;
+        resid += (l > Q) ? (l - Q) : 0;   // Q: the quota used
     }
     int resid_total;
-    block_exclusive_sum(resid, wsum, resid_total);
+    plan_block_sum(resid, wsum, resid_total);
     // the block's alignment padding is written too, so a block is fully
     // defined by its counts
-    for (int i = lay.load_after + R + tid; i < lay.words; i += kBlock) out[i] = 0;
+    for (int i = lay.load_after + R + tid; i < lay.words; i += kPlanBlock) out[i] = 0;
     if (tid == 0) {
         out[lay.slot_off + P] = slot_total;
         out[lay.quota] = s_quota;
@@ -583,7 +671,7 @@ __global__ __launch_bounds__(kBlock) void k_plan(
 }  // namespace
 
 size_t plan_lds_bytes(int E, int R, int P) {
-    return sizeof(int32_t) * (static_cast<size_t>(9) * E + 1 + 3 * R + 5 * P);
+    return sizeof(int32_t) * (static_cast<size_t>(10) * E + 1 + 3 * R + 5 * P);
 }
 
 hipError_t plan_prepare(size_t lds_bytes) {
@@ -594,9 +682,10 @@ hipError_t plan_prepare(size_t lds_bytes) {
 
 hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        int32_t *placement, hipStream_t s) {
-    hipLaunchKernelGGL(k_plan, dim3(L), dim3(kBlock), c.plan_lds, s, counts,
-                       c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
+    hipLaunchKernelGGL(k_plan, dim3(L), dim3(kPlanBlock), c.plan_lds, s,
+                       counts, c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
                        static_cast<int>(c.cfg.plan_policy),
+                       static_cast<int>(c.cfg.quota_mode),
                        static_cast<uint32_t>(c.plan_lds), c.lay, placement);
     return hipGetLastError();
 }

@@ -85,7 +85,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         S > ue::kMaxSpare || k < 1 || k > E || cfg->max_tokens < 0 ||
         cfg->max_layers < 1 ||
         (cfg->plan_policy != UE_PLAN_LEAST_LOADED &&
-         cfg->plan_policy != UE_PLAN_BEST_FIT))
+         cfg->plan_policy != UE_PLAN_BEST_FIT) ||
+        (cfg->quota_mode != UE_QUOTA_FIXED &&
+         cfg->quota_mode != UE_QUOTA_SEARCH))
         return UE_EUNSUPPORTED;
     const int N = E / R, NS = N + S;
     const int64_t P = static_cast<int64_t>(R) * NS;

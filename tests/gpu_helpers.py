@@ -40,7 +40,8 @@ def gpu_rebalance(ctx, routing, with_inv=True, fused=False):
     torch.cuda.synchronize(dev)
     f = ctx.placement_fields(placement)
     res = dict(counts=counts.cpu().numpy(), invalid=invalid.cpu().numpy(),
-               placement=placement.cpu().numpy(), policy=ctx.plan_policy)
+               placement=placement.cpu().numpy(), policy=ctx.plan_policy,
+               quota_mode=ctx.quota_mode)
     res["plan"] = {k: v.cpu().numpy() for k, v in f.items()}
     for k, v in out.items():
         res[k] = None if v is None else v.cpu().numpy()
@@ -56,7 +57,8 @@ def compare_with_oracle(res, routing_np, E, R, S, layers=None):
     assert np.array_equal(res["invalid"], invalid.astype(np.int32)), "invalid"
     flat = routing_np.reshape(L, -1)
     for layer in layers:
-        pl = oracle.plan(counts[layer], R, S, res.get("policy", 0))
+        pl = oracle.plan(counts[layer], R, S, res.get("policy", 0),
+                         res.get("quota_mode", 0))
         for key in PLAN_SCALARS:
             got = int(res["plan"][key][layer])
             assert got == pl[key], f"layer {layer} {key}: {got} != {pl[key]}"

@@ -14,9 +14,17 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def make_ctx(E, R, S, k, T, L=1, policy=ue.PLAN_LEAST_LOADED):
+def make_ctx(E, R, S, k, T, L=1, policy=ue.PLAN_LEAST_LOADED,
+             quota_mode=ue.QUOTA_FIXED):
     return ue.Context(E, R, S, k, max(T, 1), L, device=DEV,
-                      plan_policy=policy)
+                      plan_policy=policy, quota_mode=quota_mode)
+
+
+# (destination rule, quota mode): the default, best fit, and each with the
+# quota search
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1)]
+RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
+            "best_fit_search"]
 
 
 @pytest.mark.parametrize("case", [g for g in pins.golden_cases()
@@ -25,7 +33,8 @@ def test_golden_cases(case):
     say("golden", case["name"])
     routing = np.asarray(case["routing"], np.int32)[None]
     ctx = make_ctx(case["E"], case["R"], case["S"], case["k"], case["T"],
-                   policy=case.get("policy", 0))
+                   policy=case.get("policy", 0),
+                   quota_mode=case.get("quota_mode", 0))
     res = gpu_rebalance(ctx, torch.from_numpy(routing))
     for key in ("phys", "perm", "inv_perm", "rank_counts"):
         assert res[key].reshape(-1).tolist() == case[key], key
@@ -36,7 +45,8 @@ def test_golden_planner_only():
     for case in pins.golden_cases():
         say("golden plan", case["name"])
         ctx = make_ctx(case["E"], case["R"], case["S"], 1, 1,
-                       policy=case.get("policy", 0))
+                       policy=case.get("policy", 0),
+                       quota_mode=case.get("quota_mode", 0))
         counts = torch.tensor(case["counts"], dtype=torch.int32,
                               device=DEV)[None]
         f = ctx.placement_fields(ue.ue_plan(ctx, counts))
@@ -50,11 +60,11 @@ def test_golden_planner_only():
         assert f["rep_cap"][0, :n].tolist() == case["rep_cap"]
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
-def test_random_instances(policy):
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_random_instances(policy, quota_mode):
     """Seeded random shapes: tiny to several tiles with ragged tails, skew
     from uniform to extreme, S = 0..3, one to four layers."""
-    rng = np.random.default_rng(99 + policy)
+    rng = np.random.default_rng(99 + policy + 2 * quota_mode)
     for it in range(60):
         R = int(rng.integers(1, 17))
         N = int(rng.integers(1, 9))
@@ -69,19 +79,19 @@ def test_random_instances(policy):
         routing = np.stack([pins.random_routing(rng, T, E, k, skew)
                             for _ in range(L)])
         say(f"random {it}: E={E} R={R} S={S} k={k} T={T} L={L} "
-            f"policy={policy}")
-        ctx = make_ctx(E, R, S, k, T, L, policy)
+            f"policy={policy} quota_mode={quota_mode}")
+        ctx = make_ctx(E, R, S, k, T, L, policy, quota_mode)
         res = gpu_rebalance(ctx, torch.from_numpy(routing))
         compare_with_oracle(res, routing, E, R, S)
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
-def test_many_spares_and_ranks(policy):
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_many_spares_and_ranks(policy, quota_mode):
     """Several spare slots per rank (destinations that take more than one
     chunk and stay eligible), ranks beyond one wave's lanes (R > 64), and
     skew strong enough to exhaust the slots: the planner's held-rank path
     against the oracle."""
-    rng = np.random.default_rng(1234 + policy)
+    rng = np.random.default_rng(1234 + policy + 2 * quota_mode)
     shapes = [(128, 128, 3), (256, 128, 2), (96, 32, 8), (64, 16, 16),
               (512, 256, 4), (200, 100, 5), (1024, 1024, 1), (1024, 64, 12)]
     for it, (E, R, S) in enumerate(shapes):
@@ -93,24 +103,26 @@ def test_many_spares_and_ranks(policy):
         routing = np.stack([pins.random_routing(rng, T, E, k,
                                                 float(rng.uniform(0.8, 2.5)))
                             for _ in range(L)])
-        say(f"spares {it}: E={E} R={R} S={S} k={k} T={T} policy={policy}")
-        ctx = make_ctx(E, R, S, k, T, L, policy)
+        say(f"spares {it}: E={E} R={R} S={S} k={k} T={T} policy={policy} "
+            f"quota_mode={quota_mode}")
+        ctx = make_ctx(E, R, S, k, T, L, policy, quota_mode)
         for fused in (False, True):
             res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
             compare_with_oracle(res, routing, E, R, S)
 
 
-@pytest.mark.parametrize("policy", [0, 1], ids=["least_loaded", "best_fit"])
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
 @pytest.mark.parametrize("fused", [False, True], ids=["calls", "fused"])
 @pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
-def test_configs_full_size(name, fused, policy):
+def test_configs_full_size(name, fused, policy, quota_mode):
     """Every routing workload at its full size, every layer, bit-exact, as
     three calls and as one ue_rebalance call, under both planner rules."""
     cfg = W.CONFIGS[name]
-    say("full size", name, "fused" if fused else "calls", "policy", policy)
+    say("full size", name, "fused" if fused else "calls", "policy", policy,
+        "quota_mode", quota_mode)
     routing = W.make_routing(cfg, device=DEV)
     ctx = make_ctx(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
-                   cfg.layers, policy)
+                   cfg.layers, policy, quota_mode)
     res = gpu_rebalance(ctx, routing, fused=fused)
     compare_with_oracle(res, routing.cpu().numpy(), cfg.experts, cfg.ranks,
                         cfg.spare)
@@ -267,3 +279,5 @@ def test_refusals_leave_outputs_untouched():
             ue.Context(*bad, 100, 1, device=DEV)
     with pytest.raises(ue.UEError):
         ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=2)
+    with pytest.raises(ue.UEError):
+        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, quota_mode=2)
