@@ -241,6 +241,110 @@ def bench_rule(ue, cfg, routing, dev, steps, warmup, policy, quota_mode):
             "imbalance": imbalance(rb, cfg)}
 
 
+def bench_schedule(ue, W, dev, layers=4, reps=5):
+    """The forward schedule of a few dsv3 layers around the rebalance, with
+    real expert sizes: per layer, ue_rebalance, then the replica weight
+    sync driven by the plan's own replica table (256 experts x 3 matrices
+    of 7168 x 2048 bf16, one buffer per physical slot), then the dispatch
+    gather of the layer's activations ([65536, 7168] bf16). Timed on one
+    stream, and with the next layer's rebalance on a second stream
+    overlapping this layer's sync and gather. Also the single-layer
+    rebalance replayed from a captured graph against the same calls made
+    one by one."""
+    import torch
+    cfg = W.CONFIGS["dsv3"]
+    E, R, S, k, T = cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens
+    H = 7168
+    elems = W.STREAM_MATS[0]
+    routing = W.make_routing(cfg, device=dev, layers=layers)
+    ctx = ue.Context(E, R, S, k, T, 1, device=dev,
+                     plan_policy=ue.PLAN_BEST_FIT, quota_mode=ue.QUOTA_SEARCH)
+    N, NS, P = ctx.N, ctx.N + ctx.S, ctx.P
+    masters = torch.full((E, 3, elems), 0.01, dtype=torch.bfloat16, device=dev)
+    spares = torch.empty((R * S, 3, elems), dtype=torch.bfloat16, device=dev)
+    mw = [[masters[e, m] for m in range(3)] for e in range(E)]
+    slots = []
+    for p in range(P):
+        r, j = divmod(p, NS)
+        slots.append(mw[r * N + j] if j < N else
+                     [spares[r * S + j - N, m] for m in range(3)])
+    ctx.register_experts([elems] * 3, mw, None, slots, None)
+    x = torch.full((T, H), 1.0, dtype=torch.bfloat16, device=dev)
+    xo = torch.empty((T * k, H), dtype=torch.bfloat16, device=dev)
+    i32 = dict(dtype=torch.int32, device=dev)
+    outs = [dict(counts=torch.empty((1, E), **i32),
+                 invalid=torch.empty((1,), **i32),
+                 placement=ctx.new_placement(1),
+                 phys=torch.empty((1, T, k), **i32),
+                 rank_counts=torch.empty((1, R), **i32),
+                 perm=torch.empty((1, T * k), **i32),
+                 inv_perm=torch.empty((1, T * k), **i32),
+                 faults=torch.empty((1,), **i32)) for _ in range(layers)]
+    tables = [ue.replica_table(ctx, o["placement"], 0) for o in outs]
+    rin = [routing[l:l + 1].contiguous() for l in range(layers)]
+    a, b = torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)
+
+    def sequential():
+        for l in range(layers):
+            ue.ue_rebalance(ctx, rin[l], **outs[l])
+            ctx.weight_sync(*tables[l])
+            ue.ue_gather_rows(ctx, x, outs[l]["inv_perm"][0], xo)
+
+    def overlapped():
+        ev = [torch.cuda.Event() for _ in range(layers)]
+        a.wait_stream(torch.cuda.current_stream())
+        b.wait_stream(torch.cuda.current_stream())
+        for l in range(layers):
+            ue.ue_rebalance(ctx, rin[l], **outs[l], stream=a)
+            ev[l].record(a)
+        for l in range(layers):
+            b.wait_event(ev[l])
+            ctx.weight_sync(*tables[l], stream=b)
+            ue.ue_gather_rows(ctx, x, outs[l]["inv_perm"][0], xo, stream=b)
+        torch.cuda.current_stream().wait_stream(a)
+        torch.cuda.current_stream().wait_stream(b)
+
+    def per_layer(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = events(2)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / layers
+
+    def alone(fn):
+        return per_layer(lambda: [fn(l) for l in range(layers)])
+
+    res = {"workload": f"{layers} dsv3 layers (E=256, k=8, R=64, S=1, "
+                       "T=65536; 256 experts x 3 x 7168x2048 bf16; gather "
+                       "[65536, 7168] bf16), best fit with the quota search",
+           "ms_per_layer_one_stream": round(per_layer(sequential), 4),
+           "ms_per_layer_two_streams": round(per_layer(overlapped), 4),
+           "ms_rebalance": round(alone(
+               lambda l: ue.ue_rebalance(ctx, rin[l], **outs[l])), 4),
+           "ms_sync": round(alone(lambda l: ctx.weight_sync(*tables[l])), 4),
+           "ms_gather": round(alone(lambda l: ue.ue_gather_rows(
+               ctx, x, outs[l]["inv_perm"][0], xo)), 4)}
+    # single-layer rebalance: calls one by one against a graph replay
+    static = rin[0].clone()
+    ue.ue_rebalance(ctx, static, **outs[0])
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ue.ue_rebalance(ctx, static, **outs[0])
+    eager_us = per_layer(lambda: [ue.ue_rebalance(ctx, static, **outs[0])
+                                  for _ in range(layers)]) * 1000.0
+    graph_us = per_layer(lambda: [g.replay() for _ in range(layers)]) * 1000.0
+    res["single_layer_rebalance_us"] = {"calls": round(eager_us, 2),
+                                        "graph_replay": round(graph_us, 2)}
+    del g
+    ctx.close()
+    return res
+
+
 def bench_large_ep(ue, W, dev, policy=0, quota_mode=0):
     import torch
     cfg = W.CONFIGS["large_ep"]
@@ -393,7 +497,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--only", choices=["rebalance", "large_ep", "stale", "stream",
+    ap.add_argument("--only", choices=["rebalance", "large_ep", "stale",
+                                       "schedule", "stream",
                                        "gather"], default=None,
                     help="run one measurement (for profiling); prints its "
                          "JSON object instead of the contract line")
@@ -424,6 +529,8 @@ def main():
             res = bench_large_ep(ue, W, dev)
         elif args.only == "stream":
             res = bench_stream(ue, W, dev)
+        elif args.only == "schedule":
+            res = bench_schedule(ue, W, dev)
         elif args.only == "stale":
             res = {name: bench_stale(ue, W, dev, pol, qm) for name, (pol, qm)
                    in [("least_loaded", (0, 0))] + list(RULES.items())}
@@ -502,6 +609,8 @@ def main():
         line["stream"] = bench_stream(ue, W, dev)
         log("gather")
         line["gather"] = bench_gather(ue, W, dev)
+        log("schedule")
+        line["schedule"] = bench_schedule(ue, W, dev)
         log("stale plans")
         line["stale_plan"] = {
             "least_loaded": bench_stale(ue, W, dev),

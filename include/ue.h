@@ -254,8 +254,15 @@ int ue_register_experts(ue_ctx *ctx, int32_t n_experts, int32_t n_mats,
  * Every matrix of every replica becomes a bitwise copy of its master's.
  * The master is read once per tile and written to all its replicas.
  * n_experts must not exceed the registered count; buffer indices must be
- * < n_buffers (entries outside are skipped). Replica buffers must not
- * alias masters or each other. */
+ * < n_buffers (entries outside are skipped). Replica buffers that the table
+ * names must not alias masters or each other.
+ * A placement block's rep_off and rep_slot fields (ue_plan) form such a
+ * table when buffer p is registered for physical slot p (n_buffers = P):
+ * its first entry per expert is the native slot, the others are spare
+ * slots. Buffers of native slots are never named as replicas, so they may
+ * be the masters themselves. The plan then drives the sync (and, before
+ * backward, the restore: the same call with the saved plan) and the
+ * gradient reduction without leaving the device. */
 int ue_weight_sync(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
                    int32_t n_experts, void *stream);
 

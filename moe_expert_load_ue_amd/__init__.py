@@ -427,6 +427,18 @@ def ue_grad_reduce(ctx: Context, rep_off, rep_buf, n_experts=None,
     ctx._check(rc, "ue_grad_reduce")
 
 
+def replica_table(ctx: Context, placement, layer: int = 0):
+    """The replica table of one layer's placement block as the (rep_off,
+    rep_buf) pair that ue_weight_sync and ue_grad_reduce take: views of the
+    block's rep_off and rep_slot fields, on the device. With one buffer
+    registered per physical slot (buffer p for slot p), the plan drives the
+    sync and the reduction directly."""
+    blk = placement.reshape(-1, ctx.placement_words)[layer]
+    lay = ctx.layout
+    return (blk[lay["rep_off"]:lay["rep_off"] + ctx.E + 1],
+            blk[lay["rep_slot"]:lay["rep_slot"] + ctx.P])
+
+
 def ue_gather_rows(ctx: Context, x, inv_perm, out=None, stream=None):
     """out[pos] = x[perm[pos] // k] for one layer's inverse permutation."""
     if x.dim() != 2:

@@ -158,6 +158,30 @@ __device__ __forceinline__ uint32_t wave_sat_inclusive_sum(uint32_t x) {
     return x;
 }
 
+// Number of entries of the ascending key list `list[0, n)` below `bound`,
+// found by one wave with two LDS reads: 64 samples at stride ceil(n / 64)
+// bracket the boundary, then the entries strictly inside the bracket are
+// compared (n up to 4096).
+__device__ __forceinline__ int count_below(const int32_t *list, int n,
+                                           uint32_t bound) {
+    const int lane = threadIdx.x & 63;
+    if (n <= 64) {
+        const bool below = lane < n &&
+                           static_cast<uint32_t>(list[lane]) < bound;
+        return __builtin_popcountll(__ballot(below));
+    }
+    const int st = (n + 63) / 64;
+    const int si = lane * st;
+    const bool sb = si < n && static_cast<uint32_t>(list[si]) < bound;
+    const int nb = __builtin_popcountll(__ballot(sb));
+    if (nb == 0) return 0;
+    const int b0 = (nb - 1) * st + 1;
+    const int idx = b0 + lane;
+    const bool in = lane < st - 1 && idx < n;
+    const bool below = in && static_cast<uint32_t>(list[idx]) < bound;
+    return b0 + __builtin_popcountll(__ballot(below));
+}
+
 // The spill loop at quota Q, run by one wave. With `write` it records the
 // chunks in LDS; without, it only finds whether the plan runs out (the
 // quota search runs it so, one quota per wave).
@@ -190,16 +214,8 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
                            bool write, int &nrec_out, int &exhausted_out) {
     const int lane = threadIdx.x & 63;
     // list entries below Q (a prefix: the list is ascending)
-    int nd = 0;
-    {
-        const uint32_t qkey = static_cast<uint32_t>(Q) << rbits;
-        for (int x0 = 0; x0 < nd_all; x0 += 64) {
-            const int idx = x0 + lane;
-            const bool below = idx < nd_all &&
-                               static_cast<uint32_t>(s.dsorted[idx]) < qkey;
-            nd += __builtin_popcountll(__ballot(below));
-        }
-    }
+    const int nd = count_below(s.dsorted, nd_all,
+                               static_cast<uint32_t>(Q) << rbits);
     uint32_t hkey[RPL];
     int hfree[RPL];
 #pragma unroll
