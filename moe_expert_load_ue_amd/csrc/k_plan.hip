@@ -47,7 +47,10 @@ __device__ __forceinline__ int32_t *carve_end(const PlanLds &s, int P) {
     return s.slot_exp + P;
 }
 
-__device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
+// Chunk records: `regions` regions of 3 * R*S ints (expert, slot, amount),
+// one per wave when the quota search keeps every pass's chunks.
+__device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int S,
+                                         int P, int regions) {
     PlanLds s;
     int32_t *p = base;
     s.cnt = p; p += E;
@@ -62,9 +65,10 @@ __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int P) {
     s.dsorted = p; p += R;
     s.scount = p; p += E;
     s.slimit = p; p += E;
-    s.rec_e = p; p += P;
-    s.rec_p = p; p += P;
-    s.rec_m = p; p += P;
+    s.rec_e = p;
+    s.rec_p = p + R * S;
+    s.rec_m = p + 2 * R * S;
+    p += regions * 3 * R * S;
     s.slot_cap = p; p += P;
     s.slot_exp = p; p += P;
     return s;
@@ -98,24 +102,31 @@ __device__ __forceinline__ int plan_block_sum(int v, int *wsum, int &total) {
     return before + x - v;
 }
 
-// Exclusive scan of `n` ints in place in LDS (n up to a few thousand);
-// returns the total. Every thread must call it.
-__device__ int block_scan_inplace(int32_t *data, int n, int *wsum) {
-    const int tid = threadIdx.x;
-    const int per = (n + kPlanBlock - 1) / kPlanBlock;
-    const int b = tid * per;
-    const int e = (b + per < n) ? b + per : n;
-    int local = 0;
-    for (int i = b; i < e; ++i) local += data[i];
-    int total;
-    int run = plan_block_sum(local, wsum, total);
-    for (int i = b; i < e; ++i) {
-        const int v = data[i];
-        data[i] = run;
-        run += v;
+// Exclusive prefix sums of three values per thread at once; `wsum3` is
+// 3 * kPlanWaves ints of LDS. Contains one barrier: every thread calls it,
+// and a barrier must follow before `wsum3` is used again.
+__device__ __forceinline__ void plan_block_sum3(int v[3], int *wsum3,
+                                                int pre[3], int tot[3]) {
+    const int w = threadIdx.x >> 6;
+    int x[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        x[i] = wave_inclusive_sum(v[i]);
+        if (lane_id() == 63) wsum3[i * kPlanWaves + w] = x[i];
     }
     __syncthreads();
-    return total;
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+        int before = 0, total = 0;
+#pragma unroll
+        for (int j = 0; j < kPlanWaves; ++j) {
+            const int t = wsum3[i * kPlanWaves + j];
+            before += (j < w) ? t : 0;
+            total += t;
+        }
+        pre[i] = before + x[i] - v[i];
+        tot[i] = total;
+    }
 }
 
 // Entry c of an LDS list through a 64-entry window held one per lane:
@@ -453,18 +464,21 @@ __device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
 
 __global__ __launch_bounds__(kPlanBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
-    int P, int rbits, int policy, int quota_mode, uint32_t lds_bytes,
-    ue_placement_layout lay, int32_t *__restrict__ placement) {
+    int P, int rbits, int policy, int quota_mode, int per_wave,
+    uint32_t lds_bytes, ue_placement_layout lay,
+    int32_t *__restrict__ placement) {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kPlanWaves];
+    __shared__ int wsum3[3 * kPlanWaves];
     __shared__ int s_works[kPlanWaves];
-    __shared__ int s_ncand, s_nd, s_nrec, s_exhausted, s_quota;
+    __shared__ int s_nrecw[kPlanWaves];
+    __shared__ int s_ncand, s_nd, s_nrec, s_exhausted, s_quota, s_region;
 
     const int layer = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t *cin = counts + static_cast<int64_t>(layer) * E;
     int32_t *out = placement + static_cast<int64_t>(layer) * lay.words;
-    PlanLds s = carve(lds, E, R, P);
+    PlanLds s = carve(lds, E, R, S, P, per_wave ? kPlanWaves : 1);
     // the carve-up must fit the launch's LDS (checked, not assumed); a
     // mismatch marks the block (exhausted = -1) rather than pass silently
     if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) {
@@ -481,6 +495,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         s.nrec_e[e] = 0;
         s.first_rec[e] = 0;
         part += c;
+    }
+    for (int p = tid; p < P; p += kPlanBlock) {
+        s.slot_cap[p] = 0;
+        s.slot_exp[p] = -1;
     }
     int total;
     plan_block_sum(part, wsum, total);   // barrier: cnt visible
@@ -521,23 +539,38 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // count capped by the excess its home rank still has after the rank's
     // earlier candidates (each of those moved min(count, excess)), i.e.
     // clamp(limit - Q, 0, count) with limit = rank load - their counts
+    // (kSplit adjacent threads share a candidate, each comparing against
+    // every kSplit-th other one; their sums meet through lane swaps)
+    constexpr int kSplit = 4;
     const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
-    for (int i = tid; i < ncand; i += kPlanBlock) {
-        const int2 me = cand2[i];
+    for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
+        const int i = i0 + tid / kSplit;
+        const int q = tid % kSplit;
+        const bool act = i < ncand;
+        const int2 me = act ? cand2[i] : int2{0, 0};
         const int e = me.x & 0xFFFF;
         const int r = me.x >> 16;
         const int c = me.y;
         int pos = 0, before = 0;
-        for (int j = 0; j < ncand; ++j) {
-            const int2 o = cand2[j];
-            const int f = o.x & 0xFFFF;
-            const bool earlier = (o.y > c) || (o.y == c && f < e);
-            pos += earlier;
-            before += (earlier && (o.x >> 16) == r) ? o.y : 0;
+        if (act) {
+#pragma unroll 4
+            for (int j = q; j < ncand; j += kSplit) {
+                const int2 o = cand2[j];
+                const int f = o.x & 0xFFFF;
+                const bool earlier = (o.y > c) || (o.y == c && f < e);
+                pos += earlier;
+                before += (earlier && (o.x >> 16) == r) ? o.y : 0;
+            }
         }
-        s.sorted[pos] = e;
-        s.scount[pos] = c;
-        s.slimit[pos] = s.load[r] - before;
+        pos += __shfl_xor(pos, 1, 64);
+        pos += __shfl_xor(pos, 2, 64);
+        before += __shfl_xor(before, 1, 64);
+        before += __shfl_xor(before, 2, 64);
+        if (act && q == 0) {
+            s.sorted[pos] = e;
+            s.scount[pos] = c;
+            s.slimit[pos] = s.load[r] - before;
+        }
     }
     // ranks that can receive at some quota tried (a spare slot, load below
     // Qmax), as keys (load << rbits | rank), compacted in rank order then
@@ -559,12 +592,20 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     }
     __syncthreads();
     const int nd = s_nd;
-    for (int i = tid; i < nd; i += kPlanBlock) {
-        const uint32_t k = static_cast<uint32_t>(s.dkey[i]);
+    for (int i0 = 0; i0 < nd; i0 += kPlanBlock / kSplit) {
+        const int i = i0 + tid / kSplit;
+        const int q = tid % kSplit;
+        const bool act = i < nd;
+        const uint32_t k = act ? static_cast<uint32_t>(s.dkey[i]) : 0u;
         int pos = 0;
-        for (int j = 0; j < nd; ++j)
-            pos += static_cast<uint32_t>(s.dkey[j]) < k;
-        s.dsorted[pos] = static_cast<int32_t>(k);
+        if (act) {
+#pragma unroll 4
+            for (int j = q; j < nd; j += kSplit)
+                pos += static_cast<uint32_t>(s.dkey[j]) < k;
+        }
+        pos += __shfl_xor(pos, 1, 64);
+        pos += __shfl_xor(pos, 2, 64);
+        if (act && q == 0) s.dsorted[pos] = static_cast<int32_t>(k);
     }
     __syncthreads();
 
@@ -573,61 +614,130 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // ---- B. greedy passes. Quota search: rounds of one pass per wave over
     // the quotas in order; the first round with a quota that leaves nothing
     // over ends the search, and the lowest such quota of that round is kept
-    // (every lower one was tried); with none, Q0 stands. Then wave 0 makes
-    // the plan at the chosen quota and records it. One call site keeps the
-    // pass inlined once.
+    // (every lower one was tried); with none, Q0 stands. With a record
+    // region per wave the chosen pass's chunks are kept as they are;
+    // otherwise (and for the fixed quota) wave 0 makes the plan at the
+    // chosen quota and records it. One call site keeps the pass inlined
+    // once.
+    const int RS = R * S;
     int Q = Q0;
     int j0 = 0;
     bool rec = !search;
 #pragma unroll 1
     while (true) {
         int nrec_w = 0, exh_w = 0;
+        PlanLds sw = s;
+        if (!rec && per_wave) {
+            sw.rec_e = s.rec_e + wave * 3 * RS;
+            sw.rec_p = sw.rec_e + RS;
+            sw.rec_m = sw.rec_e + 2 * RS;
+        }
         if (!rec || wave == 0)
-            spill_pass(s, ncand, nd, R, S, N, NS,
+            spill_pass(sw, ncand, nd, R, S, N, NS,
                        rec ? Q : Q0 + (j0 + wave) * step, rbits, best_fit,
-                       rec, nrec_w, exh_w);
+                       rec || per_wave, nrec_w, exh_w);
         if (rec) {
             if (tid == 0) {
                 s_nrec = nrec_w;
                 s_exhausted = exh_w;
                 s_quota = Q;
+                s_region = 0;
             }
             break;
         }
-        if ((tid & 63) == 0) s_works[wave] = !exh_w;
+        if ((tid & 63) == 0) {
+            s_works[wave] = !exh_w;
+            s_nrecw[wave] = nrec_w;
+        }
         __syncthreads();
         int first = -1;
         for (int w = kPlanWaves - 1; w >= 0; --w)
             if (s_works[w]) first = w;
+        if (first >= 0) {
+            Q = Q0 + (j0 + first) * step;
+            if (per_wave) {
+                if (tid == 0) {
+                    s_nrec = s_nrecw[first];
+                    s_exhausted = 0;
+                    s_quota = Q;
+                    s_region = first;
+                }
+                break;
+            }
+        }
         __syncthreads();
-        if (first >= 0) Q = Q0 + (j0 + first) * step;
         j0 += kPlanWaves;
         rec = first >= 0 || j0 >= kQuotaSteps;
     }
     __syncthreads();
+    s.rec_e += s_region * 3 * RS;
+    s.rec_p += s_region * 3 * RS;
+    s.rec_m += s_region * 3 * RS;
 
     // per expert: chunks placed (records of one expert are consecutive),
     // the first of them and the remainder kept by the master; per rank: the
-    // loads after the plan. Integer adds, so the order does not matter.
+    // loads after the plan; each used spare slot takes its chunk (the slot
+    // tables were cleared in part A). Integer adds: order does not matter.
     const int nrec = s_nrec;
     for (int i = tid; i < nrec; i += kPlanBlock) {
         const int e = s.rec_e[i];
         const int m = s.rec_m[i];
+        const int p = s.rec_p[i];
         if (i == 0 || s.rec_e[i - 1] != e) s.first_rec[e] = i;
         atomicAdd(&s.nrec_e[e], 1);
         atomicSub(&s.rem[e], m);
         atomicSub(&s.load[e / N], m);
-        atomicAdd(&s.load[s.rec_p[i] / NS], m);
+        atomicAdd(&s.load[p / NS], m);
+        s.slot_exp[p] = e;
+        s.slot_cap[p] = m;
     }
     __syncthreads();
 
     // ---- C. replica table and slot tables --------------------------------
-    for (int e = tid; e < E; e += kPlanBlock) s.rep_off[e] = 1 + s.nrec_e[e];
+    // native slots hold what their masters keep
+    for (int e = tid; e < E; e += kPlanBlock) {
+        const int p = (e / N) * NS + (e % N);
+        s.slot_exp[p] = e;
+        s.slot_cap[p] = s.rem[e];
+    }
     __syncthreads();
-    const int n_rep = block_scan_inplace(s.rep_off, E, wsum);
+    // one scan for three sums: replica offsets (1 + chunks per expert),
+    // slot offsets (slot capacities) and the residual (excess over the
+    // quota used, per rank); each thread takes a contiguous run of experts
+    // and of slots
+    const int pe = (E + kPlanBlock - 1) / kPlanBlock;
+    const int pp = (P + kPlanBlock - 1) / kPlanBlock;
+    const int e0 = tid * pe, e1 = (e0 + pe < E) ? e0 + pe : E;
+    const int p0 = tid * pp, p1 = (p0 + pp < P) ? p0 + pp : P;
+    int v[3] = {0, 0, 0}, pre[3], tot[3];
+    for (int e = e0; e < e1; ++e) v[0] += 1 + s.nrec_e[e];
+    for (int p = p0; p < p1; ++p) v[1] += s.slot_cap[p];
+    for (int r = tid; r < R; r += kPlanBlock) {
+        const int l = s.load[r];
+        out[lay.load_after + r] = l;
+        v[2] += (l > Q) ? (l - Q) : 0;   // Q: the quota used
+    }
+    plan_block_sum3(v, wsum3, pre, tot);
+    const int n_rep = tot[0];
+    {
+        int run = pre[0];
+        for (int e = e0; e < e1; ++e) {
+            s.rep_off[e] = run;
+            out[lay.rep_off + e] = run;
+            run += 1 + s.nrec_e[e];
+        }
+        run = pre[1];
+        for (int p = p0; p < p1; ++p) {
+            const int c = s.slot_cap[p];
+            out[lay.slot_expert + p] = s.slot_exp[p];
+            out[lay.slot_cap + p] = c;
+            out[lay.slot_off + p] = run;
+            run += c;
+        }
+    }
+    __syncthreads();   // replica offsets visible
     for (int e = tid; e < E; e += kPlanBlock) {
         const int base = s.rep_off[e];
-        out[lay.rep_off + e] = base;
         out[lay.rep_slot + base] = (e / N) * NS + (e % N);
         out[lay.rep_cap + base] = s.rem[e];
         const int f = s.first_rec[e];
@@ -637,57 +747,29 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
             out[lay.rep_cap + base + 1 + i] = s.rec_m[f + i];
         }
     }
-    if (tid == 0) out[lay.rep_off + E] = n_rep;
     for (int i = n_rep + tid; i < P; i += kPlanBlock) {
         out[lay.rep_slot + i] = -1;
         out[lay.rep_cap + i] = 0;
     }
-    for (int p = tid; p < P; p += kPlanBlock) {
-        s.slot_cap[p] = 0;
-        s.slot_exp[p] = -1;
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kPlanBlock) {
-        const int p = (e / N) * NS + (e % N);
-        s.slot_exp[p] = e;
-        s.slot_cap[p] = s.rem[e];
-    }
-    for (int i = tid; i < nrec; i += kPlanBlock) {
-        s.slot_exp[s.rec_p[i]] = s.rec_e[i];
-        s.slot_cap[s.rec_p[i]] = s.rec_m[i];
-    }
-    __syncthreads();
-    for (int p = tid; p < P; p += kPlanBlock) {
-        out[lay.slot_expert + p] = s.slot_exp[p];
-        out[lay.slot_cap + p] = s.slot_cap[p];
-    }
-    __syncthreads();
-    const int slot_total = block_scan_inplace(s.slot_cap, P, wsum);
-    for (int p = tid; p < P; p += kPlanBlock) out[lay.slot_off + p] = s.slot_cap[p];
-    int resid = 0;
-    for (int r = tid; r < R; r += kPlanBlock) {
-        const int l = s.load[r];
-        out[lay.load_after + r] = l;
-        resid += (l > Q) ? (l - Q) : 0;   // Q: the quota used
-    }
-    int resid_total;
-    plan_block_sum(resid, wsum, resid_total);
     // the block's alignment padding is written too, so a block is fully
     // defined by its counts
     for (int i = lay.load_after + R + tid; i < lay.words; i += kPlanBlock) out[i] = 0;
     if (tid == 0) {
-        out[lay.slot_off + P] = slot_total;
+        out[lay.rep_off + E] = n_rep;
+        out[lay.slot_off + P] = tot[1];
         out[lay.quota] = s_quota;
         out[lay.exhausted] = s_exhausted;
-        out[lay.residual] = resid_total;
+        out[lay.residual] = tot[2];
         out[lay.n_rep] = n_rep;
     }
 }
 
 }  // namespace
 
-size_t plan_lds_bytes(int E, int R, int P) {
-    return sizeof(int32_t) * (static_cast<size_t>(10) * E + 1 + 3 * R + 5 * P);
+size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave) {
+    const size_t regions = per_wave ? kPlanWaves : 1;
+    return sizeof(int32_t) * (static_cast<size_t>(10) * E + 1 + 3 * R +
+                              regions * 3 * R * S + 2 * P);
 }
 
 hipError_t plan_prepare(size_t lds_bytes) {
@@ -702,6 +784,7 @@ hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        counts, c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
                        static_cast<int>(c.cfg.plan_policy),
                        static_cast<int>(c.cfg.quota_mode),
+                       c.plan_per_wave ? 1 : 0,
                        static_cast<uint32_t>(c.plan_lds), c.lay, placement);
     return hipGetLastError();
 }

@@ -138,11 +138,14 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     l.load_after = w; w += R;
     l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
 
-    c->plan_lds = ue::plan_lds_bytes(E, R, c->P);
     c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P, k);
     size_t lds_cap = prop.sharedMemPerBlock;
     if (prop.sharedMemPerBlockOptin > lds_cap)
         lds_cap = prop.sharedMemPerBlockOptin;
+    // the quota search keeps each pass's chunks when they fit in LDS
+    c->plan_per_wave = cfg->quota_mode == UE_QUOTA_SEARCH &&
+                       ue::plan_lds_bytes(E, R, S, c->P, true) + 256 <= lds_cap;
+    c->plan_lds = ue::plan_lds_bytes(E, R, S, c->P, c->plan_per_wave);
     if (c->plan_lds + 256 > lds_cap || c->reroute_lds + 256 > lds_cap ||
         ue::load_lds_bytes(E) + 256 > lds_cap) {
         delete c;

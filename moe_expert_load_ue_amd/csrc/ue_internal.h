@@ -53,6 +53,7 @@ struct ue_ctx {
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
 
     size_t plan_lds = 0;
+    bool plan_per_wave = false;   // planner keeps every pass's chunks
     size_t reroute_lds = 0;
 
     // Registered expert state (device pointer tables).
@@ -106,7 +107,9 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
                               void *out, hipStream_t s);
 
 size_t load_lds_bytes(int E);
-size_t plan_lds_bytes(int E, int R, int P);
+// per_wave: one chunk-record region per wave (the quota search keeps each
+// pass's chunks, so the chosen one needs no second pass).
+size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave);
 size_t reroute_lds_bytes(int E, int R, int P, int k);
 // Words per expert bitmap of the reroute's ranking (0: ranks by matching).
 int reroute_bitmap_words(int E, int k);
