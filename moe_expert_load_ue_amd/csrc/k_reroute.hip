@@ -240,13 +240,36 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
     // capacity prefix of each replica within its expert, from LDS; replica
     // r of expert e then covers j in [r == rep_off[e] ? 0 : rep_hi[r-1],
-    // rep_hi[r])
-    for (int e = tid; e < E; e += kBlock) {
-        int run = 0;
+    // rep_hi[r]). After a load the tile's first j of each expert (its
+    // prefix) is already known, so the same pass finds the replica that
+    // covers it: how many of the tile's assignments it still takes, its
+    // slot and the dispatch position of that first j (fields y, z, w of
+    // the expert's record; x, the tile's own order, follows the scan).
+#pragma unroll
+    for (int q = 0; q < kPerThread; ++q) {
+        const int e = tid + q * kBlock;
+        if (e >= E) break;
+        const int j0 = kAfterLoad ? pre_reg[q] : 0;
+        int run = 0, lim = 0, slot = -1, pos0 = -1;
+        bool found = false;
         const int hi = rep_off[e + 1];
         for (int i = rep_off[e]; i < hi; ++i) {
+            const int lo = run;
             run += rep_hi[i];
             rep_hi[i] = run;
+            if (kAfterLoad && !found && j0 < run) {
+                found = true;
+                const int sl = rep_slot[i];
+                if (sl >= 0) {
+                    slot = sl;
+                    pos0 = slot_off[sl] + (j0 - lo);
+                    lim = run - j0;
+                }
+            }
+        }
+        if (kAfterLoad) {
+            tbase[e] = j0;
+            einfo[e] = int4{0, lim, slot, pos0};
         }
     }
     // Physical slot and dispatch position of assignment j of expert e, or
@@ -410,45 +433,48 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int e = b; e < eend; ++e) {
             const int c = torder[e];
             torder[e] = run;
+            if (kAfterLoad) einfo[e].x = run;
             run += c;
         }
     }
 
     // ---- 3. count of each expert in earlier tiles ---------------------------
-    bool bad = false;
+    // (after a load it came with the prefixes, and the expert records are
+    // complete once the scan has written their first field)
+    int poisoned = 0;
     if (kAfterLoad) {
-#pragma unroll
-        for (int q = 0; q < kPerThread; ++q) {
-            const int e = tid + q * kBlock;
-            if (e < E) tbase[e] = pre_reg[q];
-        }
+        __syncthreads();
     } else {
         uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
-        bad = tile_lookback(st, tile, E, epoch, tcount, tbase, g.spin_limit);
+        const bool bad = tile_lookback(st, tile, E, epoch, tcount, tbase,
+                                       g.spin_limit);
+        poisoned = __syncthreads_or(bad);
     }
-    const int poisoned = __syncthreads_or(bad);
 
     // ---- 4. outputs ---------------------------------------------------------
     // Per expert, in one 16-byte word: the tile's first position in its
     // (expert, j) order, how many of the tile's assignments stay in the
     // replica covering the tile's first j, that replica's slot and the
     // dispatch position of that first j.
-    for (int e = tid; e < E; e += kBlock) {
-        int q, pos0;
-        locate(e, tbase[e], q, pos0);
-        int lim = 0;
-        if (q >= 0) {
-            // the covering replica's end: the first capacity prefix above j0
-            for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-                if (tbase[e] < rep_hi[r]) {
-                    lim = rep_hi[r] - tbase[e];
-                    break;
+    if (!kAfterLoad) {
+        for (int e = tid; e < E; e += kBlock) {
+            int q, pos0;
+            locate(e, tbase[e], q, pos0);
+            int lim = 0;
+            if (q >= 0) {
+                // the covering replica's end: the first capacity prefix
+                // above j0
+                for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
+                    if (tbase[e] < rep_hi[r]) {
+                        lim = rep_hi[r] - tbase[e];
+                        break;
+                    }
                 }
             }
+            einfo[e] = int4{torder[e], lim, q, pos0};
         }
-        einfo[e] = int4{torder[e], lim, q, pos0};
+        __syncthreads();
     }
-    __syncthreads();
     uint32_t *stage = reinterpret_cast<uint32_t *>(area);
     const bool full_tile = tile0 + kRerouteTile <= A;
     int32_t *phys_t = at(phys_l, aL);
