@@ -41,17 +41,25 @@ struct LoadArgs {
     int32_t *counts, *invalid;
 };
 
+// Two experts share a histogram word, 16 bits each: a copy of one tile
+// takes at most kLoadTile / kSub ids, far below 2^16, so neither half
+// carries into the other, and the eight copies of a word still sum
+// without carrying (kLoadTile < 2^16).
+static_assert(kLoadTile < 65536, "16-bit tile counters");
 __device__ __forceinline__ void count_one(int id, int E, int sub,
-                                          int32_t *hist) {
+                                          uint32_t *hist) {
     if (static_cast<uint32_t>(id) < static_cast<uint32_t>(E))
-        atomicAdd(&hist[id * kSub + sub], 1);
+        atomicAdd(&hist[(id >> 1) * kSub + sub], 1u << ((id & 1) << 4));
 }
 
 __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
-    int32_t *hist = lds;                   // [2][E][kSub] alternating tiles
-    int32_t *cnt = lds + 2 * kSub * g.E;   // [kLoadGroup][E] per tile
-    int32_t *gcnt = cnt + kLoadGroup * g.E;// [E] the group's counts
+    const int EH = (g.E + 1) >> 1;         // expert pairs
+    // [2][EH][kSub] alternating tiles, two 16-bit counters per word
+    uint32_t *hist = reinterpret_cast<uint32_t *>(lds);
+    // [kLoadGroup][E] per-tile counts, 16 bits each
+    uint16_t *cnt = reinterpret_cast<uint16_t *>(lds + 2 * kSub * EH);
+    int32_t *gcnt = lds + 2 * kSub * EH + (kLoadGroup * g.E + 1) / 2;  // [E]
     int32_t *excl = gcnt + g.E;            // [E] counts of earlier groups
     __shared__ uint32_t s_ticket, s_epoch;
     __shared__ int wsum[kWaves];
@@ -61,40 +69,47 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     const int tid = threadIdx.x;
     const int sub = tid & (kSub - 1);
     if (tid == 0) take_ticket(g.tick + layer, g.groups, s_ticket, s_epoch);
-    for (int i = tid; i < 2 * kSub * E; i += kBlock) hist[i] = 0;
+    for (int i = tid; i < 2 * kSub * EH; i += kBlock) hist[i] = 0u;
     __syncthreads();
     const int grp = static_cast<int>(s_ticket);
     if (grp >= g.groups) return;    // only after a corrupted earlier launch
 
     const int32_t *src = g.routing + static_cast<int64_t>(layer) * g.A;
     const int tile_first = grp * kLoadGroup;
-    // Issue the loads of every full tile of the group before counting.
-    // Plain (temporal) loads: the fused reroute reads the same routing
-    // right after, and finds it in the device-wide cache.
-    i32x4 r[kLoadGroup][kLoadItems / 4];
-    bool full[kLoadGroup];
-#pragma unroll
-    for (int s = 0; s < kLoadGroup; ++s) {
+    // The loads of a full tile are issued kAhead tiles before it is
+    // counted (a rolling set of registers). Plain (temporal) loads: the
+    // fused reroute reads the same routing right after, and finds it in the
+    // device-wide cache.
+    constexpr int kAhead = 4;
+    i32x4 r[kAhead][kLoadItems / 4];
+    auto full = [&](int s) {
         const int64_t t0 = static_cast<int64_t>(tile_first + s) * kLoadTile;
-        full[s] = g.vec4 && t0 + kLoadTile <= g.A;
-        if (full[s]) {
-            const i32x4 *v = reinterpret_cast<const i32x4 *>(src + t0);
+        return g.vec4 && t0 + kLoadTile <= g.A;
+    };
+    auto issue = [&](int s) {
+        if (full(s)) {
+            const i32x4 *v = reinterpret_cast<const i32x4 *>(
+                src + static_cast<int64_t>(tile_first + s) * kLoadTile);
 #pragma unroll
             for (int i = 0; i < kLoadItems / 4; ++i)
-                r[s][i] = v[i * kBlock + tid];
+                r[s % kAhead][i] = v[i * kBlock + tid];
         }
-    }
+    };
+#pragma unroll
+    for (int s = 0; s < kAhead && s < kLoadGroup; ++s) issue(s);
 #pragma unroll
     for (int s = 0; s < kLoadGroup; ++s) {
-        int32_t *h = hist + (s & 1) * kSub * E;
-        if (full[s]) {
+        uint32_t *h = hist + (s & 1) * kSub * EH;
+        if (full(s)) {
 #pragma unroll
             for (int i = 0; i < kLoadItems / 4; ++i) {
-                count_one(r[s][i].x, E, sub, h);
-                count_one(r[s][i].y, E, sub, h);
-                count_one(r[s][i].z, E, sub, h);
-                count_one(r[s][i].w, E, sub, h);
+                const i32x4 v = r[s % kAhead][i];
+                count_one(v.x, E, sub, h);
+                count_one(v.y, E, sub, h);
+                count_one(v.z, E, sub, h);
+                count_one(v.w, E, sub, h);
             }
+            if (s + kAhead < kLoadGroup) issue(s + kAhead);
         } else {
             const int64_t t0 = static_cast<int64_t>(tile_first + s) * kLoadTile;
             const int64_t t1 = (t0 + kLoadTile < g.A) ? t0 + kLoadTile : g.A;
@@ -105,10 +120,14 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
         // sum and clear this tile's copies while the next tile is counted
         // into the other histogram; the barrier after that count orders
         // the clearing before this histogram's next use
-        for (int e = tid; e < E; e += kBlock) {
-            i32x4 *b = reinterpret_cast<i32x4 *>(h + e * kSub);
+        for (int ep = tid; ep < EH; ep += kBlock) {
+            i32x4 *b = reinterpret_cast<i32x4 *>(h + ep * kSub);
             const i32x4 u = b[0], v = b[1];
-            cnt[s * E + e] = u.x + u.y + u.z + u.w + v.x + v.y + v.z + v.w;
+            const uint32_t t = static_cast<uint32_t>(u.x + u.y + u.z + u.w +
+                                                     v.x + v.y + v.z + v.w);
+            cnt[s * E + 2 * ep] = static_cast<uint16_t>(t & 0xFFFFu);
+            if (2 * ep + 1 < E)
+                cnt[s * E + 2 * ep + 1] = static_cast<uint16_t>(t >> 16);
             b[0] = i32x4{0, 0, 0, 0};
             b[1] = i32x4{0, 0, 0, 0};
         }
@@ -158,7 +177,10 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
 }  // namespace
 
 size_t load_lds_bytes(int E) {
-    return sizeof(int32_t) * (2 * kSub + kLoadGroup + 2) * static_cast<size_t>(E);
+    const size_t EH = (static_cast<size_t>(E) + 1) / 2;
+    return sizeof(int32_t) * (2 * kSub * EH +
+                              (static_cast<size_t>(kLoadGroup) * E + 1) / 2 +
+                              2 * static_cast<size_t>(E));
 }
 
 hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
