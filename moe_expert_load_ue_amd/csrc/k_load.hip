@@ -4,22 +4,24 @@
 // from the true token count of each expert in the current microbatch, the
 // "Load computation" component of "How dots-infra/ultraep works".
 //
-// One workgroup counts a group of kLoadGroup consecutive routing tiles of
-// one layer into LDS. Routing is skewed (a hot expert shows up in nearly
-// every token), so a tile's histogram is kept as kSub interleaved copies,
-// bin e of copy c at e * kSub + c, and lane l adds into copy l mod kSub:
-// lanes of a wave that hold the same id hit kSub different banks, which
-// bounds the serialisation of an LDS atomic at 64 / kSub lanes. Tiles
-// alternate between two such histograms, so one tile is counted while the
-// previous one is summed and cleared, with one barrier per tile. Groups then
-// combine their histograms with the decoupled lookback of ue_internal.h;
-// the group with the last ticket ends with the inclusive prefix over the
-// whole layer, which is the layer's counts. Every group also writes, for
-// each of its tiles, the count of each expert in all earlier tiles of the
-// layer (and the last group the layer's totals after the last tile): the
-// fused reroute reads those instead of scanning again. No
-// fence, no global atomics on data, no clearing launch; integer sums make
-// the result exact and order-independent.
+// One workgroup counts a group of consecutive routing tiles of one layer
+// into LDS: 8 tiles, or 16 when that still leaves two workgroups per CU
+// (fewer groups per layer shorten the lookback). Routing is skewed (a hot
+// expert shows up in nearly every token), so a tile's histogram is kept as
+// kSub interleaved copies, and lane l adds into copy l mod kSub: lanes of a
+// wave that hold the same id hit kSub different banks, which bounds the
+// serialisation of an LDS atomic at 64 / kSub lanes. Two experts share a
+// word (16 bits each): expert e of copy c is half e mod 2 of word
+// (e / 2) * kSub + c. Tiles alternate between two such histograms, so one
+// tile is counted while the previous one is summed and cleared, with one
+// barrier per tile. Groups then combine their histograms with the
+// decoupled lookback of ue_internal.h; the group with the last ticket ends
+// with the inclusive prefix over the whole layer, which is the layer's
+// counts. Every group also writes, for each of its tiles, the count of each
+// expert in all earlier tiles of the layer (and the last group the layer's
+// totals after the last tile): the fused reroute reads those instead of
+// scanning again. No fence, no global atomics on data, no clearing launch;
+// integer sums make the result exact and order-independent.
 #include "ue_internal.h"
 
 namespace ue {
@@ -52,14 +54,18 @@ __device__ __forceinline__ void count_one(int id, int E, int sub,
         atomicAdd(&hist[(id >> 1) * kSub + sub], 1u << ((id & 1) << 4));
 }
 
+// G tiles per workgroup: kLoadGroup, or kLoadGroupWide when there are
+// enough groups to fill the device (fewer groups per layer shorten the
+// lookback walks).
+template <int G>
 __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
     const int EH = (g.E + 1) >> 1;         // expert pairs
     // [2][EH][kSub] alternating tiles, two 16-bit counters per word
     uint32_t *hist = reinterpret_cast<uint32_t *>(lds);
-    // [kLoadGroup][E] per-tile counts, 16 bits each
+    // [G][E] per-tile counts, 16 bits each
     uint16_t *cnt = reinterpret_cast<uint16_t *>(lds + 2 * kSub * EH);
-    int32_t *gcnt = lds + 2 * kSub * EH + (kLoadGroup * g.E + 1) / 2;  // [E]
+    int32_t *gcnt = lds + 2 * kSub * EH + (G * g.E + 1) / 2;  // [E]
     int32_t *excl = gcnt + g.E;            // [E] counts of earlier groups
     __shared__ uint32_t s_ticket, s_epoch;
     __shared__ int wsum[kWaves];
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     if (grp >= g.groups) return;    // only after a corrupted earlier launch
 
     const int32_t *src = g.routing + static_cast<int64_t>(layer) * g.A;
-    const int tile_first = grp * kLoadGroup;
+    const int tile_first = grp * G;
     // The loads of a full tile are issued kAhead tiles before it is
     // counted (a rolling set of registers). Plain (temporal) loads: the
     // fused reroute reads the same routing right after, and finds it in the
@@ -96,9 +102,9 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
         }
     };
 #pragma unroll
-    for (int s = 0; s < kAhead && s < kLoadGroup; ++s) issue(s);
+    for (int s = 0; s < kAhead && s < G; ++s) issue(s);
 #pragma unroll
-    for (int s = 0; s < kLoadGroup; ++s) {
+    for (int s = 0; s < G; ++s) {
         uint32_t *h = hist + (s & 1) * kSub * EH;
         if (full(s)) {
 #pragma unroll
@@ -109,7 +115,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
                 count_one(v.z, E, sub, h);
                 count_one(v.w, E, sub, h);
             }
-            if (s + kAhead < kLoadGroup) issue(s + kAhead);
+            if (s + kAhead < G) issue(s + kAhead);
         } else {
             const int64_t t0 = static_cast<int64_t>(tile_first + s) * kLoadTile;
             const int64_t t1 = (t0 + kLoadTile < g.A) ? t0 + kLoadTile : g.A;
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     __syncthreads();
     for (int e = tid; e < E; e += kBlock) {
         int c = 0;
-        for (int s = 0; s < kLoadGroup; ++s) c += cnt[s * E + e];
+        for (int s = 0; s < G; ++s) c += cnt[s * E + e];
         gcnt[e] = c;
     }
     __syncthreads();
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
                   static_cast<int64_t>(layer) * (g.max_tiles + 1) * E;
     for (int e = tid; e < E; e += kBlock) {
         int run = excl[e];
-        for (int s = 0; s < kLoadGroup; ++s) {
+        for (int s = 0; s < G; ++s) {
             const int t = tile_first + s;
             if (t < g.tiles) tp[static_cast<int64_t>(t) * E + e] = run;
             run += cnt[s * E + e];
@@ -176,19 +182,25 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
 
 }  // namespace
 
-size_t load_lds_bytes(int E) {
+static size_t load_lds_bytes_for(int E, int G) {
     const size_t EH = (static_cast<size_t>(E) + 1) / 2;
     return sizeof(int32_t) * (2 * kSub * EH +
-                              (static_cast<size_t>(kLoadGroup) * E + 1) / 2 +
+                              (static_cast<size_t>(G) * E + 1) / 2 +
                               2 * static_cast<size_t>(E));
 }
+
+size_t load_lds_bytes(int E) { return load_lds_bytes_for(E, kLoadGroupWide); }
 
 hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
                        int64_t A, int32_t *counts, int32_t *invalid,
                        hipStream_t s) {
     int tiles = static_cast<int>((A + kLoadTile - 1) / kLoadTile);
     if (tiles < 1) tiles = 1;
-    const int groups = (tiles + kLoadGroup - 1) / kLoadGroup;
+    // wide groups once they still give two workgroups per CU
+    const int wide_groups = (tiles + kLoadGroupWide - 1) / kLoadGroupWide;
+    const bool wide = static_cast<int64_t>(wide_groups) * L >= 2 * c.num_cu;
+    const int G = wide ? kLoadGroupWide : kLoadGroup;
+    const int groups = (tiles + G - 1) / G;
     LoadArgs g;
     g.routing = routing;
     g.A = A;
@@ -204,8 +216,12 @@ hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
     g.tile_prefix = c.tile_prefix;
     g.counts = counts;
     g.invalid = invalid;
-    hipLaunchKernelGGL(k_load, dim3(groups, L), dim3(kBlock),
-                       load_lds_bytes(c.E), s, g);
+    if (wide)
+        hipLaunchKernelGGL(k_load<kLoadGroupWide>, dim3(groups, L),
+                           dim3(kBlock), load_lds_bytes_for(c.E, G), s, g);
+    else
+        hipLaunchKernelGGL(k_load<kLoadGroup>, dim3(groups, L), dim3(kBlock),
+                           load_lds_bytes_for(c.E, G), s, g);
     return hipGetLastError();
 }
 

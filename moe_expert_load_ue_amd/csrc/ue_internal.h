@@ -26,6 +26,7 @@ constexpr int kRerouteTile = kBlock * kRerouteItems;
 constexpr int kLoadItems = kRerouteItems;
 constexpr int kLoadTile = kRerouteTile;
 constexpr int kLoadGroup = 16384 / kLoadTile;   // tiles per load workgroup
+constexpr int kLoadGroupWide = 2 * kLoadGroup;  // ... when groups are many
 
 }  // namespace ue
 
