@@ -472,7 +472,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     __shared__ int wsum3[3 * kPlanWaves];
     __shared__ int s_works[kPlanWaves];
     __shared__ int s_nrecw[kPlanWaves];
-    __shared__ int s_ncand, s_nd, s_nrec, s_exhausted, s_quota, s_region;
+    __shared__ int s_nrec, s_exhausted, s_quota, s_region;
 
     const int layer = blockIdx.x;
     const int tid = threadIdx.x;
@@ -515,26 +515,35 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     }
     __syncthreads();
 
-    // candidates in id order: experts whose home rank is above Q0 (above
-    // any quota tried, a superset of each pass's candidates)
+    // Two lists compacted with one scan: the candidates in id order
+    // (experts whose home rank is above Q0, so above any quota tried: a
+    // superset of each pass's candidates), packed as (home rank << 16 |
+    // expert) with the count beside it (E and R below 2^16); and the ranks
+    // that can receive at some quota tried (a spare slot, load below Qmax),
+    // as keys (load << rbits | rank), in rank order.
+    int ncand, nd;
     {
-        const int per = (E + kPlanBlock - 1) / kPlanBlock;
-        const int b = tid * per;
-        const int e_end = (b + per < E) ? b + per : E;
-        int local = 0;
-        for (int e = b; e < e_end; ++e) local += (s.load[e / N] > Q0);
-        int n;
-        int pos = plan_block_sum(local, wsum, n);
-        // packed (home rank << 16 | expert), E and R below 2^16, and the
-        // count beside it
+        const int pe = (E + kPlanBlock - 1) / kPlanBlock;
+        const int e0 = tid * pe, e1 = (e0 + pe < E) ? e0 + pe : E;
+        const int pr = (R + kPlanBlock - 1) / kPlanBlock;
+        const int r0 = tid * pr, r1 = (r0 + pr < R) ? r0 + pr : R;
+        int v[3] = {0, 0, 0}, pre[3], tot[3];
+        for (int e = e0; e < e1; ++e) v[0] += (s.load[e / N] > Q0);
+        for (int r = r0; r < r1; ++r) v[1] += (S > 0 && s.load[r] < Qmax);
+        plan_block_sum3(v, wsum3, pre, tot);
         int2 *cand2 = reinterpret_cast<int2 *>(s.cand);
-        for (int e = b; e < e_end; ++e)
+        for (int e = e0; e < e1; ++e)
             if (s.load[e / N] > Q0)
-                cand2[pos++] = int2{((e / N) << 16) | e, s.cnt[e]};
-        if (tid == 0) s_ncand = n;
+                cand2[pre[0]++] = int2{((e / N) << 16) | e, s.cnt[e]};
+        for (int r = r0; r < r1; ++r)
+            if (S > 0 && s.load[r] < Qmax)
+                s.dkey[pre[1]++] = static_cast<int32_t>(
+                    (static_cast<uint32_t>(s.load[r]) << rbits) |
+                    static_cast<uint32_t>(r));
+        ncand = tot[0];
+        nd = tot[1];
     }
     __syncthreads();
-    const int ncand = s_ncand;
     // rank each candidate by (count desc, id asc); at quota Q it moves its
     // count capped by the excess its home rank still has after the rank's
     // earlier candidates (each of those moved min(count, excess)), i.e.
@@ -572,26 +581,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
             s.slimit[pos] = s.load[r] - before;
         }
     }
-    // ranks that can receive at some quota tried (a spare slot, load below
-    // Qmax), as keys (load << rbits | rank), compacted in rank order then
-    // placed by their rank among the keys (distinct, so the order is strict)
-    {
-        const int per = (R + kPlanBlock - 1) / kPlanBlock;
-        const int b = tid * per;
-        const int r_end = (b + per < R) ? b + per : R;
-        int local = 0;
-        for (int r = b; r < r_end; ++r) local += (S > 0 && s.load[r] < Qmax);
-        int n;
-        int pos = plan_block_sum(local, wsum, n);
-        for (int r = b; r < r_end; ++r)
-            if (S > 0 && s.load[r] < Qmax)
-                s.dkey[pos++] = static_cast<int32_t>(
-                    (static_cast<uint32_t>(s.load[r]) << rbits) |
-                    static_cast<uint32_t>(r));
-        if (tid == 0) s_nd = n;
-    }
-    __syncthreads();
-    const int nd = s_nd;
+    // the receiving ranks placed by their rank among the keys (distinct,
+    // so the order is strict)
     for (int i0 = 0; i0 < nd; i0 += kPlanBlock / kSplit) {
         const int i = i0 + tid / kSplit;
         const int q = tid % kSplit;
