@@ -5,7 +5,8 @@
 // reduction reads the master and each replica and writes the master; the
 // gather reads a row once and writes it k times. The probe times a 1:1 copy,
 // a 1:2 fan-out, a 3:1 sum, read-only and write-only streams, each with
-// 16-byte vectors over a persistent grid, and prints GB/s per pattern.
+// 16-byte vectors over a persistent grid, and prints GB/s per pattern; then
+// the rate of non-returning LDS atomic adds per cycle per CU.
 //
 // Build: hipcc --offload-arch=gfx950 -O3 -std=c++17 hbm_probe.hip -o hbm_probe
 // Every index stays below the buffer's vector count (chunk loops are bounded
@@ -77,6 +78,32 @@ __global__ __launch_bounds__(256) void k_write(u32x4 *out, long n16) {
     }
 }
 
+// LDS atomic throughput: each thread issues kLdsIters non-returning adds
+// into a 2048-word LDS array, at hashed (random) or lane-linear addresses;
+// every address is masked into the array.
+constexpr int kLdsIters = 2048;
+template <bool kRandom>
+__global__ __launch_bounds__(256) void k_lds_add(unsigned *out) {
+    __shared__ unsigned a[2048];
+    for (int i = threadIdx.x; i < 2048; i += 256) a[i] = 0;
+    __syncthreads();
+    unsigned x = threadIdx.x * 2654435761u + blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    for (int i = 0; i < kLdsIters; ++i) {
+        unsigned addr;
+        if (kRandom) {
+            x = x * 1664525u + 1013904223u;
+            addr = (x >> 8) & 2047u;
+        } else {
+            addr = static_cast<unsigned>(lane + 64 * (i & 31)) & 2047u;
+        }
+        __hip_atomic_fetch_add(&a[addr], 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = a[5];
+}
+
 int main() {
     const long bytes = 1L << 30;            // per buffer, 4x the cache
     const long n16 = bytes / 16;
@@ -128,6 +155,32 @@ int main() {
         })) return 1;
     if (timed("hipMemcpyAsync device to device", 2.0 * bytes, [&] {
             (void)hipMemcpyAsync(buf[3], buf[0], bytes, hipMemcpyDeviceToDevice, 0);
+        })) return 1;
+    // LDS atomics: adds per cycle per CU at the device clock
+    int clock_khz = 0;
+    CHECK(hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeClockRate, dev));
+    const int lgrid = ncu * 8;
+    auto lds = [&](const char *name, auto launch) -> int {
+        launch();
+        CHECK(hipDeviceSynchronize());
+        CHECK(hipEventRecord(e0, 0));
+        for (int r = 0; r < 5; ++r) launch();
+        CHECK(hipEventRecord(e1, 0));
+        CHECK(hipEventSynchronize(e1));
+        float ms = 0;
+        CHECK(hipEventElapsedTime(&ms, e0, e1));
+        const double adds = double(lgrid) * 256 * kLdsIters;
+        const double per_s = adds / (ms / 5 * 1e-3);
+        std::printf("%-34s %9.2f adds/cycle/CU (%d CUs, %d MHz)\n", name,
+                    per_s / (clock_khz * 1e3) / ncu, ncu, clock_khz / 1000);
+        return 0;
+    };
+    unsigned *sink = reinterpret_cast<unsigned *>(buf[3]);
+    if (lds("LDS atomic add, random addresses", [&] {
+            hipLaunchKernelGGL(k_lds_add<true>, dim3(lgrid), dim3(256), 0, 0, sink);
+        })) return 1;
+    if (lds("LDS atomic add, lane-linear", [&] {
+            hipLaunchKernelGGL(k_lds_add<false>, dim3(lgrid), dim3(256), 0, 0, sink);
         })) return 1;
     return 0;
 }
