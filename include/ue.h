@@ -29,8 +29,13 @@
  *  - The return value is UE_OK (0) or a negative ue_status. Every argument
  *    is validated before anything is launched or written: a refused call
  *    leaves all outputs untouched. The reason is in ue_last_error().
- *  - A context is not thread-safe: use one context per concurrent stream.
- *    Calls on one context must not overlap in time on different streams.
+ *  - A context is not thread-safe: one host thread at a time. Its routing
+ *    calls (ue_load, ue_plan, ue_reroute, ue_rebalance) use the context's
+ *    workspace and must not overlap one another in time on different
+ *    streams. ue_weight_sync, ue_grad_reduce and ue_gather_rows use no
+ *    workspace and may run on another stream beside them (the next layer's
+ *    rebalance beside this layer's sync), while kernel timing is off and
+ *    the registered tables are not replaced meanwhile.
  *  - All shapes are int32; the number of assignments per layer, T*k, must
  *    stay below 2^30.
  */
