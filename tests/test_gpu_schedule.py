@@ -185,3 +185,28 @@ def test_graph_replay_rebalance_and_sync():
         counts, _ = oracle.load(routing, E)
         pl = oracle.plan(counts[0], R, S, ue.PLAN_BEST_FIT, ue.QUOTA_SEARCH)
         check_replicas(pl, mw, sw, NS, N)
+
+
+def test_graph_replay_batched_layers():
+    """ue_rebalance over several layers (which forks onto the context's
+    second stream and joins again) captured once and replayed on fresh
+    routing, every layer against the oracle."""
+    E, R, S, k, T, L = 64, 8, 2, 8, 3001, 9
+    ctx = ue.Context(E, R, S, k, T, L, device=DEV)
+    outs = routing_outputs(ctx, L, T)
+    rng = np.random.default_rng(9)
+    cases = [np.stack([pins.random_routing(rng, T, E, k, s)
+                       for s in rng.uniform(0.3, 2.2, L)]) for _ in range(3)]
+    static = torch.from_numpy(cases[0]).to(DEV)
+    ue.ue_rebalance(ctx, static, **outs)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ue.ue_rebalance(ctx, static, **outs)
+    for i, routing in enumerate(cases[1:] + cases[:1]):
+        say("batched graph replay", i)
+        static.copy_(torch.from_numpy(routing))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        compare_with_oracle(as_result(ctx, outs), routing, E, R, S)
