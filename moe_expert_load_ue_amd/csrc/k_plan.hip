@@ -16,20 +16,28 @@
 //   the least-loaded rank's headroom, it goes whole to the eligible rank
 //   with the smallest headroom that still holds it (ties: lowest id), so
 //   partly filled ranks close up instead of many ranks each taking a bit.
+//   The quota search (also per context) makes the same plan at the quotas
+//   Q0 + j * ceil(Q0 / 256), j = 0..63, in order, and keeps the first that
+//   leaves nothing over (with none, Q0 stands): the pages call the
+//   scheduler quota-driven without saying how the quota is set, and one
+//   spare slot per rank leaves too little room at Q0 itself.
 //
-// Layout of the work:
-//   A. all 256 threads: counts and rank loads into LDS, the quota, the
-//      candidate list (compacted in id order, then ranked by comparison
-//      counting, which is exact and needs no sort network);
-//   B. wave 0 alone: the sequential spill loop, in scalar registers. The
+// Layout of the work (1024 threads):
+//   A. all threads: counts and rank loads into LDS, Q0, the candidate list
+//      and the list of ranks that can receive (compacted together by one
+//      scan, then each ranked by comparison counting, four threads per
+//      item: exact, and no sort network);
+//   B. one wave per greedy pass, with the pass's state in registers. The
 //      least-loaded eligible rank is the smaller of two minima: the next
-//      entry of the list of ranks eligible at the start, sorted once by
-//      (load, id) in part A (such a rank has received nothing yet, so its
-//      key is unchanged), and the smallest key among ranks that received a
-//      chunk and are still eligible, held by their owner lanes and reduced
-//      with DPP only while that set is non-empty (never with one spare slot
-//      per rank, where a destination fills its only slot);
-//   C. all threads: replica table (CSR) and slot tables by prefix sums.
+//      entry of the receiving list, sorted once by (load, id) in part A
+//      (such a rank has received nothing yet, so its key is unchanged), and
+//      the smallest key among ranks that received a chunk and are still
+//      eligible, held by their owner lanes and reduced with DPP only while
+//      that set is non-empty (never with one spare slot per rank, where a
+//      destination fills its only slot). The fixed quota takes one pass on
+//      wave 0; the search runs 16 quotas at a time, one per wave;
+//   C. all threads: replica table (CSR) and slot tables by one three-way
+//      scan.
 // Everything is integer and deterministic; the result does not depend on
 // scheduling.
 #include "ue_internal.h"
@@ -194,8 +202,8 @@ __device__ __forceinline__ int count_below(const int32_t *list, int n,
 }
 
 // The spill loop at quota Q, run by one wave. With `write` it records the
-// chunks in LDS; without, it only finds whether the plan runs out (the
-// quota search runs it so, one quota per wave).
+// chunks in LDS (a search pass into a region of its own, when LDS allows
+// one per wave); without, it only finds whether the plan runs out.
 //  - Candidate c (in order) moves A_c = min(count, its home rank's excess
 //    over Q left by the rank's earlier candidates) = clamp(limit_c - Q, 0,
 //    count_c), where limit_c = rank load - counts of the rank's earlier
