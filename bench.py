@@ -7,15 +7,21 @@ reroute (physical routing, per-rank counts, stable dispatch permutation and
 its inverse). Inputs are seeded synthetic routing, resident in HBM before
 timing. ``value`` is routed assignments per second over the whole job.
 
-The same run also measures, each on its own workload: the large-EP
-rebalance latency (R=256, T=262144, one layer); replica weight sync and
+The same run also measures, each on its own workload: the same rebalance
+under the other planner rules (best fit, and each rule with the quota
+search), with the balance each reaches; the large-EP rebalance latency
+(R=256, T=262144, one layer) under every rule; replica weight sync and
 gradient reduction on 32 DeepSeek-V3 experts with 64 replica buffers (GB/s
 and fraction of the 8 TB/s HBM peak, algorithmic bytes); the dispatch gather
-of one pipeline microbatch ([131072, 4096] bf16 -> [1048576, 4096]); and the
-oracle on the host as the CPU baseline.
+of one pipeline microbatch ([131072, 4096] bf16 -> [1048576, 4096]); the
+per-layer schedule (rebalance, plan-driven sync, gather) of four dsv3
+layers with real expert sizes, on one and two streams, and a graph replay
+of the single-layer rebalance; the balance that plans made from earlier
+loads reach (pipeline drift, dsv3 at a later step); and the oracle on the
+host as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
-       [--no-cpu] [--only rebalance|stream|gather|large_ep]
+       [--no-cpu] [--only rebalance|large_ep|stale|schedule|stream|gather]
 """
 from __future__ import annotations
 
