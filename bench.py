@@ -101,10 +101,33 @@ def phase_times(rb, steps):
     for _ in range(steps):
         rb.step()
         ms = ue.ue_kernel_times(rb.ctx)
+        assert len(ms) == len(t), "three kernels per rebalance"
         for name, v in zip(t, ms):
             t[name].append(v)
     ue.ue_set_timing(rb.ctx, False)
     return {k: statistics.mean(v) for k, v in t.items()}
+
+
+def cold_times(rb, reps=20):
+    """Rebalance time with the device-wide cache flushed before each call
+    (a 1 GiB buffer written in between): the routing then comes from HBM,
+    not from where the gate just wrote it. Median, p10, p90 in us."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=rb.routing.device)
+    out = []
+    for i in range(reps + 2):
+        flush.fill_(float(i))
+        e0, e1 = events(2)
+        e0.record()
+        rb.step()
+        e1.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            out.append(e0.elapsed_time(e1) * 1000.0)
+    out.sort()
+    del flush
+    return [round(out[len(out) // 10], 2), round(out[len(out) // 2], 2),
+            round(out[9 * len(out) // 10], 2)]
 
 
 def imbalance(rb, cfg):
@@ -135,6 +158,7 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     log(f"dsv3: timing {steps} steps after {warmup} warmup")
     ms = time_steps(rb.step, steps, warmup)
     phases = phase_times(rb, max(steps, 10))
+    rb.cold = cold_times(rb)
     single = Rebalance(ue, cfg, routing[:1].contiguous(), dev)
     ms_one = time_steps(single.step, 50, 10)
     return cfg, rb, ms, phases, ms_one
@@ -589,6 +613,8 @@ def main():
                                  round(ms * 1000.0 / L, 3),
                              "dsv3_single_layer": round(ms_one * 1000.0, 2)},
         "kernel_us": {k: round(v * 1000.0, 2) for k, v in phases.items()},
+        "kernels_per_rebalance": len(phases),
+        "us_per_rebalance_cold_p10_p50_p90": rb.cold,
         "roofline": {"bound": "hbm", "kernel": "k_reroute",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),

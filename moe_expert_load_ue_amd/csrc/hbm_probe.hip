@@ -156,6 +156,13 @@ int main() {
     if (timed("hipMemcpyAsync device to device", 2.0 * bytes, [&] {
             (void)hipMemcpyAsync(buf[3], buf[0], bytes, hipMemcpyDeviceToDevice, 0);
         })) return 1;
+    // what the device reports of its memory (the transfers per clock are
+    // not reported, so no peak is derived here)
+    int mem_khz = 0, bus_bits = 0;
+    CHECK(hipDeviceGetAttribute(&mem_khz, hipDeviceAttributeMemoryClockRate, dev));
+    CHECK(hipDeviceGetAttribute(&bus_bits, hipDeviceAttributeMemoryBusWidth, dev));
+    std::printf("%-34s memory clock %d kHz, bus %d bits\n",
+                "device-reported memory", mem_khz, bus_bits);
     // LDS atomics: adds per cycle per CU at the device clock
     int clock_khz = 0;
     CHECK(hipDeviceGetAttribute(&clock_khz, hipDeviceAttributeClockRate, dev));
