@@ -474,19 +474,32 @@ def cpu_baseline(routing, cfg, min_seconds=10.0):
     import oracle
     r = routing.cpu().numpy()
     L = r.shape[0]
-    passes, dt = 0, 0.0
-    while dt < min_seconds:
+    r3 = r.reshape(L, 1, -1)
+    flat = r.reshape(L, -1)
+    passes, t = 0, {"load": 0.0, "plan": 0.0, "reroute": 0.0}
+    while sum(t.values()) < min_seconds:
         t0 = time.perf_counter()
-        oracle.rebalance(r, cfg.experts, cfg.ranks, cfg.spare)
-        dt += time.perf_counter() - t0
+        counts, _ = oracle.load(r3, cfg.experts)
+        t1 = time.perf_counter()
+        pls = [oracle.plan(counts[l], cfg.ranks, cfg.spare) for l in range(L)]
+        t2 = time.perf_counter()
+        for l in range(L):
+            oracle.reroute(flat[l], pls[l])
+        t3 = time.perf_counter()
+        t["load"] += t1 - t0
+        t["plan"] += t2 - t1
+        t["reroute"] += t3 - t2
         passes += 1
-    n = passes * L * cfg.assignments
+    dt = sum(t.values())
+    n = passes * r.size
     return {"value": n / dt, "unit": "assignments/s", "cores": 1,
             "kind": "oracle",
             "sample": f"{passes} passes over all {L} dsv3 layers "
                       f"({n} assignments), load+plan+reroute, {dt:.1f} s "
                       f"on one host thread of {os.cpu_count()}",
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2),
+            "ms_per_pass": {k: round(v / passes * 1000.0, 2)
+                            for k, v in t.items()}}
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
