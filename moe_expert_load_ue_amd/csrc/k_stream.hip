@@ -15,7 +15,9 @@
 // reduction loads the master chunk and each replica chunk in table order
 // and adds them left to right in fp32 (round to nearest even, no
 // reassociation, no packed fp32 instructions). The gather reads each token
-// row once and writes it to the k dispatch positions of that token.
+// row once and writes it to the k dispatch positions of that token. Loads
+// are nontemporal; so are the stores of sync and reduction, while the
+// gather's stores are plain (measured 2.5% faster for its 1 : 8 mix).
 #include "ue_internal.h"
 
 namespace ue {
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(
 #pragma unroll
                 for (int i = 0; i < kGatherVec; ++i) {
                     const int64_t idx = v0 + i * 64 + lane;
-                    if (idx < nvec) __builtin_nontemporal_store(v[i], dst + idx);
+                    if (idx < nvec) dst[idx] = v[i];
                 }
             }
         }
