@@ -68,7 +68,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     int32_t *gcnt = lds + 2 * kSub * EH + (G * g.E + 1) / 2;  // [E]
     int32_t *excl = gcnt + g.E;            // [E] counts of earlier groups
     __shared__ uint32_t s_ticket, s_epoch;
-    __shared__ int wsum[kWaves];
+    __shared__ int wsum[kWaves], wany[kWaves];
 
     const int E = g.E;
     const int layer = blockIdx.y;
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_groups * E;
     const bool bad = tile_lookback(st, grp, E, s_epoch, gcnt, excl,
                                    g.spin_limit);
-    const int poisoned = __syncthreads_or(bad);
+    const int poisoned = block_any(bad, wany);
 
     // per tile of the group: count of each expert in all earlier tiles
     int32_t *tp = g.tile_prefix +

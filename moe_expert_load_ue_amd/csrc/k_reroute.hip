@@ -75,14 +75,16 @@ __device__ __forceinline__ T *at(T *p, int i) {
 
 // Bitmap path: expert e's token bitmap is words [e*Wp, e*Wp + W), with an
 // odd stride Wp so that neighbouring experts fall in other banks; the
-// popcount prefix of each word (at most one tile's tokens, so 16 bits) sits
-// at the same index of a second, 16-bit array.
+// popcount prefix of each word follows in a second array: one byte per
+// word (rows of W) when at most 8 words per expert keep every prefix below
+// 256, else 16 bits per word at the words' own indices.
 __host__ __device__ __forceinline__ int bm_stride(int W) { return W | 1; }
+__host__ __device__ __forceinline__ bool bm_pre8(int W) { return W <= 8; }
 
-// Ints of the bitmap region (words, then the 16-bit prefixes).
+// Ints of the bitmap region (words, then the prefixes).
 __host__ __device__ __forceinline__ int bitmap_ints(int E, int W) {
     const int n = E * bm_stride(W);
-    return n + (n + 1) / 2;
+    return n + (bm_pre8(W) ? (E * W + 3) / 4 : (n + 1) / 2);
 }
 
 // Largest bitmap region (ints); beyond it, the configuration ranks by
@@ -115,7 +117,7 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
 template <bool kAfterLoad>
 __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
-    __shared__ int wsum[kWaves];
+    __shared__ int wsum[kWaves], wany[kWaves];
     __shared__ uint32_t s_ticket, s_epoch;
 
     const int E = g.E, P = g.P, R = g.R;
@@ -135,16 +137,14 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     int32_t *area = lds;
     int4 *einfo = reinterpret_cast<int4 *>(area + region_a_ints(E, W));
     int32_t *tcount = reinterpret_cast<int32_t *>(einfo + E);
-    int32_t *torder = tcount + E;
-    int32_t *tbase = torder + E;
+    int32_t *tbase = tcount + E;
     int32_t *rep_off = tbase + E;
     int32_t *rep_slot = rep_off + E + 1;
     int32_t *rep_hi = rep_slot + P;   // capacity prefix: end of each replica
     int32_t *slot_off = rep_hi + P;
-    int32_t *rank_hist = slot_off + P;
     // the carve-up must fit the launch's LDS (checked, not assumed); a
     // mismatch poisons the layer's fault count rather than pass silently
-    if (static_cast<size_t>(rank_hist + R - lds) * 4 > g.lds_bytes) {
+    if (static_cast<size_t>(slot_off + P - lds) * 4 > g.lds_bytes) {
         if (tid == 0 && blockIdx.x == 0 && g.faults) g.faults[layer] = kPoisonBit;
         return;
     }
@@ -213,7 +213,6 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
     }
     const int32_t *pl = g.placement + static_cast<int64_t>(layer) * g.lay.words;
-    for (int r = tid; r < R; r += kBlock) rank_hist[r] = 0;
     // The table is read as the planner wrote it, with every index clamped,
     // so a corrupt block can only produce faults.
     for (int e = tid; e <= E; e += kBlock) {
@@ -229,7 +228,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
     const bool bitmap = W > 0;
     uint32_t *bm = reinterpret_cast<uint32_t *>(area);          // [E][Wp]
-    uint16_t *bpre = reinterpret_cast<uint16_t *>(area + E * Wp);  // [E][Wp]
+    const bool pre8 = bm_pre8(W);
+    uint8_t *bpre8 = reinterpret_cast<uint8_t *>(area + E * Wp);    // [E][W]
+    uint16_t *bpre16 = reinterpret_cast<uint16_t *>(area + E * Wp); // [E][Wp]
     if (bitmap)
         for (int i = tid; i < E * Wp; i += kBlock) bm[i] = 0u;
     __syncthreads();
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         }
     }
     if (kAfterLoad && bitmap) __syncthreads();
-    int use_match = !bitmap || (!kAfterLoad && __syncthreads_or(dup));
+    int use_match = !bitmap || (!kAfterLoad && block_any(dup, wany));
     if (!use_match) {
         // prefix of popcounts over each expert's words (read in batches so
         // the reads overlap); tile counts, checked against the load's
@@ -344,7 +345,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             const int e = tid + q * kBlock;
             if (e >= E) break;
             const uint32_t *row = bm + e * Wp;
-            uint16_t *prow = bpre + e * Wp;
+            uint16_t *prow = bpre16 + e * Wp;
+            uint8_t *prow8 = bpre8 + e * W;
             int run = 0;
             for (int i0 = 0; i0 < W; i0 += 8) {
                 uint32_t bits[8];
@@ -353,15 +355,17 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                     bits[j] = i0 + j < W ? row[i0 + j] : 0u;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if (i0 + j < W) prow[i0 + j] = static_cast<uint16_t>(run);
+                    if (i0 + j < W) {
+                        if (pre8) prow8[i0 + j] = static_cast<uint8_t>(run);
+                        else prow[i0 + j] = static_cast<uint16_t>(run);
+                    }
                     run += __builtin_popcount(bits[j]);
                 }
             }
             tcount[e] = run;
-            torder[e] = run;
             if (kAfterLoad) dup |= run != pre_next[q] - pre_reg[q];
         }
-        if (kAfterLoad) use_match = __syncthreads_or(dup);
+        if (kAfterLoad) use_match = block_any(dup, wany);
         else __syncthreads();
     }
     if (!use_match) {
@@ -369,9 +373,12 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
             const int tl = rank[i];
-            const int word = (id >= 0 ? id : 0) * Wp + (tl >> 5);
+            const int e = id >= 0 ? id : 0;
+            const int word = e * Wp + (tl >> 5);
             const uint32_t below = (1u << (tl & 31)) - 1u;
-            rank[i] = bpre[word] + __builtin_popcount(bm[word] & below);
+            const int pre = pre8 ? static_cast<int>(bpre8[e * W + (tl >> 5)])
+                                 : static_cast<int>(bpre16[word]);
+            rank[i] = pre + __builtin_popcount(bm[word] & below);
         }
     } else {
         // matching path: ranks within rounds of 64 consecutive items
@@ -412,7 +419,6 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 run += c;
             }
             tcount[e] = run;
-            torder[e] = run;
         }
         __syncthreads();
 #pragma unroll
@@ -422,19 +428,19 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
 
     // ---- 2. the tile's own (expert, j) order --------------------------------
     __syncthreads();
+    // (the first field of each expert's record; the total is the number
+    // of valid items in the tile)
+    int n_valid;
     {
         const int per = (E + kBlock - 1) / kBlock;
         const int b = tid * per;
         const int eend = (b + per < E) ? b + per : E;
         int local = 0;
-        for (int e = b; e < eend; ++e) local += torder[e];
-        int total;
-        int run = block_exclusive_sum(local, wsum, total);
+        for (int e = b; e < eend; ++e) local += tcount[e];
+        int run = block_exclusive_sum(local, wsum, n_valid);
         for (int e = b; e < eend; ++e) {
-            const int c = torder[e];
-            torder[e] = run;
-            if (kAfterLoad) einfo[e].x = run;
-            run += c;
+            einfo[e].x = run;
+            run += tcount[e];
         }
     }
 
@@ -448,7 +454,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
         const bool bad = tile_lookback(st, tile, E, epoch, tcount, tbase,
                                        g.spin_limit);
-        poisoned = __syncthreads_or(bad);
+        poisoned = block_any(bad, wany);
     }
 
     // ---- 4. outputs ---------------------------------------------------------
@@ -471,7 +477,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                     }
                 }
             }
-            einfo[e] = int4{torder[e], lim, q, pos0};
+            einfo[e].y = lim;
+            einfo[e].z = q;
+            einfo[e].w = pos0;
         }
         __syncthreads();
     }
@@ -527,7 +535,6 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     __syncthreads();
     // perm in the tile's (expert, j) order: each entry's dispatch position
     // again from its expert's fast path (or the replica walk)
-    const int n_valid = torder[E - 1] + tcount[E - 1];
     for (int s2 = tid; s2 < n_valid; s2 += kBlock) {
         const uint32_t v = stage[s2];
         const int e = static_cast<int>(v >> 11);
@@ -541,6 +548,11 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
     if (tile != g.tiles - 1) return;
+    // the per-rank histogram takes region A once the staged entries are read
+    __syncthreads();
+    int32_t *rank_hist = area;
+    for (int r = tid; r < R; r += kBlock) rank_hist[r] = 0;
+    __syncthreads();
     // Assignments j in [lo, top) of a replica land at slot_off + (j - lo);
     // those whose position falls outside [0, A) (a plan made for other
     // counts) are faults like those beyond the expert's capacity.
@@ -577,7 +589,12 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
 }
 
 // Largest number of tokens that kRerouteTile consecutive assignments touch.
-int tile_tokens(int k) { return (kRerouteTile - 1) / k + 2; }
+// (a tile of whole tokens when k divides the tile size, since tiles start
+// at multiples of it)
+int tile_tokens(int k) {
+    return kRerouteTile % k == 0 ? kRerouteTile / k
+                                 : (kRerouteTile - 1) / k + 2;
+}
 
 }  // namespace
 
@@ -589,10 +606,11 @@ int reroute_bitmap_words(int E, int k) {
 
 size_t reroute_lds_bytes(int E, int R, int P, int k) {
     const int W = reroute_bitmap_words(E, k);
-    // region A; einfo (4 words per expert), tcount, torder, tbase;
-    // rep_off (+1); three P-sized tables; the rank histogram
+    // region A (which also takes the last tile's rank histogram); einfo
+    // (4 words per expert), tcount, tbase, rep_off (+1); three P-sized
+    // tables
     return sizeof(int32_t) * (static_cast<size_t>(region_a_ints(E, W)) +
-                              static_cast<size_t>(8) * E + 1 + 3 * P + R);
+                              static_cast<size_t>(7) * E + 1 + 3 * P);
 }
 
 hipError_t reroute_prepare(size_t lds_bytes) {

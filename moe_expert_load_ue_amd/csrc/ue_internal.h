@@ -202,6 +202,22 @@ __device__ __forceinline__ int block_exclusive_sum(int v, int *wsum,
     return before + x - v;
 }
 
+// Whether `pred` holds on any thread of the workgroup; `wany` holds one
+// int per wave. (The same as __syncthreads_or, without the 256 bytes of
+// static LDS that the library's version claims, which can cost a
+// workgroup per CU.)
+__device__ __forceinline__ bool block_any(bool pred, int *wany) {
+    const int w = threadIdx.x >> 6;
+    const bool mine = __ballot(pred) != 0;
+    if (lane_id() == 0) wany[w] = mine;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) any |= wany[i];
+    __syncthreads();
+    return any != 0;
+}
+
 // Set of lanes holding the same value as this lane, among lanes where
 // `valid`: one ballot per bit of the value (values < 2^bits).
 __device__ __forceinline__ uint64_t match_peers(int v, bool valid, int bits) {
