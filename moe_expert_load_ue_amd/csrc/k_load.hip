@@ -147,8 +147,9 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     __syncthreads();
 
     uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_groups * E;
-    const bool bad = tile_lookback(st, grp, E, s_epoch, gcnt, excl,
-                                   g.spin_limit);
+    const bool bad = tile_lookback(
+        st, grp, E, s_epoch, [&](int e) { return gcnt[e]; },
+        [&](int e, int v) { excl[e] = v; }, g.spin_limit);
     const int poisoned = block_any(bad, wany);
 
     // per tile of the group: count of each expert in all earlier tiles

@@ -135,10 +135,14 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int Wp = bm_stride(W);
 
     int32_t *area = lds;
+    // Per expert, in one 16-byte record: {the tile's own count, then its
+    // first position in the tile's (expert, j) order : 16 | how many of the
+    // tile's assignments stay in the replica covering the tile's first j,
+    // at most a tile : 16; that replica's slot; the dispatch position of
+    // that first j; the expert's assignments in earlier tiles (that j)}.
     int4 *einfo = reinterpret_cast<int4 *>(area + region_a_ints(E, W));
-    int32_t *tcount = reinterpret_cast<int32_t *>(einfo + E);
-    int32_t *tbase = tcount + E;
-    int32_t *rep_off = tbase + E;
+    uint16_t *ehalf = reinterpret_cast<uint16_t *>(einfo);   // [E][8]
+    int32_t *rep_off = reinterpret_cast<int32_t *>(einfo + E);
     int32_t *rep_slot = rep_off + E + 1;
     int32_t *rep_hi = rep_slot + P;   // capacity prefix: end of each replica
     int32_t *slot_off = rep_hi + P;
@@ -268,10 +272,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 }
             }
         }
-        if (kAfterLoad) {
-            tbase[e] = j0;
-            einfo[e] = int4{0, lim, slot, pos0};
-        }
+        if (kAfterLoad)
+            einfo[e] = int4{(lim < kRerouteTile ? lim : kRerouteTile) << 16,
+                            slot, pos0, j0};
     }
     // Physical slot and dispatch position of assignment j of expert e, or
     // -1 for both if no replica covers j (only a plan made for other counts
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                     run += __builtin_popcount(bits[j]);
                 }
             }
-            tcount[e] = run;
+            ehalf[8 * e] = static_cast<uint16_t>(run);
             if (kAfterLoad) dup |= run != pre_next[q] - pre_reg[q];
         }
         if (kAfterLoad) use_match = block_any(dup, wany);
@@ -387,9 +390,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         for (int i = tid; i < kWaves * E; i += kBlock) whist[i] = 0;
         __syncthreads();
         int32_t *my_hist = whist + w * E;
-        // rank[i] packs the leader's count before the round (13 bits; a
-        // tile holds kRerouteTile <= 4096 items), the rank below (6 bits)
-        // and the leader lane (6 bits) until the leaders' counts are fetched
+        // rank[i] is the leader's count before the round (fetched from the
+        // leader lane right after its add) plus the rank below
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
@@ -400,14 +402,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             if (valid && below == 0)
                 old = atomicAdd(&my_hist[id], __builtin_popcountll(peers));
             const int leader = peers ? __builtin_ctzll(peers) : lane;
-            rank[i] = (old & 0x1FFF) | static_cast<int>(below << 13) |
-                      (leader << 19);
-        }
-#pragma unroll
-        for (int i = 0; i < kRerouteItems; ++i) {
-            const int pk = rank[i];
-            const int before = __shfl(pk, (pk >> 19) & 63, 64) & 0x1FFF;
-            rank[i] = before + ((pk >> 13) & 63);
+            rank[i] = __shfl(old, leader, 64) + static_cast<int>(below);
         }
         __syncthreads();
         for (int e = tid; e < E; e += kBlock) {
@@ -418,7 +413,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 whist[v * E + e] = run;
                 run += c;
             }
-            tcount[e] = run;
+            ehalf[8 * e] = static_cast<uint16_t>(run);
         }
         __syncthreads();
 #pragma unroll
@@ -436,13 +431,19 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         const int b = tid * per;
         const int eend = (b + per < E) ? b + per : E;
         int local = 0;
-        for (int e = b; e < eend; ++e) local += tcount[e];
+        for (int e = b; e < eend; ++e) local += ehalf[8 * e];
         int run = block_exclusive_sum(local, wsum, n_valid);
         for (int e = b; e < eend; ++e) {
-            einfo[e].x = run;
-            run += tcount[e];
+            const int c = ehalf[8 * e];
+            ehalf[8 * e] = static_cast<uint16_t>(run);
+            run += c;
         }
     }
+    // the tile's count of expert e, from the order's starts
+    auto tile_count = [&](int e) {
+        const int next = e + 1 < E ? static_cast<int>(ehalf[8 * (e + 1)]) : n_valid;
+        return next - static_cast<int>(ehalf[8 * e]);
+    };
 
     // ---- 3. count of each expert in earlier tiles ---------------------------
     // (after a load it came with the prefixes, and the expert records are
@@ -452,34 +453,35 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         __syncthreads();
     } else {
         uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
-        const bool bad = tile_lookback(st, tile, E, epoch, tcount, tbase,
-                                       g.spin_limit);
+        __syncthreads();   // every start written
+        const bool bad = tile_lookback(
+            st, tile, E, epoch, tile_count,
+            [&](int e, int v) { einfo[e].w = v; }, g.spin_limit);
         poisoned = block_any(bad, wany);
     }
 
     // ---- 4. outputs ---------------------------------------------------------
-    // Per expert, in one 16-byte word: the tile's first position in its
-    // (expert, j) order, how many of the tile's assignments stay in the
-    // replica covering the tile's first j, that replica's slot and the
-    // dispatch position of that first j.
+    // (after a load the expert records were completed with the prefixes)
     if (!kAfterLoad) {
         for (int e = tid; e < E; e += kBlock) {
+            const int j0 = einfo[e].w;
             int q, pos0;
-            locate(e, tbase[e], q, pos0);
+            locate(e, j0, q, pos0);
             int lim = 0;
             if (q >= 0) {
                 // the covering replica's end: the first capacity prefix
                 // above j0
                 for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-                    if (tbase[e] < rep_hi[r]) {
-                        lim = rep_hi[r] - tbase[e];
+                    if (j0 < rep_hi[r]) {
+                        lim = rep_hi[r] - j0;
                         break;
                     }
                 }
             }
-            einfo[e].y = lim;
-            einfo[e].z = q;
-            einfo[e].w = pos0;
+            ehalf[8 * e + 1] =
+                static_cast<uint16_t>(lim < kRerouteTile ? lim : kRerouteTile);
+            einfo[e].y = q;
+            einfo[e].z = pos0;
         }
         __syncthreads();
     }
@@ -487,50 +489,33 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const bool full_tile = tile0 + kRerouteTile <= A;
     int32_t *phys_t = at(phys_l, aL);
     int32_t *inv_t = inv_l ? at(inv_l, aL) : nullptr;
-    int p_out[kRerouteItems], pos_out[kRerouteItems];
-    bool slow = false;
+    // Each item is finished in turn (its outputs stored at once) so that
+    // no per-item output array stays live across the tile. Items past the
+    // replica covering the tile's first j (or faults) walk the expert's
+    // capacity prefixes: rare, and skipped by every wave none of whose
+    // lanes needs it.
 #pragma unroll
     for (int i = 0; i < kRerouteItems; ++i) {
         const int id = ids[i];
         const int4 f = einfo[id >= 0 ? id : 0];
         const int jt = rank[i];                        // j within the tile
-        const bool fast = id >= 0 && jt < f.y;
-        slow |= id >= 0 && !fast;
-        p_out[i] = fast ? f.z : -1;
-        pos_out[i] = fast ? f.w + jt : -1;
-        stage[id >= 0 ? f.x + jt : kRerouteTile + tid] =
+        int p = -1, pos = -1;
+        if (id >= 0) {
+            if (jt < (f.x >> 16)) {
+                p = f.y;
+                pos = f.z + jt;
+            } else {
+                locate(id, f.w + jt, p, pos);
+            }
+        }
+        const bool ok = p >= 0 && pos >= 0 && pos < A;
+        if (full_tile || aL + 64 * i < A) {
+            __builtin_nontemporal_store(ok ? p : -1, phys_t + 64 * i);
+            if (inv_t) __builtin_nontemporal_store(ok ? pos : -1, inv_t + 64 * i);
+        }
+        stage[id >= 0 ? (f.x & 0xFFFF) + jt : kRerouteTile + tid] =
             static_cast<uint32_t>(64 * i + aL - tile0) |
             (static_cast<uint32_t>(id >= 0 ? id : 0) << 11);
-    }
-    // Items past the replica covering the tile's first j (or faults) walk
-    // the expert's capacity prefixes; rare, so skipped per wave.
-    if (__ballot(slow) != 0) {
-#pragma unroll
-        for (int i = 0; i < kRerouteItems; ++i) {
-            const int id = ids[i];
-            if (id < 0 || p_out[i] >= 0) continue;
-            locate(id, tbase[id] + rank[i], p_out[i], pos_out[i]);
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < kRerouteItems; ++i) {
-        const bool ok = p_out[i] >= 0 && pos_out[i] >= 0 && pos_out[i] < A;
-        p_out[i] = ok ? p_out[i] : -1;
-        pos_out[i] = ok ? pos_out[i] : -1;
-    }
-    if (full_tile) {
-#pragma unroll
-        for (int i = 0; i < kRerouteItems; ++i) {
-            __builtin_nontemporal_store(p_out[i], phys_t + 64 * i);
-            if (inv_t) __builtin_nontemporal_store(pos_out[i], inv_t + 64 * i);
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < kRerouteItems; ++i) {
-            if (aL + 64 * i >= A) continue;
-            __builtin_nontemporal_store(p_out[i], phys_t + 64 * i);
-            if (inv_t) __builtin_nontemporal_store(pos_out[i], inv_t + 64 * i);
-        }
     }
     __syncthreads();
     // perm in the tile's (expert, j) order: each entry's dispatch position
@@ -539,9 +524,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         const uint32_t v = stage[s2];
         const int e = static_cast<int>(v >> 11);
         const int4 f = einfo[e];
-        const int jt = s2 - f.x;
-        int p = f.z, pos = f.w + jt;
-        if (jt >= f.y) locate(e, tbase[e] + jt, p, pos);
+        const int jt = s2 - (f.x & 0xFFFF);
+        int p = f.y, pos = f.z + jt;
+        if (jt >= (f.x >> 16)) locate(e, f.w + jt, p, pos);
         if (p >= 0 && pos >= 0 && pos < A)
             *at(perm_l, pos) = tile0 + static_cast<int>(v & 2047u);
     }
@@ -558,7 +543,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     // counts) are faults like those beyond the expert's capacity.
     int part_valid = 0, part_over = 0;
     for (int e = tid; e < E; e += kBlock) {
-        const int total = tbase[e] + tcount[e];
+        const int total = einfo[e].w + tile_count(e);
         part_valid += total;
         int placed = 0, lo = 0;
         for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
@@ -606,11 +591,10 @@ int reroute_bitmap_words(int E, int k) {
 
 size_t reroute_lds_bytes(int E, int R, int P, int k) {
     const int W = reroute_bitmap_words(E, k);
-    // region A (which also takes the last tile's rank histogram); einfo
-    // (4 words per expert), tcount, tbase, rep_off (+1); three P-sized
-    // tables
+    // region A (which also takes the last tile's rank histogram); the
+    // expert records (4 words each); rep_off (+1); three P-sized tables
     return sizeof(int32_t) * (static_cast<size_t>(region_a_ints(E, W)) +
-                              static_cast<size_t>(7) * E + 1 + 3 * P);
+                              static_cast<size_t>(5) * E + 1 + 3 * P);
 }
 
 hipError_t reroute_prepare(size_t lds_bytes) {

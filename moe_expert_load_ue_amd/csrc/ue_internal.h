@@ -267,24 +267,25 @@ __device__ __forceinline__ uint64_t pack_state(uint32_t epoch, uint32_t flag,
 }
 
 // Every thread calls it. `st` points at the layer's words [tiles][nbins];
-// `cnt` (LDS) holds this tile's per-bin counts; on return `excl` (LDS) holds
-// the per-bin count of all earlier tiles (visible after the caller's
-// barrier). Returns true in a thread that saw a poisoned or timed-out wait.
+// `cnt(b)` gives this tile's count of bin b (from LDS); `set_excl(b, v)`
+// stores the count of bin b in all earlier tiles (in LDS, visible after the
+// caller's barrier); each thread passes only the bins b = tid + i * kBlock
+// to both. Returns true in a thread that saw a poisoned or timed-out wait.
+template <class Count, class SetExcl>
 __device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
                                               int nbins, uint32_t epoch,
-                                              const int32_t *cnt,
-                                              int32_t *excl,
+                                              Count cnt, SetExcl set_excl,
                                               uint32_t spin_limit) {
     const int tid = threadIdx.x;
     uint64_t *mine = st + static_cast<int64_t>(tile) * nbins;
     for (int b = tid; b < nbins; b += kBlock)
         atomic_store_agent(mine + b,
                            pack_state(epoch, tile == 0 ? kFlagPrefix : kFlagAgg,
-                                      static_cast<uint32_t>(cnt[b])));
+                                      static_cast<uint32_t>(cnt(b))));
     bool poisoned = false;
     for (int b = tid; b < nbins; b += kBlock) {
         if (tile == 0) {
-            excl[b] = 0;
+            set_excl(b, 0);
             continue;
         }
         // Poll a window of kLookbackWindow predecessors per round trip (the
@@ -334,8 +335,8 @@ __device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
         }
         atomic_store_agent(mine + b,
                            pack_state(epoch, bad ? kFlagPoison : kFlagPrefix,
-                                      acc + static_cast<uint32_t>(cnt[b])));
-        excl[b] = static_cast<int32_t>(acc);
+                                      acc + static_cast<uint32_t>(cnt(b))));
+        set_excl(b, static_cast<int32_t>(acc));
         poisoned |= bad;
     }
     return poisoned;
