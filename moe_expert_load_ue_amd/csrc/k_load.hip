@@ -39,7 +39,8 @@ struct LoadArgs {
     uint32_t spin_limit;
     uint64_t *state;           // [max_layers][max_groups][E]
     uint64_t *tick;            // [max_layers]
-    int32_t *tile_prefix;      // [max_layers][max_tiles + 1][E]
+    int32_t *group_base;       // [max_layers][max_groups][E]
+    uint16_t *tile_off;        // [max_layers][max_tiles + max_groups][E]
     int32_t *counts, *invalid;
 };
 
@@ -152,16 +153,25 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
         [&](int e, int v) { excl[e] = v; }, g.spin_limit);
     const int poisoned = block_any(bad, wany);
 
-    // per tile of the group: count of each expert in all earlier tiles
-    int32_t *tp = g.tile_prefix +
-                  static_cast<int64_t>(layer) * (g.max_tiles + 1) * E;
+    // the group's count of each expert in all earlier groups; per tile of
+    // the group, the count in the group's earlier tiles (16 bits: a group
+    // holds at most G * kLoadTile assignments), then the group's own count
+    // in the row after its last tile
+    static_assert(kLoadGroupWide * kLoadTile <= 65535, "16-bit tile offsets");
+    int32_t *gb = g.group_base +
+                  (static_cast<int64_t>(layer) * g.max_groups + grp) * E;
+    uint16_t *to = g.tile_off +
+                   (static_cast<int64_t>(layer) * (g.max_tiles + g.max_groups) +
+                    tile_first + grp) * E;
+    const int ntiles = g.tiles - tile_first < G ? g.tiles - tile_first : G;
     for (int e = tid; e < E; e += kBlock) {
-        int run = excl[e];
-        for (int s = 0; s < G; ++s) {
-            const int t = tile_first + s;
-            if (t < g.tiles) tp[static_cast<int64_t>(t) * E + e] = run;
+        gb[e] = excl[e];
+        int run = 0;
+        for (int s = 0; s < ntiles; ++s) {
+            to[s * E + e] = static_cast<uint16_t>(run);
             run += cnt[s * E + e];
         }
+        to[ntiles * E + e] = static_cast<uint16_t>(run);
     }
     if (grp != g.groups - 1) return;
 
@@ -171,7 +181,6 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     for (int e = tid; e < E; e += kBlock) {
         const int c = excl[e] + gcnt[e];
         out[e] = c;
-        tp[static_cast<int64_t>(g.tiles) * E + e] = c;   // row tiles: totals
         part += c;
     }
     int total;
@@ -192,15 +201,21 @@ static size_t load_lds_bytes_for(int E, int G) {
 
 size_t load_lds_bytes(int E) { return load_lds_bytes_for(E, kLoadGroupWide); }
 
+int load_group_tiles(const ue_ctx &c, int tiles, int L) {
+    // wide groups once they still give two workgroups per CU
+    const int wide_groups = (tiles + kLoadGroupWide - 1) / kLoadGroupWide;
+    return static_cast<int64_t>(wide_groups) * L >= 2 * c.num_cu
+               ? kLoadGroupWide
+               : kLoadGroup;
+}
+
 hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
                        int64_t A, int32_t *counts, int32_t *invalid,
                        hipStream_t s) {
     int tiles = static_cast<int>((A + kLoadTile - 1) / kLoadTile);
     if (tiles < 1) tiles = 1;
-    // wide groups once they still give two workgroups per CU
-    const int wide_groups = (tiles + kLoadGroupWide - 1) / kLoadGroupWide;
-    const bool wide = static_cast<int64_t>(wide_groups) * L >= 2 * c.num_cu;
-    const int G = wide ? kLoadGroupWide : kLoadGroup;
+    const int G = load_group_tiles(c, tiles, L);
+    const bool wide = G == kLoadGroupWide;
     const int groups = (tiles + G - 1) / G;
     LoadArgs g;
     g.routing = routing;
@@ -214,7 +229,8 @@ hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
     g.spin_limit = 1u << 22;
     g.state = c.load_state;
     g.tick = c.load_tick;
-    g.tile_prefix = c.tile_prefix;
+    g.group_base = c.group_base;
+    g.tile_off = c.tile_off;
     g.counts = counts;
     g.invalid = invalid;
     if (wide)

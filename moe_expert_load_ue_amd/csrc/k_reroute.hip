@@ -51,6 +51,7 @@ struct RerouteArgs {
     const int32_t *placement;
     int32_t A;                 // assignments per layer (< 2^30)
     int E, R, NS, P, k, ebits, tiles, max_tiles;
+    int load_group, max_groups;// the load's tiles per group; groups
     int bm_words;              // words per expert bitmap (0: no bitmap path)
     uint32_t spin_limit;       // bound on one lookback wait
     uint32_t lds_bytes;        // dynamic LDS the launch provides
@@ -58,7 +59,8 @@ struct RerouteArgs {
     int32_t *phys, *perm, *inv_perm;
     uint64_t *state;           // [max_layers][max_tiles][E] own lookback
     uint64_t *tick;            // [max_layers] own ticket and epoch
-    const int32_t *tile_prefix;// [max_layers][max_tiles + 1][E] from the load
+    const int32_t *group_base; // [max_layers][max_groups][E] from the load
+    const uint16_t *tile_off;  // [max_layers][max_tiles + max_groups][E]
     int32_t *rank_counts, *faults;
 };
 
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     const int A = g.A;
     constexpr int kPerThread = kMaxExperts / kBlock;
     int32_t ids[kRerouteItems];
-    int32_t pre_reg[kPerThread], pre_next[kPerThread];
+    int32_t pre_reg[kPerThread], cnt_reg[kPerThread];
     int tile = 0;
     // Item i of a lane is assignment aL + 64 i: each step of a wave covers
     // 64 consecutive assignments, so global reads and writes coalesce.
@@ -197,21 +199,31 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
             }
         }
     };
-    auto load_prefix = [&](int t, int32_t *dst) {
-        const int32_t *tp = g.tile_prefix +
-                            (static_cast<int64_t>(layer) * (g.max_tiles + 1) + t) * E;
+    // tile t's count of each expert in all earlier tiles, and in t itself:
+    // its group's base plus the tile's 16-bit offset in the group, and the
+    // next row's offset (the next tile's, or the group's own count)
+    auto load_prefix = [&](int t, int32_t *pre, int32_t *cnt) {
+        const int grp = t / g.load_group;
+        const int32_t *gb = g.group_base +
+                            (static_cast<int64_t>(layer) * g.max_groups + grp) * E;
+        const uint16_t *to = g.tile_off +
+                             (static_cast<int64_t>(layer) * (g.max_tiles + g.max_groups) +
+                              t + grp) * E;
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             const int e = tid + q * kBlock;
-            dst[q] = e < E ? tp[e] : 0;
+            const int b = e < E ? gb[e] : 0;
+            const int o0 = e < E ? to[e] : 0;
+            const int o1 = e < E ? to[E + e] : 0;
+            pre[q] = b + o0;
+            cnt[q] = o1 - o0;
         }
     };
     if (kAfterLoad) {
         tile = item % static_cast<int>(gridDim.x);
         if (tile >= g.tiles) return;
         load_ids(tile, ids);
-        load_prefix(tile, pre_reg);
-        load_prefix(tile + 1, pre_next);   // row tiles holds the totals
+        load_prefix(tile, pre_reg, cnt_reg);
         if (tid == 0) s_epoch = 0;
     } else if (tid == 0) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
@@ -366,7 +378,7 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 }
             }
             ehalf[8 * e] = static_cast<uint16_t>(run);
-            if (kAfterLoad) dup |= run != pre_next[q] - pre_reg[q];
+            if (kAfterLoad) dup |= run != cnt_reg[q];
         }
         if (kAfterLoad) use_match = block_any(dup, wany);
         else __syncthreads();
@@ -635,7 +647,10 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.inv_perm = inv_perm;
     g.state = c.scan_state;
     g.tick = c.rr_tick;
-    g.tile_prefix = c.tile_prefix;
+    g.group_base = c.group_base;
+    g.tile_off = c.tile_off;
+    g.load_group = load_group_tiles(c, tiles, L);
+    g.max_groups = c.max_load_groups;
     g.rank_counts = rank_counts;
     g.faults = faults;
     if (after_load) {

@@ -174,8 +174,13 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     };
     const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_groups * E);
     const size_t o_ltick = take(sizeof(uint64_t) * Lmax);
-    // per-tile expert prefixes: one row per tile plus the totals
-    const size_t o_tprefix = take(sizeof(int32_t) * Lmax * (rr_tiles + 1) * E);
+    // the load's prefixes: a base row per group of tiles and a 16-bit row
+    // per tile plus one per group (row t + g for tile t of group g, and row
+    // t + g + 1 after the group's last tile t), so below tiles + groups;
+    // groups of kLoadGroup tiles are the most numerous
+    const size_t o_gbase = take(sizeof(int32_t) * Lmax * ld_groups * E);
+    const size_t o_toff =
+        take(sizeof(uint16_t) * Lmax * (rr_tiles + ld_groups) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
     c->ws_bytes = off;
@@ -194,7 +199,8 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     char *b = static_cast<char *>(c->ws);
     c->load_state = reinterpret_cast<uint64_t *>(b + o_lstate);
     c->load_tick = reinterpret_cast<uint64_t *>(b + o_ltick);
-    c->tile_prefix = reinterpret_cast<int32_t *>(b + o_tprefix);
+    c->group_base = reinterpret_cast<int32_t *>(b + o_gbase);
+    c->tile_off = reinterpret_cast<uint16_t *>(b + o_toff);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
     *out = c;

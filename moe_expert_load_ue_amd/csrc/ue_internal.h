@@ -49,7 +49,13 @@ struct ue_ctx {
     int max_load_groups = 0;       // load tile groups of the largest layer
     uint64_t *load_state = nullptr;// [max_layers][max_load_groups][E]
     uint64_t *load_tick = nullptr; // [max_layers] {epoch:32 | ticket:32}
-    int32_t *tile_prefix = nullptr;// [max_layers][max_rr_tiles][E]
+    // the load's per-tile prefixes, in two parts: per group of tiles, the
+    // count of each expert in all earlier groups, and per tile the count
+    // in the group's earlier tiles (16 bits; each group also has a row
+    // after its last tile: the group's own counts). Tile t of group g has
+    // row t + g.
+    int32_t *group_base = nullptr; // [max_layers][max_load_groups][E]
+    uint16_t *tile_off = nullptr;  // [max_layers][max_rr_tiles + max_load_groups][E]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
 
@@ -108,6 +114,9 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
                               void *out, hipStream_t s);
 
 size_t load_lds_bytes(int E);
+// Tiles per load workgroup for a launch over L layers of `tiles` tiles
+// (the fused reroute finds its tile's prefix rows with it).
+int load_group_tiles(const ue_ctx &c, int tiles, int L);
 // per_wave: one chunk-record region per wave (the quota search keeps each
 // pass's chunks, so the chosen one needs no second pass).
 size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave);

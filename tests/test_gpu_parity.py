@@ -181,6 +181,25 @@ def test_duplicate_expert_in_token():
         compare_with_oracle(res, routing[None], E, R, S)
 
 
+@pytest.mark.parametrize("k", [8, 4, 3])
+def test_expert_in_every_token(k):
+    """One expert in every token: its rank within a tile reaches the tile's
+    last token, the largest per-word popcount prefix (one byte per word at
+    k = 8, 16 bits at k = 4 and k = 3, which does not divide the tile)."""
+    rng = np.random.default_rng(31 + k)
+    E, R, S, T = 64, 8, 2, 7000
+    routing = np.empty((T, k), np.int32)
+    for t in range(T):
+        routing[t] = np.concatenate(
+            [[5], rng.choice(np.delete(np.arange(E), 5), k - 1, replace=False)])
+        rng.shuffle(routing[t])
+    say(f"expert in every token: k={k}")
+    ctx = make_ctx(E, R, S, k, T)
+    for fused in (False, True):
+        res = gpu_rebalance(ctx, torch.from_numpy(routing[None]), fused=fused)
+        compare_with_oracle(res, routing[None], E, R, S)
+
+
 def test_kernel_times():
     cfg = W.CONFIGS["tiny"]
     routing = W.make_routing(cfg, device=DEV)
