@@ -357,6 +357,48 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
     cand.init(s.sorted, ncand);
     ccount.init(s.scount, ncand);
     climit.init(s.slimit, ncand);
+    if (RPL == 1 && S == 1 && !best_fit) {
+        // One spare slot per rank under the least-loaded rule: a rank that
+        // takes a chunk has no slot left, so nothing is held, nothing is
+        // taken out of order and the list is consumed strictly in order
+        // (the records so far are the list entries before di). With at
+        // most 64 ranks the list sits one entry per lane, and the prefix
+        // sums of its headrooms hold for the whole pass (below 2^31: at
+        // most R * Q), so each amount is placed with one ballot: the run
+        // from di ends at the first lane whose headroom sum since di
+        // reaches it; lanes before it fill to Q and that lane takes the
+        // rest. No lane reaching it means the list runs out.
+        const bool inl = lane < nd;
+        const uint32_t key = inl ? static_cast<uint32_t>(s.dsorted[lane]) : 0u;
+        const int h = inl ? Q - static_cast<int>(key >> rbits) : 0;
+        const int hsum = wave_inclusive_sum(h);
+        for (int c = 0; c < ncand; ++c) {
+            const int cnt = ccount.get(c);
+            const int over = climit.get(c) - Q;
+            const int rem = over <= 0 ? 0 : (cnt < over ? cnt : over);
+            if (rem == 0) continue;
+            const int e = cand.get(c);
+            const int base = di > 0 ? __builtin_amdgcn_readlane(hsum, di - 1) : 0;
+            const uint64_t hit = __ballot(inl && lane >= di && hsum - base >= rem);
+            const int last = hit ? __builtin_ctzll(hit) : nd - 1;
+            if (write && lane >= di && lane <= last && inl) {
+                const int at = nrec + (lane - di);
+                s.rec_e[at] = e;
+                s.rec_p[at] = static_cast<int>(key & rmask) * NS + N;
+                s.rec_m[at] = lane == last && hit ? rem - (hsum - h - base) : h;
+            }
+            const int taken = last >= di ? last - di + 1 : 0;
+            nrec += taken;
+            di += taken;
+            if (!hit) {
+                exhausted = 1;
+                break;
+            }
+        }
+        nrec_out = nrec;
+        exhausted_out = exhausted;
+        return;
+    }
     for (int c = 0; c < ncand && !exhausted; ++c) {
         const int e = cand.get(c);
         const int cnt = ccount.get(c);
