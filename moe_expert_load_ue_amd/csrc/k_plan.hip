@@ -357,42 +357,80 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
     cand.init(s.sorted, ncand);
     ccount.init(s.scount, ncand);
     climit.init(s.slimit, ncand);
-    if (RPL == 1 && S == 1 && !best_fit) {
-        // One spare slot per rank under the least-loaded rule: a rank that
-        // takes a chunk has no slot left, so nothing is held, nothing is
-        // taken out of order and the list is consumed strictly in order
-        // (the records so far are the list entries before di). With at
-        // most 64 ranks the list sits one entry per lane, and the prefix
-        // sums of its headrooms hold for the whole pass (below 2^31: at
-        // most R * Q), so each amount is placed with one ballot: the run
-        // from di ends at the first lane whose headroom sum since di
-        // reaches it; lanes before it fill to Q and that lane takes the
-        // rest. No lane reaching it means the list runs out.
+    if (RPL == 1 && S == 1) {
+        // One spare slot per rank and at most 64 ranks: a rank that takes a
+        // chunk has no slot left, so nothing is held; the list sits one
+        // entry per lane, with the prefix sums of the headrooms of the
+        // entries not taken out of order (below 2^31: at most R * Q). An
+        // amount is placed with one ballot: the run from di ends at the
+        // first lane whose headroom sum since di reaches it; the lanes
+        // before it fill to Q and that lane takes the rest, or under best
+        // fit, when the rest is below its headroom, the rest goes to the
+        // most loaded entry from there on that holds it (lowest id among
+        // equal loads), which leaves the list and the sums. No lane
+        // reaching it means the list runs out. Candidates are read 64 at a
+        // time and those with nothing to move are skipped with the ballot.
         const bool inl = lane < nd;
         const uint32_t key = inl ? static_cast<uint32_t>(s.dsorted[lane]) : 0u;
-        const int h = inl ? Q - static_cast<int>(key >> rbits) : 0;
-        const int hsum = wave_inclusive_sum(h);
-        for (int c = 0; c < ncand; ++c) {
-            const int cnt = ccount.get(c);
-            const int over = climit.get(c) - Q;
-            const int rem = over <= 0 ? 0 : (cnt < over ? cnt : over);
-            if (rem == 0) continue;
-            const int e = cand.get(c);
-            const int base = di > 0 ? __builtin_amdgcn_readlane(hsum, di - 1) : 0;
-            const uint64_t hit = __ballot(inl && lane >= di && hsum - base >= rem);
-            const int last = hit ? __builtin_ctzll(hit) : nd - 1;
-            if (write && lane >= di && lane <= last && inl) {
-                const int at = nrec + (lane - di);
-                s.rec_e[at] = e;
-                s.rec_p[at] = static_cast<int>(key & rmask) * NS + N;
-                s.rec_m[at] = lane == last && hit ? rem - (hsum - h - base) : h;
-            }
-            const int taken = last >= di ? last - di + 1 : 0;
-            nrec += taken;
-            di += taken;
-            if (!hit) {
-                exhausted = 1;
-                break;
+        const int L = static_cast<int>(key >> rbits);
+        const int h = inl ? Q - L : 0;
+        int hsum = wave_inclusive_sum(h);
+        bool gone = false;
+        for (int c0 = 0; c0 < ncand && !exhausted; c0 += 64) {
+            const int ci = c0 + lane;
+            const bool cv = ci < ncand;
+            const int over_l = cv ? s.slimit[ci] - Q : 0;
+            const int cnt_l = cv ? s.scount[ci] : 0;
+            const int rem_l = over_l <= 0 ? 0 : (cnt_l < over_l ? cnt_l : over_l);
+            const int e_l = cv ? s.sorted[ci] : 0;
+            uint64_t todo = __ballot(rem_l > 0);
+            while (todo) {
+                const int j = __builtin_ctzll(todo);
+                todo &= todo - 1;
+                const int rem = __builtin_amdgcn_readlane(rem_l, j);
+                const int e = __builtin_amdgcn_readlane(e_l, j);
+                const int base = di > 0 ? __builtin_amdgcn_readlane(hsum, di - 1) : 0;
+                const bool live = inl && !gone && lane >= di;
+                const uint64_t hit = __ballot(live && hsum - base >= rem);
+                const int hl = hit ? __builtin_ctzll(hit) : 64;
+                const int hh = hit ? __builtin_amdgcn_readlane(h, hl) : 0;
+                const int need =
+                    hit ? rem - (__builtin_amdgcn_readlane(hsum, hl) - hh - base) : 0;
+                const bool bf = hit && best_fit && need < hh;
+                const bool put = live && (lane < hl || (lane == hl && !bf));
+                const uint64_t puts = __ballot(put);
+                if (write && put) {
+                    const int at = nrec + static_cast<int>(mask_rank(puts));
+                    s.rec_e[at] = e;
+                    s.rec_p[at] = static_cast<int>(key & rmask) * NS + N;
+                    s.rec_m[at] = lane == hl ? need : h;
+                }
+                nrec += __builtin_popcountll(puts);
+                if (!hit) {
+                    exhausted = 1;
+                    break;
+                }
+                if (!bf) {
+                    di = hl + 1;
+                    continue;
+                }
+                di = hl;
+                const bool fits = inl && !gone && lane >= di && L <= Q - need;
+                const uint64_t bq = __ballot(fits);      // the hit lane fits
+                const int Lw = __builtin_amdgcn_readlane(L, 63 - __builtin_clzll(bq));
+                const int bi = __builtin_ctzll(__ballot(fits && L == Lw));
+                const int db = static_cast<int>(
+                    static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), bi)) &
+                    rmask);
+                if (write && lane == 0) {
+                    s.rec_e[nrec] = e;
+                    s.rec_p[nrec] = db * NS + N;
+                    s.rec_m[nrec] = need;
+                }
+                ++nrec;
+                const int hb = __builtin_amdgcn_readlane(h, bi);
+                hsum -= lane >= bi ? hb : 0;
+                gone = gone || lane == bi;
             }
         }
         nrec_out = nrec;
