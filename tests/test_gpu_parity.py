@@ -111,6 +111,32 @@ def test_many_spares_and_ranks(policy, quota_mode):
             compare_with_oracle(res, routing, E, R, S)
 
 
+@pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
+def test_one_spare_slot_up_to_64_ranks(policy, quota_mode):
+    """One spare slot per rank and at most 64 ranks, the planner's
+    one-ballot path: ranks from 1 to 64, skew from none to extreme (plans
+    that run out of slots, best-fit placements out of list order, no
+    receiving rank at all), several layers per call."""
+    rng = np.random.default_rng(777 + policy + 2 * quota_mode)
+    for it in range(24):
+        R = int(rng.choice([1, 2, 3, 7, 16, 31, 32, 33, 63, 64]))
+        N = int(rng.integers(1, 9))
+        E = R * N
+        if E > 1024:
+            continue
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.choice([0, 5, 700, 4096, 9001]))
+        L = int(rng.integers(1, 4))
+        routing = np.stack([pins.random_routing(rng, T, E, k,
+                                                float(rng.uniform(0, 3.5)))
+                            for _ in range(L)])
+        say(f"one slot {it}: E={E} R={R} k={k} T={T} L={L} policy={policy} "
+            f"quota_mode={quota_mode}")
+        ctx = make_ctx(E, R, 1, k, T, L, policy, quota_mode)
+        res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=True)
+        compare_with_oracle(res, routing, E, R, 1)
+
+
 def test_many_layers_ragged_wide_load_groups():
     """130 layers of 63 tiles each, the last one ragged: enough load groups
     (130 x 4 of 16 tiles) for the 16-tile groups on a 256-CU device, with a
