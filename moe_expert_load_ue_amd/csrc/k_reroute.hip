@@ -16,15 +16,17 @@
 //      tokens per expert in LDS (one LDS OR per item), takes a prefix of
 //      popcounts over each bitmap's words, and reads every rank back as
 //      prefix + popcount of the bits below the token. A token that names
-//      the same expert twice is seen when its second OR finds the bit set;
+//      the same expert twice is seen when its second OR finds the bit set
+//      (after a load: when the popcounts fall short of the tile's count);
 //      such a tile (and any configuration whose bitmaps do not fit) ranks by
 //      matching lanes with equal ids instead: one ballot per id bit within
 //      rounds of 64 consecutive items, and a per-wave counter per expert;
 //   2. scans the tile counts across experts (the tile's own sorted order);
 //   3. decoupled lookback over earlier tiles (ue_internal.h) gives the count
 //      of each expert before this tile; when the load kernel has just
-//      counted the same routing with the same tiles, the prefix it published
-//      for the previous tile is read instead (no ticket, no waiting);
+//      counted the same routing with the same tiles, the counts it published
+//      (its group's base plus the tile's offset in the group) are read
+//      instead (no ticket, no waiting);
 //   4. j = tile prefix + rank; the replica is found through a per-expert
 //      fast path (the replica covering the tile's first assignment of e and
 //      how many of the tile's assignments it still takes) or, for items that
@@ -99,7 +101,8 @@ static_assert(kRerouteTile <= 2048, "staged entries keep 11 bits of position");
 static_assert(kMaxExperts <= (1 << 20), "staged entries keep the expert above");
 
 // Size in ints of region A, shared in turn by the rank bitmaps (or the
-// per-wave counters of the matching path) and by the staged perm entries;
+// per-wave counters of the matching path), the staged perm entries and, in
+// the last tile, the per-rank histogram;
 // a multiple of 4 so that what follows stays 16-byte aligned. The rest of
 // the LDS (per-expert arrays and the replica table) follows it.
 __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
