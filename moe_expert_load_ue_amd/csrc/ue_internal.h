@@ -179,14 +179,17 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
     return a < c ? a : c;
 }
 
-// Inclusive sum over lanes below and including this one.
+// Inclusive sum over lanes below and including this one, by DPP lane
+// moves (no LDS round trip): shifts by 1, 2, 4 and 8 within each row of 16
+// lanes (a lane with no source adds 0), then the last lane of row 0 into
+// rows 1 and 3 and the last lane of row 1 into rows 2 and 3.
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
 }
 
