@@ -137,6 +137,14 @@ __device__ __forceinline__ void plan_block_sum3(int v[3], int *wsum3,
     }
 }
 
+// Sum over the four lanes of a quad (lanes 4q .. 4q + 3), in every one of
+// them: DPP quad permutations swapping neighbours, then pairs.
+__device__ __forceinline__ int quad_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+    x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+    return x;
+}
+
 // Entry c of an LDS list through a 64-entry window held one per lane:
 // readlane with a uniform index, one LDS read per 64 entries.
 struct ListWindow {
@@ -639,6 +647,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // (kSplit adjacent threads share a candidate, each comparing against
     // every kSplit-th other one; their sums meet through lane swaps)
     constexpr int kSplit = 4;
+    static_assert(kSplit == 4, "quad_sum joins the four threads of a candidate");
     const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
     for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
         const int i = i0 + tid / kSplit;
@@ -659,10 +668,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
                 before += (earlier && (o.x >> 16) == r) ? o.y : 0;
             }
         }
-        pos += __shfl_xor(pos, 1, 64);
-        pos += __shfl_xor(pos, 2, 64);
-        before += __shfl_xor(before, 1, 64);
-        before += __shfl_xor(before, 2, 64);
+        pos = quad_sum(pos);
+        before = quad_sum(before);
         if (act && q == 0) {
             s.sorted[pos] = e;
             s.scount[pos] = c;
@@ -682,8 +689,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
             for (int j = q; j < nd; j += kSplit)
                 pos += static_cast<uint32_t>(s.dkey[j]) < k;
         }
-        pos += __shfl_xor(pos, 1, 64);
-        pos += __shfl_xor(pos, 2, 64);
+        pos = quad_sum(pos);
         if (act && q == 0) s.dsorted[pos] = static_cast<int32_t>(k);
     }
     __syncthreads();
