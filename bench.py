@@ -499,7 +499,43 @@ def cpu_baseline(routing, cfg, min_seconds=10.0):
                       f"on one host thread of {os.cpu_count()}",
             "seconds": round(dt, 2),
             "ms_per_pass": {k: round(v / passes * 1000.0, 2)
-                            for k, v in t.items()}}
+                            for k, v in t.items()},
+            "streaming": cpu_streaming()}
+
+
+def cpu_streaming():
+    """The oracle's replica weight sync, gradient reduction and gather on
+    one host thread, each on a bounded sample of its workload (one
+    2048 x 7168 expert matrix with two replicas; 2048 tokens of 4096 bf16
+    features gathered for top-8), in algorithmic GB/s."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(4)
+    shape = (2048, 7168)
+    w = rng.integers(0, 1 << 16, size=shape, dtype=np.uint16)   # bf16 bits
+    g = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    reps = [(rng.standard_normal(shape) * 0.02).astype(np.float32)
+            for _ in range(2)]
+    T, k, H = 2048, 8, 4096
+    x = rng.integers(0, 1 << 16, size=(T, H), dtype=np.uint16)
+    perm = rng.permutation(T * k).astype(np.int32)
+    out = {}
+    for name, fn, nbytes in (
+            ("weight_sync", lambda: oracle.weight_sync(w, 2), 3 * w.nbytes),
+            ("grad_reduce", lambda: oracle.grad_reduce(g, reps),
+             4 * g.nbytes),
+            ("gather", lambda: oracle.gather(x, perm, k),
+             x.nbytes + T * k * H * 2)):
+        fn()
+        t0 = time.perf_counter()
+        for _ in range(3):
+            fn()
+        dt = (time.perf_counter() - t0) / 3
+        out[name + "_GB_per_s"] = round(nbytes / dt / 1e9, 2)
+    out["sample"] = ("one 2048x7168 matrix: bf16 master to 2 replicas, fp32 "
+                     "master + 2 replica gradients; gather of 2048 tokens x "
+                     "4096 bf16 for top-8; algorithmic bytes, one thread")
+    return out
 
 
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)),
