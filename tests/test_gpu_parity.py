@@ -112,15 +112,17 @@ def test_many_spares_and_ranks(policy, quota_mode):
 
 
 @pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
-def test_one_spare_slot_up_to_64_ranks(policy, quota_mode):
-    """One spare slot per rank and at most 64 ranks, the planner's
-    one-ballot path: ranks from 1 to 64, skew from none to extreme (plans
-    that run out of slots, best-fit placements out of list order, no
-    receiving rank at all), several layers per call."""
+def test_one_spare_slot_up_to_256_ranks(policy, quota_mode):
+    """One spare slot per rank, ranks from 1 to 256: the planner's
+    one-ballot path up to 64 ranks and its general loop above, with skew
+    from none to extreme (plans that run out of slots, best-fit placements
+    out of list order, no receiving rank at all), several layers per
+    call."""
     rng = np.random.default_rng(777 + policy + 2 * quota_mode)
-    for it in range(24):
-        R = int(rng.choice([1, 2, 3, 7, 16, 31, 32, 33, 63, 64]))
-        N = int(rng.integers(1, 9))
+    for it in range(32):
+        R = int(rng.choice([1, 2, 3, 7, 16, 31, 32, 33, 63, 64, 65, 100,
+                            128, 129, 200, 256]))
+        N = int(rng.integers(1, min(8, 1024 // R) + 1))
         E = R * N
         if E > 1024:
             continue
