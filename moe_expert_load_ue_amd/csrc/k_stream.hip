@@ -186,16 +186,24 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(
                 const int64_t idx = v0 + i * 64 + lane;
                 if (idx < nvec) v[i] = __builtin_nontemporal_load(src + idx);
             }
-            for (int j = 0; j < k; ++j) {
-                const int pos = inv_perm[static_cast<int64_t>(t) * k + j];
-                if (static_cast<uint64_t>(pos) >= static_cast<uint64_t>(n_pos))
-                    continue;
-                u32x4 *dst = reinterpret_cast<u32x4 *>(
-                    out + static_cast<int64_t>(pos) * row_bytes);
+            // the token's destinations, 64 at a time: one load per lane,
+            // then each broadcast from its lane, so that the row's stores
+            // do not wait on one position load after another
+            for (int j0 = 0; j0 < k; j0 += 64) {
+                const int nj = k - j0 < 64 ? k - j0 : 64;
+                const int my_pos =
+                    lane < nj ? inv_perm[static_cast<int64_t>(t) * k + j0 + lane] : -1;
+                for (int j = 0; j < nj; ++j) {
+                    const int pos = __builtin_amdgcn_readlane(my_pos, j);
+                    if (static_cast<uint64_t>(pos) >= static_cast<uint64_t>(n_pos))
+                        continue;
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(
+                        out + static_cast<int64_t>(pos) * row_bytes);
 #pragma unroll
-                for (int i = 0; i < kGatherVec; ++i) {
-                    const int64_t idx = v0 + i * 64 + lane;
-                    if (idx < nvec) dst[idx] = v[i];
+                    for (int i = 0; i < kGatherVec; ++i) {
+                        const int64_t idx = v0 + i * 64 + lane;
+                        if (idx < nvec) dst[idx] = v[i];
+                    }
                 }
             }
         }
