@@ -49,6 +49,9 @@ def _eq(name, got, want):
 
 
 def check_golden(g):
+    if g.get("kind") == "faults":
+        check_golden_faults(g)
+        return
     pl = oracle.plan(np.asarray(g["counts"], np.int32), g["R"], g["S"],
                      g.get("policy", 0), g.get("quota_mode", 0))
     for key in ("quota", "exhausted", "residual", "n_rep"):
@@ -69,6 +72,34 @@ def check_golden(g):
         assert rr["faults"] == 0
         for key in ("phys", "perm", "inv_perm", "rank_counts"):
             _eq(f"{g['name']}: {key}", rr[key], g[key])
+
+
+PERM_FILL = -777
+
+
+def check_golden_faults(g):
+    """A plan made from other counts applied to routing with ids out of
+    range: faulted assignments get phys = inv_perm = -1, take no position,
+    and are left out of rank_counts; perm positions nothing fills keep the
+    caller's value."""
+    pl = oracle.plan(np.asarray(g["plan_counts"], np.int32), g["R"], g["S"],
+                     g.get("policy", 0), g.get("quota_mode", 0))
+    for key in ("rep_off", "slot_off"):
+        _eq(f"{g['name']}: {key}", pl[key], g[key])
+    n = pl["n_rep"]
+    _eq(f"{g['name']}: rep_slot", pl["rep_slot"][:n], g["rep_slot"])
+    _eq(f"{g['name']}: rep_cap", pl["rep_cap"][:n], g["rep_cap"])
+    routing = np.asarray(g["routing"], np.int32)
+    counts, invalid = oracle.load(routing[None], g["E"])
+    _eq(f"{g['name']}: routing counts", counts[0], g["routing_counts"])
+    assert invalid[0] == g["invalid"], f"{g['name']}: invalid"
+    rr = oracle.reroute(routing.reshape(-1), pl, perm_fill=PERM_FILL)
+    assert rr["faults"] == g["faults"], \
+        f"{g['name']}: faults {rr['faults']} != {g['faults']}"
+    for key in ("phys", "inv_perm", "rank_counts"):
+        _eq(f"{g['name']}: {key}", rr[key], g[key])
+    want_perm = [PERM_FILL if v is None else v for v in g["perm"]]
+    _eq(f"{g['name']}: perm", rr["perm"], want_perm)
 
 
 # --------------------------------------------------------------------------
@@ -139,6 +170,13 @@ def exhausts_at(counts, R, S, policy, Q):
     return False
 
 
+# The two checks below re-run the planning rule in Python (the quota
+# search's steps, each chunk's destination). They are a second statement of
+# the rule, not a fact independent of it, so the mutant tests also require
+# every planted mistake to be caught with both switched off.
+REPLAYS = True
+
+
 def check_quota(counts, R, S, policy, quota_mode, pl):
     """Quota 0: ceil(total / R). Quota search: one of Q0 + j ceil(Q0/256),
     j < 64; every lower one exhausts when the rule is run on its own; the
@@ -148,6 +186,8 @@ def check_quota(counts, R, S, policy, quota_mode, pl):
     Q = pl["quota"]
     if quota_mode == 0:
         assert Q == Q0, "quota is ceil(total / ranks)"
+        return
+    if not REPLAYS:
         return
     step = -(-Q0 // 256)
     grid = [Q0 + j * step for j in range(64)]
@@ -258,6 +298,8 @@ def check_choices(counts, R, S, policy, pl):
     the chunk is min(source excess, expert remainder, headroom) and takes
     the lowest free spare slot; an expert stops short only when no rank is
     eligible, and then nothing moves after it."""
+    if not REPLAYS:
+        return
     counts = np.asarray(counts, np.int64)
     E = counts.size
     N, NS = E // R, E // R + S

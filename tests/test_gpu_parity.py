@@ -28,7 +28,8 @@ RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
 
 
 @pytest.mark.parametrize("case", [g for g in pins.golden_cases()
-                                  if "routing" in g], ids=lambda g: g["name"])
+                                  if "routing" in g and "kind" not in g],
+                         ids=lambda g: g["name"])
 def test_golden_cases(case):
     say("golden", case["name"])
     routing = np.asarray(case["routing"], np.int32)[None]
@@ -41,8 +42,40 @@ def test_golden_cases(case):
     compare_with_oracle(res, routing, case["E"], case["R"], case["S"])
 
 
+@pytest.mark.parametrize("case", [g for g in pins.golden_cases()
+                                  if g.get("kind") == "faults"],
+                         ids=lambda g: g["name"])
+def test_golden_faults(case):
+    """The hand-worked fault case through ue_load, ue_plan (on the counts
+    the plan was made from) and ue_reroute: faulted assignments get phys =
+    inv_perm = -1 and no position, rank_counts leave them out, and perm
+    positions nothing fills keep the value the caller put there."""
+    say("golden faults", case["name"])
+    fill = pins.PERM_FILL
+    routing = torch.tensor(case["routing"], dtype=torch.int32,
+                           device=DEV)[None]
+    ctx = make_ctx(case["E"], case["R"], case["S"], case["k"], case["T"])
+    invalid = torch.full((1,), -7, dtype=torch.int32, device=DEV)
+    counts = ue.ue_load(ctx, routing, invalid=invalid)
+    plan_counts = torch.tensor(case["plan_counts"], dtype=torch.int32,
+                               device=DEV)[None]
+    placement = ue.ue_plan(ctx, plan_counts)
+    perm = torch.full((1, case["T"] * case["k"]), fill, dtype=torch.int32,
+                      device=DEV)
+    out = ue.ue_reroute(ctx, routing, placement, perm=perm)
+    torch.cuda.synchronize()
+    assert counts[0].tolist() == case["routing_counts"]
+    assert int(invalid[0]) == case["invalid"]
+    assert int(out["faults"][0]) == case["faults"]
+    for key in ("phys", "inv_perm", "rank_counts"):
+        assert out[key].reshape(-1).tolist() == case[key], key
+    assert perm[0].tolist() == [fill if v is None else v for v in case["perm"]]
+
+
 def test_golden_planner_only():
     for case in pins.golden_cases():
+        if case.get("kind") == "faults":
+            continue
         say("golden plan", case["name"])
         ctx = make_ctx(case["E"], case["R"], case["S"], 1, 1,
                        policy=case.get("policy", 0),

@@ -5,12 +5,19 @@ comparison, a dropped term of the chunk size, a wrong index, a missing
 state update. Each mutant is compiled from the oracle's C source with one
 substitution and run through the same checks as the oracle itself."""
 import os
+import subprocess
+import sys
 
 import numpy as np
 import pytest
 
-import oracle
-import pins
+# the module also runs as a child process (see caught()), outside pytest
+_ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if _ROOT not in sys.path:
+    sys.path.insert(0, _ROOT)
+
+import oracle  # noqa: E402
+import pins  # noqa: E402
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ue_oracle.c")
 
@@ -68,6 +75,28 @@ MUTANTS = {
     "plan made at the plain quota": (
         "const int exhausted = greedy_at(counts, E, R, S, policy, Q, load,",
         "const int exhausted = greedy_at(counts, E, R, S, policy, Q0, load,"),
+    "search grain 128": ("(Q0 + 255) / 256", "(Q0 + 127) / 128"),
+    "search 32 steps": ("for (int32_t j = 0; j < 64; ++j)",
+                        "for (int32_t j = 0; j < 32; ++j)"),
+    "search without a working step keeps the last one tried": (
+        "        for (int32_t j = 0; j < 64; ++j) {\n"
+        "            const int64_t M = Q0 + j * step;\n",
+        "        for (int32_t j = 0; j < 64; ++j) {\n"
+        "            const int64_t M = Q0 + j * step;\n"
+        "            Q = M;\n"),
+    "fault counted in rank counts": (
+        "        const int32_t p = rep_slot[hit];\n",
+        "        const int32_t p = rep_slot[hit];\n"
+        "        rank_counts[p / NS] += 1;\n"),
+    "faulted assignment keeps a position": ("        inv_perm[a] = -1;\n",
+                                            "        inv_perm[a] = 0;\n"),
+    "ids out of range not counted as faults": (
+        "        if (e < 0 || e >= E) {\n            ++faults;",
+        "        if (e < 0 || e >= E) {\n            ;"),
+    "capacity overflow goes to the last replica": (
+        "        if (hit < 0) {\n            ++faults;\n            continue;\n        }",
+        "        if (hit < 0) {\n            hit = rep_off[e + 1] - 1;\n"
+        "            prefix -= rep_cap[hit];\n        }"),
     "replica before master": ("rep_slot[n] = (e / N) * NS + (e % N);\n"
                               "        rep_cap[n] = (int32_t)rem[e];\n"
                               "        ++n;\n",
@@ -95,19 +124,60 @@ def run_all_pins():
     pins.check_invalid_ids()
 
 
+# exit status of the child when a pin caught the mistake
+CAUGHT = 3
+
+
+def build_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    return oracle.build(out=str(tmp_path / "libmutant.so"), src=str(mutated),
+                        strict=False)
+
+
+def caught(lib, replays):
+    """Runs every pin against the mutant library in a child process. A pin
+    failing, or the mutant crashing (a planted mistake can overrun the
+    oracle's own buffers), both count as caught; the child passing every
+    pin does not, and any other failure of the child is an error."""
+    proc = subprocess.run(
+        [sys.executable, os.path.abspath(__file__), lib, str(int(replays))],
+        capture_output=True, text=True, timeout=600)
+    if proc.returncode == 0:
+        return False
+    if proc.returncode == CAUGHT or proc.returncode < 0:
+        return True
+    raise RuntimeError(f"mutant run failed (rc {proc.returncode}):\n"
+                       f"{proc.stderr[-2000:]}")
+
+
 def test_unmutated_oracle_passes():
     run_all_pins()
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
-    old, new = MUTANTS[name]
-    src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
-    mutated = tmp_path / "mutant.c"
-    mutated.write_text(src.replace(old, new))
-    lib = oracle.build(out=str(tmp_path / "libmutant.so"), src=str(mutated),
-                       strict=False)
-    with oracle.library(lib):
-        with pytest.raises((AssertionError, IndexError, ValueError)):
+    assert caught(build_mutant(name, tmp_path), replays=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught_without_replays(name, tmp_path):
+    """The same, with the Python replays of the rule (quota steps, chunk
+    destinations) switched off: the hand-worked cases, closed forms,
+    library routines, invariants and brute force must catch every
+    mistake on their own."""
+    assert caught(build_mutant(name, tmp_path), replays=False)
+
+
+if __name__ == "__main__":
+    # child process of caught(): argv = library path, replays (0 or 1)
+    pins.REPLAYS = bool(int(sys.argv[2]))
+    with oracle.library(sys.argv[1]):
+        try:
             run_all_pins()
+        except (AssertionError, IndexError, ValueError):
+            sys.exit(CAUGHT)
+    sys.exit(0)
