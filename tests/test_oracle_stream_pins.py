@@ -65,3 +65,56 @@ def test_gather_hand_worked():
     perm = rng.permutation(150)
     assert np.array_equal(oracle.gather(x, perm, 3),
                           np.take(x, perm // 3, axis=0))
+
+
+def test_grad_reduce_rounded_order_and_rounding():
+    """The binary32 result of the binary64 left-to-right sum.
+    (1 + 2^-24) + 2^-24 is carried exactly and rounds to 1 + 2^-23, where a
+    binary32 running sum would tie to even twice and give 1; 1 + 2^-60 - 1
+    gives 0 left to right (1 + 2^-60 rounds to 1 in binary64), where the
+    exact sum or another order gives 2^-60. On terms whose binary64 partial
+    sums are exact (magnitudes within 2^-10 .. 2^-3), every result is the
+    correctly rounded binary32 of the exact sum, checked with fractions."""
+    from fractions import Fraction
+    u = np.float32(2.0 ** -24)
+    got = oracle.grad_reduce_rounded(np.ones(3, np.float32),
+                                     [np.full(3, u), np.full(3, u)])
+    assert got.dtype == np.float32
+    assert np.all(got == np.float32(1.0 + 2.0 ** -23))
+    got = oracle.grad_reduce_rounded(np.ones(1, np.float32),
+                                     [np.full(1, 2.0 ** -60, np.float32),
+                                      -np.ones(1, np.float32)])
+    assert got[0] == 0.0
+    got = oracle.grad_reduce_rounded(np.ones(1, np.float32),
+                                     [-np.ones(1, np.float32),
+                                      np.full(1, 2.0 ** -60, np.float32)])
+    assert got[0] == np.float32(2.0 ** -60)
+
+    def round_f32(q):
+        # nearest float32 to the rational q, ties to even (normal range)
+        f = np.float32(float(q))
+        if Fraction(float(f)) == q:
+            return f
+        g = np.nextafter(f, np.float32(np.inf) if Fraction(float(f)) < q
+                         else np.float32(-np.inf))
+        lo, hi = sorted((f, g))
+        dl, dh = abs(Fraction(float(lo)) - q), abs(Fraction(float(hi)) - q)
+        if dl != dh:
+            return lo if dl < dh else hi
+        return lo if int(np.array(lo).view(np.int32)) % 2 == 0 else hi
+
+    rng = np.random.default_rng(2)
+
+    def terms(n):
+        mag = 2.0 ** rng.uniform(-10, -3, n)
+        return (mag * rng.choice([-1.0, 1.0], n)).astype(np.float32)
+
+    master = terms(400)
+    reps = [terms(400) for _ in range(4)]
+    got = oracle.grad_reduce_rounded(master, reps)
+    for i in range(400):
+        q = Fraction(float(master[i])) + sum(Fraction(float(r[i]))
+                                             for r in reps)
+        assert got[i] == round_f32(q), i
+    # with no replica the master comes back unchanged
+    assert np.array_equal(oracle.grad_reduce_rounded(master, []), master)
