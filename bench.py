@@ -164,35 +164,6 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     return cfg, rb, ms, phases, ms_one
 
 
-def stale_rank_loads(slot_expert, slot_cap, counts_new, N, NS, R):
-    """Rank loads when plans made from other counts are applied to
-    ``counts_new`` [L, E]: each expert's new count is split over the slots
-    the old plan gave it in proportion to their old capacities (an expert
-    the old plan saw no tokens of stays whole on its native slot). Slot
-    tables are [L, P] (slot_expert -1: unused). Returns float64 [L, R]."""
-    import torch
-    L, P = slot_expert.shape
-    E = counts_new.shape[1]
-    dev = counts_new.device
-    se = slot_expert.long()
-    used = se >= 0
-    e_of = torch.where(used, se, torch.zeros_like(se))
-    cap = torch.where(used, slot_cap.double(), torch.zeros_like(se,
-                                                               dtype=torch.float64))
-    tot = torch.zeros((L, E), dtype=torch.float64, device=dev)
-    tot.scatter_add_(1, e_of, cap)
-    t = torch.gather(tot, 1, e_of)
-    native = (torch.arange(P, device=dev) % NS < N)[None, :].expand(L, P)
-    share = torch.where(t > 0, cap / t.clamp(min=1.0),
-                        native.to(torch.float64))
-    share = torch.where(used, share, torch.zeros_like(share))
-    load = torch.gather(counts_new.double(), 1, e_of) * share
-    rank = (torch.arange(P, device=dev) // NS)[None, :].expand(L, P)
-    out = torch.zeros((L, R), dtype=torch.float64, device=dev)
-    out.scatter_add_(1, rank, load)
-    return out
-
-
 def _spread(x):
     import numpy as np
     x = np.asarray(x, dtype=np.float64)
@@ -205,8 +176,8 @@ def bench_stale(ue, W, dev, policy=0, quota_mode=0):
     the exact current ones: the previous microbatch's plan and the plan of
     the summed earlier microbatches under the pipeline workload's drift,
     and the previous step's plan of the same dsv3 layer (same distribution,
-    fresh tokens). Plans are made by the library; only the split of the
-    new counts over the old plan's slots is evaluated here."""
+    fresh tokens). Plans and the split of the new counts over an old plan's
+    replicas (ue_stale_loads) are made by the library."""
     import torch
     out = {}
     cfg = W.CONFIGS["pipeline"]
@@ -218,12 +189,10 @@ def bench_stale(ue, W, dev, policy=0, quota_mode=0):
     f = ctx.placement_fields(rb.placement)
     mean = counts.sum(1).double() / cfg.ranks
     cum = torch.cumsum(counts, 0, dtype=torch.int32)[:-1].contiguous()
-    hist = ctx.placement_fields(ue.ue_plan(ctx, cum))
-    N, NS = ctx.N, ctx.N + ctx.S
-    prev = stale_rank_loads(f["slot_expert"][:-1], f["slot_cap"][:-1],
-                            counts[1:], N, NS, cfg.ranks)
-    summed = stale_rank_loads(hist["slot_expert"], hist["slot_cap"],
-                              counts[1:], N, NS, cfg.ranks)
+    hist_pl = ue.ue_plan(ctx, cum)
+    later = counts[1:].contiguous()
+    prev = ue.ue_stale_loads(ctx, rb.placement[:-1].contiguous(), later)
+    summed = ue.ue_stale_loads(ctx, hist_pl, later)
     m1 = mean[1:]
     out["pipeline_drift"] = {
         "microbatches": "1..15 (each planned from earlier ones)",
@@ -239,12 +208,11 @@ def bench_stale(ue, W, dev, policy=0, quota_mode=0):
     ctx = ue.Context(cfg.experts, cfg.ranks, cfg.spare, cfg.topk, cfg.tokens,
                      cfg.layers, device=dev, plan_policy=policy,
                      quota_mode=quota_mode)
-    old = ctx.placement_fields(ue.ue_plan(ctx, ue.ue_load(ctx, r0)))
+    old = ue.ue_plan(ctx, ue.ue_load(ctx, r0))
     c1 = ue.ue_load(ctx, r1)
     now = ctx.placement_fields(ue.ue_plan(ctx, c1))
     mean = c1.sum(1).double() / cfg.ranks
-    st = stale_rank_loads(old["slot_expert"], old["slot_cap"], c1, ctx.N,
-                          ctx.N + ctx.S, cfg.ranks)
+    st = ue.ue_stale_loads(ctx, old, c1)
     out["dsv3_next_step"] = {
         "layers": "58 (plan of the same layer one step earlier)",
         "no_rebalance": _spread((now["load_before"].max(1).values / mean).cpu()),

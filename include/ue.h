@@ -38,6 +38,13 @@
  *    the registered tables are not replaced meanwhile.
  *  - All shapes are int32; the number of assignments per layer, T*k, must
  *    stay below 2^30.
+ *  - Workgroups of one launch combine per-tile counts through bounded waits
+ *    on each other (decoupled lookback). A wait that outlasts the context's
+ *    wait limit (ue_set_wait_limit) gives up, and every kernel still runs
+ *    to its end; the layer is then marked poisoned: bit 30 (0x40000000,
+ *    UE_POISONED) is set in that layer's `invalid` (ue_load, ue_rebalance)
+ *    and `faults` (ue_reroute, ue_rebalance) words, the other bits keep
+ *    their counts, and the layer's other outputs are unspecified.
  */
 #ifndef UE_H
 #define UE_H
@@ -98,6 +105,9 @@ enum {
     UE_QUOTA_SEARCH = 1        /* the lowest of Q0 + j*ceil(Q0/256), j < 64,
                                   at which nothing is left over (else Q0)   */
 };
+
+/* Bit of a layer's invalid / faults word marking a wait that gave up. */
+#define UE_POISONED 0x40000000
 
 typedef struct ue_ctx ue_ctx;
 
@@ -179,7 +189,12 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
  *   Q0 + j*ceil(Q0/256), j = 0..63 (Q0 = ceil(sum(counts)/R)), in order,
  *   and the first that leaves nothing over is kept; with none, Q0 stands.
  *   The placement's quota field holds the quota used.
- *   counts     device, int32 [L, E] (e.g. from ue_load)
+ *   counts     device, int32 [L, E] (e.g. from ue_load); every count >= 0
+ *              and each layer's sum below 2^30 (ue_load's counts always
+ *              are). A layer that breaks this is not planned: its block
+ *              gets exhausted = -1 and an empty replica table (rep_off all
+ *              0, n_rep 0), so every assignment of a later ue_reroute with
+ *              it is a fault.
  *   placement  device, L blocks of ue_placement_bytes() bytes, out
  * Fully on the device; nothing returns to the host. */
 int ue_plan(ue_ctx *ctx, const int32_t *counts, int32_t L, void *placement,
@@ -219,6 +234,33 @@ int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
                  int32_t *counts, int32_t *invalid, void *placement,
                  int32_t *phys, int32_t *rank_counts, int32_t *perm,
                  int32_t *inv_perm, int32_t *faults, void *stream);
+
+/* Rank loads under an earlier plan: the periodic, historical-load
+ * balancing that the UltraEP abstract (arXiv 2606.04101) and the news
+ * write-up (section on the problem UltraEP solves) contrast with exact-load
+ * balancing. Each layer's placement block (from ue_plan on earlier counts)
+ * is applied to that layer's new counts: the plan keeps its replicas and
+ * their proportions, so of expert e's n new assignments, with old
+ * capacities c_1..c_m (master first, then replicas in table order) summing
+ * to C, replica i takes floor(n * c_<=i / C) - floor(n * c_<i / C); an
+ * expert the plan saw no tokens of (C = 0) stays whole on its master.
+ *   placement   device, L blocks from ue_plan (on other counts)
+ *   counts      device, int32 [L, E], the new counts (each >= 0, the sum of
+ *               a layer below 2^30)
+ *   rank_loads  device, int32 [L, R] out: assignments per rank
+ * Exact integer arithmetic; the same covering rule as ue_reroute with the
+ * capacities rescaled. Errors: UE_EINVAL (null or misaligned pointers),
+ * UE_ESHAPE (L outside 1..max_layers). */
+int ue_stale_loads(ue_ctx *ctx, const void *placement, const int32_t *counts,
+                   int32_t L, int32_t *rank_loads, void *stream);
+
+/* Polls one cross-workgroup wait may take before it gives up and marks
+ * its layer poisoned (see the conventions above); default 4,194,304, far
+ * beyond any wait of a healthy device. 0 makes every wait give up without
+ * polling, so every layer with more than one tile group is marked: a way to
+ * exercise the error path with every kernel still ending normally.
+ * Applies to later calls on the context. */
+int ue_set_wait_limit(ue_ctx *ctx, uint32_t polls);
 
 /* Kernel timing. With timing enabled, every call records a HIP event on its
  * stream before its first kernel and after each kernel it launches.
@@ -273,9 +315,13 @@ int ue_weight_sync(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
 
 /* Replica gradient reduction ("Replica gradient reduction": replica
  * gradients are summed into master gradients during backward). Same CSR as
- * ue_weight_sync. Per element, in fp32 with round-to-nearest-even and no
- * reassociation: g = master; g += replica_1; g += replica_2; ...;
- * master = g. Replica gradients are left unchanged. */
+ * ue_weight_sync. Per element, with the running sum in binary64 and no
+ * reassociation: g = master; g += replica_1; g += replica_2; ...; then
+ * master = g rounded once to binary32 (nearest even). The fp32 gradient is
+ * thus within one rounding of the exact sum (unless the binary64 partial
+ * sums themselves round, which takes terms some 2^29 apart in magnitude),
+ * also where replicas cancel the master. Replica gradients are left
+ * unchanged. */
 int ue_grad_reduce(ue_ctx *ctx, const int32_t *rep_off, const int32_t *rep_buf,
                    int32_t n_experts, void *stream);
 

@@ -86,6 +86,8 @@ SIGNATURES = {
     "ue_grad_reduce": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp]),
     "ue_gather_rows": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                       _vp]),
+    "ue_stale_loads": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "ue_set_wait_limit": (ctypes.c_int, [_vp, ctypes.c_uint32]),
 }
 
 _lib = None
@@ -284,6 +286,26 @@ def ue_plan(ctx: Context, counts, placement=None, stream=None):
     return placement
 
 
+def ue_stale_loads(ctx: Context, placement, counts, rank_loads=None,
+                   stream=None):
+    """Rank loads int32 [L, R] when placement blocks made from earlier counts
+    are applied to new counts int32 [L, E]."""
+    counts = counts.reshape(-1, ctx.E)
+    L = counts.shape[0]
+    _need(counts, "counts", torch.int32, ctx.device)
+    _need(placement, "placement", torch.int32, ctx.device,
+          L * ctx.placement_words)
+    if rank_loads is None:
+        rank_loads = torch.empty((L, ctx.R), dtype=torch.int32,
+                                 device=ctx.device)
+    _need(rank_loads, "rank_loads", torch.int32, ctx.device, L * ctx.R)
+    rc = library().ue_stale_loads(ctx._h, _ptr(placement), _ptr(counts), L,
+                                  _ptr(rank_loads),
+                                  _stream(stream, ctx.device))
+    ctx._check(rc, "ue_stale_loads")
+    return rank_loads
+
+
 def ue_reroute(ctx: Context, routing, placement, phys=None, rank_counts=None,
                perm=None, inv_perm=None, faults=None, with_inv=True,
                stream=None):
@@ -318,6 +340,16 @@ def ue_reroute(ctx: Context, routing, placement, phys=None, rank_counts=None,
     ctx._check(rc, "ue_reroute")
     return dict(phys=phys, rank_counts=rank_counts, perm=perm,
                 inv_perm=inv_perm, faults=faults)
+
+
+POISONED = 0x40000000   # bit of invalid / faults: a wait gave up
+
+
+def ue_set_wait_limit(ctx: Context, polls: int):
+    """Polls one cross-workgroup wait may take before it gives up (0: at
+    once, marking every multi-group layer poisoned)."""
+    ctx._check(library().ue_set_wait_limit(ctx._h, int(polls)),
+               "ue_set_wait_limit")
 
 
 def ue_set_timing(ctx: Context, enable: bool = True):

@@ -41,6 +41,7 @@ struct LoadArgs {
     uint64_t *tick;            // [max_layers]
     int32_t *group_base;       // [max_layers][max_groups][E]
     uint16_t *tile_off;        // [max_layers][max_tiles + max_groups][E]
+    int32_t *status;           // [max_layers] poisoned flag of the call
     int32_t *counts, *invalid;
 };
 
@@ -185,9 +186,14 @@ __global__ __launch_bounds__(kBlock) void k_load(LoadArgs g) {
     }
     int total;
     block_exclusive_sum(part, wsum, total);
-    if (tid == 0 && g.invalid)
-        g.invalid[layer] = static_cast<int32_t>(g.A - total) |
-                           (poisoned ? kPoisonBit : 0);
+    if (tid == 0) {
+        // the last group's lookback saw every group's words, so it is
+        // poisoned exactly when some wait of the layer gave up
+        g.status[layer] = poisoned;
+        if (g.invalid)
+            g.invalid[layer] = static_cast<int32_t>(g.A - total) |
+                               (poisoned ? kPoisonBit : 0);
+    }
 }
 
 }  // namespace
@@ -226,11 +232,12 @@ hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
     g.max_groups = c.max_load_groups;
     g.max_tiles = c.max_rr_tiles;
     g.vec4 = (A % 4 == 0) && (reinterpret_cast<uintptr_t>(routing) % 16 == 0);
-    g.spin_limit = 1u << 22;
+    g.spin_limit = c.wait_limit;
     g.state = c.load_state;
     g.tick = c.load_tick;
     g.group_base = c.group_base;
     g.tile_off = c.tile_off;
+    g.status = c.load_status;
     g.counts = counts;
     g.invalid = invalid;
     if (wide)

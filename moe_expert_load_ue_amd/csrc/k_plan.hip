@@ -569,6 +569,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     __shared__ int s_works[kPlanWaves];
     __shared__ int s_nrecw[kPlanWaves];
     __shared__ int s_nrec, s_exhausted, s_quota, s_region;
+    __shared__ uint32_t wsat[kPlanWaves];
 
     const int layer = blockIdx.x;
     const int tid = threadIdx.x;
@@ -583,7 +584,9 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     }
 
     // ---- A. loads, quota, candidates ----------------------------------
+    // (E <= kPlanBlock: one count per thread)
     int part = 0;
+    uint32_t sat = 0;    // the count, a negative one as 2^30
     for (int e = tid; e < E; e += kPlanBlock) {
         const int c = cin[e];
         s.cnt[e] = c;
@@ -591,13 +594,37 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         s.nrec_e[e] = 0;
         s.first_rec[e] = 0;
         part += c;
+        sat = c < 0 ? (1u << 30) : static_cast<uint32_t>(c);
     }
     for (int p = tid; p < P; p += kPlanBlock) {
         s.slot_cap[p] = 0;
         s.slot_exp[p] = -1;
     }
+    // counts must be >= 0 and sum below 2^30 (the int32 loads, the packed
+    // rank keys and the headroom sums rely on it; ue_load's counts always
+    // do): a saturating sum per wave, joined after the barrier below
+    sat = wave_sat_inclusive_sum(sat);
+    if ((tid & 63) == 63) wsat[tid >> 6] = sat;
     int total;
-    plan_block_sum(part, wsum, total);   // barrier: cnt visible
+    plan_block_sum(part, wsum, total);   // barrier: cnt and wsat visible
+    {
+        uint64_t all = 0;
+#pragma unroll
+        for (int w = 0; w < kPlanWaves; ++w) all += wsat[w];
+        if (all >= (1u << 30)) {
+            // not planned: an empty table (no replica, every later reroute
+            // assignment a fault), marked exhausted = -1; uniform across
+            // the block, so every thread leaves here
+            for (int i = tid; i < lay.words; i += kPlanBlock) {
+                const bool neg1 =
+                    i == lay.exhausted ||
+                    (i >= lay.rep_slot && i < lay.rep_slot + P) ||
+                    (i >= lay.slot_expert && i < lay.slot_expert + P);
+                out[i] = neg1 ? -1 : 0;
+            }
+            return;
+        }
+    }
     const int Q0 = (total + R - 1) / R;
     const bool search = quota_mode == UE_QUOTA_SEARCH;
     const int step = (Q0 + kQuotaGrain - 1) / kQuotaGrain;

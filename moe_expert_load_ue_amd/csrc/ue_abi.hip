@@ -183,6 +183,7 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         take(sizeof(uint16_t) * Lmax * (rr_tiles + ld_groups) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
+    const size_t o_lstat = take(sizeof(int32_t) * Lmax);
     c->ws_bytes = off;
     he = hipMalloc(&c->ws, c->ws_bytes);
     if (he != hipSuccess) {
@@ -203,6 +204,7 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     c->tile_off = reinterpret_cast<uint16_t *>(b + o_toff);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
+    c->load_status = reinterpret_cast<int32_t *>(b + o_lstat);
     *out = c;
     return UE_OK;
 }
@@ -238,6 +240,13 @@ int ue_set_timing(ue_ctx *ctx, int enable) {
     }
     ctx->timing = enable != 0;
     ctx->n_ev = 0;
+    return UE_OK;
+}
+
+int ue_set_wait_limit(ue_ctx *ctx, uint32_t polls) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    ctx->wait_limit = polls;
     return UE_OK;
 }
 
@@ -355,6 +364,25 @@ int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
         rank_counts, perm, inv_perm, faults, s);
     tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_reroute launch");
+}
+
+int ue_stale_loads(ue_ctx *ctx, const void *placement, const int32_t *counts,
+                   int32_t L, int32_t *rank_loads, void *stream) {
+    if (!ctx) return UE_EINVAL;
+    ctx->err.clear();
+    if (L < 1 || L > ctx->cfg.max_layers)
+        return fail(ctx, UE_ESHAPE, "L=%d outside 1..%d", L, ctx->cfg.max_layers);
+    if (!placement || !counts || !rank_loads)
+        return fail(ctx, UE_EINVAL, "ue_stale_loads: null pointer");
+    if (!aligned(placement, 4) || !aligned(counts, 4) || !aligned(rank_loads, 4))
+        return fail(ctx, UE_EINVAL,
+                    "ue_stale_loads: arrays must be 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    tbegin(ctx, s);
+    hipError_t he = ue::launch_stale(*ctx, static_cast<const int32_t *>(placement),
+                                     counts, L, rank_loads, s);
+    tmark(ctx, s);
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_stale launch");
 }
 
 int ue_register_experts(ue_ctx *ctx, int32_t n_experts, int32_t n_mats,

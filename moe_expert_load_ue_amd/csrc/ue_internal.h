@@ -58,6 +58,12 @@ struct ue_ctx {
     uint16_t *tile_off = nullptr;  // [max_layers][max_rr_tiles + max_load_groups][E]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
+    // per layer, written by the load's last group on every call: nonzero
+    // when a lookback wait of that call gave up (the fused reroute reports
+    // it in faults)
+    int32_t *load_status = nullptr;// [max_layers]
+    // polls of one cross-workgroup wait before it gives up
+    uint32_t wait_limit = 1u << 22;
 
     size_t plan_lds = 0;
     bool plan_per_wave = false;   // planner keeps every pass's chunks
@@ -109,6 +115,9 @@ hipError_t launch_weight_sync(const ue_ctx &c, const int32_t *rep_off,
 hipError_t launch_grad_reduce(const ue_ctx &c, const int32_t *rep_off,
                               const int32_t *rep_buf, int n_experts,
                               hipStream_t s);
+hipError_t launch_stale(const ue_ctx &c, const int32_t *placement,
+                        const int32_t *counts, int L, int32_t *rank_loads,
+                        hipStream_t s);
 hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
                               const int32_t *inv_perm, int T, int k, int H,
                               void *out, hipStream_t s);
@@ -264,7 +273,8 @@ __device__ __forceinline__ void atomic_store_agent(uint32_t *p, uint32_t v) {
 // Words of earlier calls carry an older epoch and are never taken for
 // current ones, so nothing is cleared between calls. A wait that outlasts
 // `spin_limit` polls gives up and publishes POISON instead, which every
-// later tile propagates; callers report it.
+// later tile propagates; callers report it. A limit of 0 gives up at once,
+// without polling (every tile but the first is then poisoned).
 constexpr uint32_t kFlagAgg = 1;
 constexpr uint32_t kFlagPrefix = 2;
 constexpr uint32_t kFlagPoison = 3;
@@ -305,7 +315,7 @@ __device__ __forceinline__ bool tile_lookback(uint64_t *st, int tile,
         // add AGG values until a PREFIX; a word not yet published restarts
         // the next window at that tile.
         uint32_t acc = 0;
-        bool bad = false, done = false;
+        bool bad = spin_limit == 0, done = bad;
         int t = tile - 1;
         uint32_t spins = 0;
         while (!done) {

@@ -25,6 +25,10 @@ Steps and the passages they follow (page titles as they appear on the web):
   reduced during backward). Computed in float64.
 * ``gather`` -- token dispatch into physical-expert order (gitdiagram: token
   dispatch consumes the physical routing).
+* ``stale_loads`` -- rank loads when a plan made from earlier counts is
+  applied to new ones: the periodic, history-driven balancing the pages
+  contrast with exact-load balancing (UltraEP abstract; news write-up,
+  section on the problem UltraEP solves).
 """
 from __future__ import annotations
 
@@ -186,6 +190,40 @@ def rebalance(routing: np.ndarray, n_experts: int, n_ranks: int,
     return res
 
 
+def stale_loads(pl: dict, counts_new: np.ndarray) -> np.ndarray:
+    """Rank loads when the plan ``pl`` (made from earlier counts) is applied
+    to one layer's new counts (int ``[E]``): the periodic, historical-load
+    balancing that the UltraEP abstract (arXiv 2606.04101) and the news
+    write-up (section on the problem UltraEP solves) contrast with exact-load
+    balancing. The plan keeps its replicas and their proportions: of expert
+    e's n new assignments, with old capacities c_1..c_m (master first, then
+    replicas in table order) summing to C, replica i takes those j with
+    floor(n * c_<i / C) <= j < floor(n * c_<=i / C) -- the capacity prefix
+    scaled from C to n. An expert the plan saw no tokens of (C = 0) stays
+    whole on its master. Returns int64 ``[R]``."""
+    n_new = np.asarray(counts_new, dtype=np.int64).reshape(-1)
+    E, R = pl["E"], pl["R"]
+    NS = pl["N"] + pl["S"]
+    loads = np.zeros(R, dtype=np.int64)
+    for e in range(E):
+        n = int(n_new[e])
+        lo, hi = int(pl["rep_off"][e]), int(pl["rep_off"][e + 1])
+        caps = [int(c) for c in pl["rep_cap"][lo:hi]]
+        slots = [int(p) for p in pl["rep_slot"][lo:hi]]
+        C = sum(caps)
+        if C == 0:
+            loads[slots[0] // NS] += n
+            continue
+        before = 0
+        acc = 0
+        for slot, cap in zip(slots, caps):
+            acc += cap
+            upto = (n * acc) // C
+            loads[slot // NS] += upto - before
+            before = upto
+    return loads
+
+
 def weight_sync(master: np.ndarray, n_replicas: int) -> list:
     """Every replica receives a bitwise copy of the master weights."""
     return [np.array(master, copy=True) for _ in range(n_replicas)]
@@ -197,6 +235,16 @@ def grad_reduce(master: np.ndarray, replicas: list) -> np.ndarray:
     for rep in replicas:
         acc = acc + np.asarray(rep, dtype=np.float64)
     return acc
+
+
+def grad_reduce_rounded(master: np.ndarray, replicas: list) -> np.ndarray:
+    """The same sum as the fp32 gradient it becomes: one binary64 add at a
+    time from the master through the replicas in table order (no fused or
+    reassociated adds), then one rounding to binary32, nearest even."""
+    acc = np.array(master, dtype=np.float64, copy=True)
+    for rep in replicas:
+        acc = np.add(acc, np.asarray(rep, dtype=np.float64), dtype=np.float64)
+    return acc.astype(np.float32)
 
 
 def gather(x: np.ndarray, perm: np.ndarray, k: int) -> np.ndarray:

@@ -188,9 +188,9 @@ def test_graph_replay_rebalance_and_sync():
 
 
 def test_graph_replay_batched_layers():
-    """ue_rebalance over several layers (which forks onto the context's
-    second stream and joins again) captured once and replayed on fresh
-    routing, every layer against the oracle."""
+    """ue_rebalance over nine layers (three launches on the caller's
+    stream) captured once and replayed on fresh routing, every layer
+    against the oracle."""
     E, R, S, k, T, L = 64, 8, 2, 8, 3001, 9
     ctx = ue.Context(E, R, S, k, T, L, device=DEV)
     outs = routing_outputs(ctx, L, T)
@@ -210,3 +210,64 @@ def test_graph_replay_batched_layers():
         graph.replay()
         torch.cuda.synchronize()
         compare_with_oracle(as_result(ctx, outs), routing, E, R, S)
+
+
+def test_two_stream_schedule():
+    """The overlapped forward schedule: every layer's rebalance on one
+    stream, each layer's plan-driven weight sync and dispatch gather on a
+    second stream once that layer's rebalance has finished (an event), so
+    the next layers' rebalances run beside this layer's copies. Every
+    layer's routing outputs and gather against the oracle; the replica
+    buffers, shared by all layers and written in layer order, end as the
+    last layer naming each slot left them."""
+    E, R, S, k, T, H, L = 64, 8, 2, 8, 4096, 64, 4
+    ctx = ue.Context(E, R, S, k, T, 1, device=DEV,
+                     plan_policy=ue.PLAN_BEST_FIT, quota_mode=ue.QUOTA_SEARCH)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(79)
+    mw, mg, sw, sg = slot_state(ctx, gen)
+    rng = np.random.default_rng(10)
+    routings = [pins.random_routing(rng, T, E, k, s)[None]
+                for s in (1.4, 0.6, 2.0, 1.1)]
+    rin = [torch.from_numpy(r).to(DEV) for r in routings]
+    outs = [routing_outputs(ctx, 1, T) for _ in range(L)]
+    tables = [ue.replica_table(ctx, o["placement"], 0) for o in outs]
+    x = (torch.randn((T, H), generator=gen, device=DEV)).to(torch.bfloat16)
+    xo = [torch.empty((T * k, H), dtype=torch.bfloat16, device=DEV)
+          for _ in range(L)]
+    a, b = torch.cuda.Stream(device=DEV), torch.cuda.Stream(device=DEV)
+    ev = [torch.cuda.Event() for _ in range(L)]
+    torch.cuda.synchronize()
+    say("two-stream schedule")
+    for l in range(L):
+        ue.ue_rebalance(ctx, rin[l], **outs[l], stream=a)
+        ev[l].record(a)
+    for l in range(L):
+        b.wait_event(ev[l])
+        ctx.weight_sync(*tables[l], stream=b)
+        ue.ue_gather_rows(ctx, x, outs[l]["inv_perm"][0], xo[l], stream=b)
+    torch.cuda.synchronize()
+
+    xs = bits(x).reshape(T, H)
+    N, NS = ctx.N, ctx.N + ctx.S
+    last = {}                                   # slot -> expert, layer order
+    for l in range(L):
+        compare_with_oracle(as_result(ctx, outs[l]), routings[l], E, R, S)
+        counts, _ = oracle.load(routings[l], E)
+        pl = oracle.plan(counts[0], R, S, ue.PLAN_BEST_FIT, ue.QUOTA_SEARCH)
+        rr = oracle.reroute(routings[l].reshape(-1), pl)
+        want = oracle.gather(xs, rr["perm"], k)
+        assert np.array_equal(bits(xo[l]).reshape(T * k, H), want), \
+            f"layer {l} gather"
+        for e in range(E):
+            for i in range(pl["rep_off"][e] + 1, pl["rep_off"][e + 1]):
+                last[int(pl["rep_slot"][i])] = e
+    for p in range(ctx.P):
+        if p % NS < N:
+            continue
+        for m in range(len(MATS)):
+            got = bits(sw[p][m])
+            if p in last:
+                assert np.array_equal(got, bits(mw[last[p]][m])), f"slot {p}"
+            else:
+                assert np.all(got == -1), f"unused slot {p}"
