@@ -40,6 +40,8 @@
 //      scan.
 // Everything is integer and deterministic; the result does not depend on
 // scheduling.
+#include <mutex>
+
 #include "ue_internal.h"
 
 namespace ue {
@@ -884,10 +886,19 @@ size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave) {
                               regions * 3 * R * S + 2 * P);
 }
 
+// The limit only rises (the largest need so far), so a context or call
+// with a smaller need never lowers what another one relies on.
 hipError_t plan_prepare(size_t lds_bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_plan),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(lds_bytes));
+    static std::mutex mu;
+    static size_t granted = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (lds_bytes <= granted) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_plan),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        static_cast<int>(lds_bytes));
+    if (e == hipSuccess) granted = lds_bytes;
+    return e;
 }
 
 hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,

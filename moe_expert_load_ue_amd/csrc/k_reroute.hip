@@ -41,6 +41,7 @@
 //      beyond an expert's capacity or outside [0, T*k).
 // No fences and no global atomics on data.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "ue_internal.h"
@@ -616,14 +617,22 @@ size_t reroute_lds_bytes(int E, int R, int P, int k) {
                               static_cast<size_t>(5) * E + 1 + 3 * P);
 }
 
+// The limit only rises (the largest need so far), so a context or call
+// with a smaller need never lowers what another one relies on.
 hipError_t reroute_prepare(size_t lds_bytes) {
+    static std::mutex mu;
+    static size_t granted = 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (lds_bytes <= granted) return hipSuccess;
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&k_reroute<false>),
         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&k_reroute<true>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               static_cast<int>(lds_bytes));
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_reroute<true>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                static_cast<int>(lds_bytes));
+    if (e == hipSuccess) granted = lds_bytes;
+    return e;
 }
 
 static hipError_t launch(const ue_ctx &c, bool after_load,

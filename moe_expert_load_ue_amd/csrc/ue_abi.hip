@@ -58,6 +58,83 @@ void tmark(ue_ctx *c, hipStream_t s) {
 
 }  // namespace
 
+namespace ue {
+
+hipError_t device_info(int dev, DeviceInfo &out) {
+    hipDeviceProp_t prop;
+    hipError_t he = hipGetDeviceProperties(&prop, dev);
+    if (he != hipSuccess) return he;
+    out.num_cu = prop.multiProcessorCount;
+    out.lds_cap = prop.sharedMemPerBlock;
+    if (prop.sharedMemPerBlockOptin > out.lds_cap)
+        out.lds_cap = prop.sharedMemPerBlockOptin;
+    return hipSuccess;
+}
+
+int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
+               ue_ctx &c) {
+    const int E = cfg.num_experts, R = cfg.num_ranks,
+              S = cfg.spare_per_rank, k = cfg.topk;
+    if (E < 1 || E > kMaxExperts || R < 1 || E % R != 0 || S < 0 ||
+        S > kMaxSpare || k < 1 || k > E || cfg.max_tokens < 0 ||
+        cfg.max_layers < 1 ||
+        (cfg.plan_policy != UE_PLAN_LEAST_LOADED &&
+         cfg.plan_policy != UE_PLAN_BEST_FIT) ||
+        (cfg.quota_mode != UE_QUOTA_FIXED &&
+         cfg.quota_mode != UE_QUOTA_SEARCH))
+        return UE_EUNSUPPORTED;
+    const int N = E / R, NS = N + S;
+    const int64_t P = static_cast<int64_t>(R) * NS;
+    const int64_t A = static_cast<int64_t>(cfg.max_tokens) * k;
+    if (P > kMaxSlots || A >= (int64_t(1) << 30)) return UE_EUNSUPPORTED;
+    c.cfg = cfg;
+    c.E = E;
+    c.R = R;
+    c.S = S;
+    c.N = N;
+    c.NS = NS;
+    c.P = static_cast<int>(P);
+    c.k = k;
+    c.ebits = bits_for(E);
+    c.rbits = bits_for(R);
+    c.device = dev;
+    c.num_cu = info.num_cu;
+
+    // Placement block layout (int32 words).
+    ue_placement_layout &l = c.lay;
+    int w = 0;
+    l.quota = w++;
+    l.exhausted = w++;
+    l.residual = w++;
+    l.n_rep = w++;
+    l.rep_off = w; w += E + 1;
+    l.rep_slot = w; w += c.P;
+    l.rep_cap = w; w += c.P;
+    l.slot_expert = w; w += c.P;
+    l.slot_cap = w; w += c.P;
+    l.slot_off = w; w += c.P + 1;
+    l.load_before = w; w += R;
+    l.load_after = w; w += R;
+    l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
+
+    c.reroute_lds = reroute_lds_bytes(E, R, c.P, k);
+    // the quota search keeps each pass's chunks when they fit in LDS
+    c.plan_per_wave = cfg.quota_mode == UE_QUOTA_SEARCH &&
+                      plan_lds_bytes(E, R, S, c.P, true) + 256 <= info.lds_cap;
+    c.plan_lds = plan_lds_bytes(E, R, S, c.P, c.plan_per_wave);
+    if (c.plan_lds + 256 > info.lds_cap || c.reroute_lds + 256 > info.lds_cap ||
+        load_lds_bytes(E) + 256 > info.lds_cap)
+        return UE_EUNSUPPORTED;
+    // kernels that need more than 64 KiB of dynamic LDS have their limit
+    // raised to the need (it only ever rises)
+    if ((c.plan_lds > 65536 && plan_prepare(c.plan_lds) != hipSuccess) ||
+        (c.reroute_lds > 65536 && reroute_prepare(c.reroute_lds) != hipSuccess))
+        return UE_EUNSUPPORTED;
+    return UE_OK;
+}
+
+}  // namespace ue
+
 extern "C" {
 
 const char *ue_status_name(int status) {
@@ -74,90 +151,28 @@ const char *ue_status_name(int status) {
 }
 
 const char *ue_last_error(const ue_ctx *ctx) {
-    return ctx ? ctx->err.c_str() : "null context";
+    // no context: the calling thread's last ue_rebalance_static error
+    return ctx ? ctx->err.c_str() : ue::static_last_error();
 }
 
 int ue_create(const ue_config *cfg, ue_ctx **out) {
     if (!cfg || !out) return UE_EINVAL;
-    const int E = cfg->num_experts, R = cfg->num_ranks,
-              S = cfg->spare_per_rank, k = cfg->topk;
-    if (E < 1 || E > ue::kMaxExperts || R < 1 || E % R != 0 || S < 0 ||
-        S > ue::kMaxSpare || k < 1 || k > E || cfg->max_tokens < 0 ||
-        cfg->max_layers < 1 ||
-        (cfg->plan_policy != UE_PLAN_LEAST_LOADED &&
-         cfg->plan_policy != UE_PLAN_BEST_FIT) ||
-        (cfg->quota_mode != UE_QUOTA_FIXED &&
-         cfg->quota_mode != UE_QUOTA_SEARCH))
-        return UE_EUNSUPPORTED;
-    const int N = E / R, NS = N + S;
-    const int64_t P = static_cast<int64_t>(R) * NS;
-    const int64_t A = static_cast<int64_t>(cfg->max_tokens) * k;
-    if (P > ue::kMaxSlots || A >= (int64_t(1) << 30)) return UE_EUNSUPPORTED;
-
     ue_ctx *c = new (std::nothrow) ue_ctx();
     if (!c) return UE_ENOMEM;
-    c->cfg = *cfg;
-    c->E = E;
-    c->R = R;
-    c->S = S;
-    c->N = N;
-    c->NS = NS;
-    c->P = static_cast<int>(P);
-    c->k = k;
-    c->ebits = bits_for(E);
-    c->rbits = bits_for(R);
-
-    hipError_t he = hipGetDevice(&c->device);
-    if (he != hipSuccess) {
-        int rc = hip_fail(c, he, "hipGetDevice");
-        delete c;
-        return rc;
-    }
-    hipDeviceProp_t prop;
-    he = hipGetDeviceProperties(&prop, c->device);
+    int dev = 0;
+    ue::DeviceInfo info;
+    hipError_t he = hipGetDevice(&dev);
+    if (he == hipSuccess) he = ue::device_info(dev, info);
     if (he != hipSuccess) {
         delete c;
         return UE_EHIP;
     }
-    c->num_cu = prop.multiProcessorCount;
-
-    // Placement block layout (int32 words).
-    ue_placement_layout &l = c->lay;
-    int w = 0;
-    l.quota = w++;
-    l.exhausted = w++;
-    l.residual = w++;
-    l.n_rep = w++;
-    l.rep_off = w; w += E + 1;
-    l.rep_slot = w; w += c->P;
-    l.rep_cap = w; w += c->P;
-    l.slot_expert = w; w += c->P;
-    l.slot_cap = w; w += c->P;
-    l.slot_off = w; w += c->P + 1;
-    l.load_before = w; w += R;
-    l.load_after = w; w += R;
-    l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
-
-    c->reroute_lds = ue::reroute_lds_bytes(E, R, c->P, k);
-    size_t lds_cap = prop.sharedMemPerBlock;
-    if (prop.sharedMemPerBlockOptin > lds_cap)
-        lds_cap = prop.sharedMemPerBlockOptin;
-    // the quota search keeps each pass's chunks when they fit in LDS
-    c->plan_per_wave = cfg->quota_mode == UE_QUOTA_SEARCH &&
-                       ue::plan_lds_bytes(E, R, S, c->P, true) + 256 <= lds_cap;
-    c->plan_lds = ue::plan_lds_bytes(E, R, S, c->P, c->plan_per_wave);
-    if (c->plan_lds + 256 > lds_cap || c->reroute_lds + 256 > lds_cap ||
-        ue::load_lds_bytes(E) + 256 > lds_cap) {
+    if (int rc = ue::init_shape(*cfg, dev, info, *c)) {
         delete c;
-        return UE_EUNSUPPORTED;
+        return rc;
     }
-    if ((c->plan_lds > 65536 && ue::plan_prepare(c->plan_lds) != hipSuccess) ||
-        (c->reroute_lds > 65536 &&
-         ue::reroute_prepare(c->reroute_lds) != hipSuccess)) {
-        delete c;
-        return UE_EUNSUPPORTED;
-    }
-
+    const int E = c->E, k = c->k;
+    const int64_t A = static_cast<int64_t>(cfg->max_tokens) * k;
     const int Lmax = cfg->max_layers;
     int64_t rr_tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
     if (rr_tiles < 1) rr_tiles = 1;

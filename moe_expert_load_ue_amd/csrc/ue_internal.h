@@ -122,6 +122,21 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
                               const int32_t *inv_perm, int T, int k, int H,
                               void *out, hipStream_t s);
 
+// What the kernels need to know of a device.
+struct DeviceInfo {
+    int num_cu = 0;
+    size_t lds_cap = 0;      // dynamic LDS one workgroup may have
+};
+hipError_t device_info(int dev, DeviceInfo &out);
+// Validates a configuration and fills the shape fields of `c` (sizes,
+// placement layout, LDS needs) for device `dev`, raising kernels' LDS
+// limits where needed; allocates nothing. UE_OK or UE_EUNSUPPORTED.
+int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
+               ue_ctx &c);
+
+// Error text of the calling thread's last ue_rebalance_static call.
+const char *static_last_error();
+
 size_t load_lds_bytes(int E);
 // Tiles per load workgroup for a launch over L layers of `tiles` tiles
 // (the fused reroute finds its tile's prefix rows with it).
