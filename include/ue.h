@@ -123,7 +123,8 @@ int ue_create(const ue_config *cfg, ue_ctx **out);
 void ue_destroy(ue_ctx *ctx);
 
 /* Last error message of the context ("" if none); valid until the next
- * call on the context. */
+ * call on the context. With ctx NULL: the message of the calling thread's
+ * last ue_rebalance_static call. */
 const char *ue_last_error(const ue_ctx *ctx);
 
 /* Short name of a status code. */
@@ -261,6 +262,32 @@ int ue_stale_loads(ue_ctx *ctx, const void *placement, const int32_t *counts,
  * exercise the error path with every kernel still ending normally.
  * Applies to later calls on the context. */
 int ue_set_wait_limit(ue_ctx *ctx, uint32_t polls);
+
+/* ue_rebalance without a context and without allocating: for callers
+ * that cannot allocate device memory where they rebalance (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, outputs and results as ue_rebalance, with the context
+ * replaced by its configuration (validated as ue_create does: the same
+ * UE_EUNSUPPORTED cases; L <= max_layers and T <= max_tokens).
+ * Its scratch is one device array of UE_STATIC_SCRATCH_BYTES (16 MiB) in
+ * the library, which every device the library runs on holds until the
+ * process ends. A call needs, with tiles = max(1, ceil(T*k / 2048)) and
+ * groups = ceil(tiles / 8), each term rounded up to 256 bytes:
+ *   8 L + 8 L groups E + 4 L + 4 L groups E + 2 L (tiles + groups) E
+ * bytes (the 58-layer dsv3 rebalance, E=256, T=65536, k=8: 14.3 MB). A call
+ * needing more is refused with UE_ESHAPE before anything is launched.
+ * Each call first clears the ticket and lookback words it uses with a
+ * fill kernel on `stream` (no memset, so the call may be captured in a
+ * graph). Calls share the array: calls that overlap in time on one device
+ * race and give wrong results; order them on one stream. The first call on
+ * a device looks up the array's address there (hipGetSymbolAddress).
+ * Calls no allocation routine. Error text: ue_last_error(NULL). */
+#define UE_STATIC_SCRATCH_BYTES (16u << 20)
+int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,
+                        int32_t L, int32_t T, int32_t *counts,
+                        int32_t *invalid, void *placement, int32_t *phys,
+                        int32_t *rank_counts, int32_t *perm,
+                        int32_t *inv_perm, int32_t *faults, void *stream);
 
 /* Kernel timing. With timing enabled, every call records a HIP event on its
  * stream before its first kernel and after each kernel it launches.

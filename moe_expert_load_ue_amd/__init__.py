@@ -88,6 +88,9 @@ SIGNATURES = {
                                       _vp]),
     "ue_stale_loads": (ctypes.c_int, [_vp, _vp, _vp, _i32, _vp, _vp]),
     "ue_set_wait_limit": (ctypes.c_int, [_vp, ctypes.c_uint32]),
+    "ue_rebalance_static": (ctypes.c_int, [ctypes.POINTER(ue_config), _vp,
+                                           _i32, _i32, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -402,6 +405,52 @@ def ue_rebalance(ctx: Context, routing, counts=None, invalid=None,
     return dict(counts=counts, invalid=invalid, placement=placement,
                 phys=phys, rank_counts=rank_counts, perm=perm,
                 inv_perm=inv_perm, faults=faults)
+
+
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
+def placement_words(num_experts, num_ranks, spare_per_rank):
+    """int32 words of one layer's placement block for a configuration (the
+    layout ue_get_placement_layout reports, padded to 64 words)."""
+    E, R = int(num_experts), int(num_ranks)
+    P = R * (E // R + int(spare_per_rank))
+    return (6 + E + 5 * P + 2 * R + 63) // 64 * 64
+
+
+def ue_rebalance_static(cfg: ue_config, routing, counts, invalid, placement,
+                        phys, rank_counts, perm, inv_perm, faults,
+                        stream=None):
+    """ue_rebalance with no context and no allocation (see
+    ``ue_rebalance_static`` in ue.h): every output is the caller's
+    preallocated tensor (invalid and inv_perm may be None)."""
+    if not isinstance(cfg, ue_config):
+        raise TypeError("cfg must be a ue_config")
+    if routing.dim() == 2:
+        routing = routing.unsqueeze(0)
+    L, T, k = routing.shape
+    if k != cfg.topk:
+        raise ValueError(f"routing has {k} experts per token, cfg {cfg.topk}")
+    dev = routing.device
+    _need(routing, "routing", torch.int32, dev)
+    A = T * k
+    words = placement_words(cfg.num_experts, cfg.num_ranks,
+                            cfg.spare_per_rank)
+    for t, name, n in ((counts, "counts", L * cfg.num_experts),
+                       (invalid, "invalid", L),
+                       (placement, "placement", L * words),
+                       (phys, "phys", L * A),
+                       (rank_counts, "rank_counts", L * cfg.num_ranks),
+                       (perm, "perm", L * A), (inv_perm, "inv_perm", L * A),
+                       (faults, "faults", L)):
+        if t is not None or name not in ("invalid", "inv_perm"):
+            _need(t, name, torch.int32, dev, n)
+    rc = library().ue_rebalance_static(
+        ctypes.byref(cfg), _ptr(routing), L, T, _ptr(counts), _ptr(invalid),
+        _ptr(placement), _ptr(phys), _ptr(rank_counts), _ptr(perm),
+        _ptr(inv_perm), _ptr(faults), _stream(stream, dev))
+    if rc != UE_OK:
+        raise UEError(rc, library().ue_last_error(None).decode())
 
 
 def ue_register_experts(ctx: Context, mat_elems, master_w=None, master_g=None,

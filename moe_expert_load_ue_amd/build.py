@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libue.so")
 SOURCES = ["ue_abi.hip", "k_load.hip", "k_plan.hip", "k_reroute.hip",
-           "k_stream.hip", "k_stale.hip"]
+           "k_stream.hip", "k_stale.hip", "ue_static.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
