@@ -121,8 +121,11 @@ def plan(counts: np.ndarray, n_ranks: int, n_spare: int,
          policy: int = 0, quota_mode: int = 0) -> dict:
     """Quota plan for one layer from its ``counts`` (int32 ``[E]``).
     ``policy`` 0: least-loaded destination; 1: best fit for a chunk the
-    least-loaded rank would not fill. ``quota_mode`` 0: Q = ceil(total /
-    R); 1: the lowest of 64 raised quotas at which nothing is left."""
+    least-loaded rank would not fill; 2: best fit with the candidates in
+    covering order (amounts one rank can take first, smallest first, then
+    the rest, largest first; fixed at the plain quota). ``quota_mode`` 0:
+    Q = ceil(total / R); 1: the lowest of 64 raised quotas at which
+    nothing is left."""
     c = np.ascontiguousarray(counts, dtype=np.int32).reshape(-1)
     E, R, S = c.size, int(n_ranks), int(n_spare)
     if E % R != 0:

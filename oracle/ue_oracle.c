@@ -35,8 +35,10 @@
  *    the replica whose capacity prefix covers j (master first, then replicas
  *    in creation order);
  *    the dispatch permutation is the stable counting sort by physical slot.
- *  Two variants, each one step different (see Step 2): best fit for a
- *  remainder the least-loaded rank would not fill, and a quota search that
+ *  Three variants, each one step different (see Step 2): best fit for a
+ *  remainder the least-loaded rank would not fill; best fit with the
+ *  candidates visited in covering order (amounts one rank can take first,
+ *  smallest first, then the rest, largest first); and a quota search that
  *  raises Q in small steps until the plan is no longer exhausted.
  *
  * Everything is integer; there is nothing to round.
@@ -72,7 +74,8 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  * policy 0: every chunk goes to the least-loaded eligible rank (the rule
  * stated above). policy 1 (best fit): when that rank would be left with
  * room to spare, the chunk goes to the eligible rank with the smallest
- * headroom that still takes all of it, ties to the lowest id.
+ * headroom that still takes all of it, ties to the lowest id. policy 2:
+ * policy 1's destinations, candidates in covering order (greedy_cover_at).
  *
  * quota_mode 0: Q = ceil(sum(counts) / R). quota_mode 1 (quota search):
  * with one spare slot a rank takes one chunk, so a chunk that leaves a
@@ -100,16 +103,14 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  * slot_off the exclusive prefix sum of slot_cap (P+1 entries).
  *
  * Returns 0, or -1 if the shape is not one the slot model covers. */
-/* One greedy pass at quota Q: native loads, candidates, spill loop. Fills
- * load, rem, nfree and the spill records; returns 1 if the plan stopped
- * with excess left (exhausted), else 0. */
-static int greedy_at(const int32_t *counts, int32_t E, int32_t R, int32_t S,
-                     int32_t policy, int64_t Q, int64_t *load, int64_t *rem,
-                     int32_t *nfree, int32_t *cand, int32_t *rec_e,
-                     int32_t *rec_p, int64_t *rec_m, int32_t *nrec_out)
+/* Native placement: every rank's load is the sum of its N native experts'
+ * counts; every expert still holds all its tokens; every rank has all S
+ * spare slots free. */
+static void native_state(const int32_t *counts, int32_t E, int32_t R,
+                         int32_t S, int64_t *load, int64_t *rem,
+                         int32_t *nfree)
 {
     const int32_t N = E / R;
-    const int32_t NS = N + S;
     for (int32_t r = 0; r < R; ++r) {
         load[r] = 0;
         nfree[r] = S;
@@ -118,6 +119,68 @@ static int greedy_at(const int32_t *counts, int32_t E, int32_t R, int32_t S,
         load[e / N] += counts[e];
         rem[e] = counts[e];
     }
+}
+
+/* Destination of an amount m: the least-loaded rank with a free spare slot
+ * and load below Q (ties: lowest id), or -1 if there is none. With best
+ * fit, when that rank could take the whole amount with room to spare, the
+ * eligible rank whose headroom is the smallest that still holds it (the
+ * most loaded such rank; ties: lowest id). */
+static int32_t pick_destination(const int64_t *load, const int32_t *nfree,
+                                int32_t R, int64_t Q, int64_t m, int best_fit)
+{
+    /* ascending scan with a strict comparison keeps the lowest rank id
+     * among ties */
+    int32_t d = -1;
+    for (int32_t x = 0; x < R; ++x) {
+        if (nfree[x] <= 0 || load[x] >= Q)
+            continue;
+        if (d < 0 || load[x] < load[d])
+            d = x;
+    }
+    if (d >= 0 && best_fit && m < Q - load[d]) {
+        int32_t b = d;
+        for (int32_t x = 0; x < R; ++x) {
+            if (nfree[x] > 0 && load[x] < Q && Q - load[x] >= m &&
+                load[x] > load[b])
+                b = x;
+        }
+        d = b;
+    }
+    return d;
+}
+
+/* Moves a chunk of expert e (home rank r) into d's lowest free spare slot:
+ * the amount m capped by d's headroom. Records (expert, slot, chunk) and
+ * returns the chunk. */
+static int64_t place_chunk(int32_t e, int32_t r, int32_t d, int64_t m,
+                           int64_t Q, int32_t N, int32_t S, int64_t *load,
+                           int64_t *rem, int32_t *nfree, int32_t *rec_e,
+                           int32_t *rec_p, int64_t *rec_m, int32_t *nrec)
+{
+    if (Q - load[d] < m)
+        m = Q - load[d];
+    rec_e[*nrec] = e;
+    rec_p[*nrec] = d * (N + S) + N + (S - nfree[d]);
+    rec_m[*nrec] = m;
+    ++*nrec;
+    rem[e] -= m;
+    load[r] -= m;
+    load[d] += m;
+    nfree[d] -= 1;
+    return m;
+}
+
+/* One greedy pass at quota Q for policies 0 and 1: native loads,
+ * candidates, spill loop. Fills load, rem, nfree and the spill records;
+ * returns 1 if the plan stopped with excess left (exhausted), else 0. */
+static int greedy_at(const int32_t *counts, int32_t E, int32_t R, int32_t S,
+                     int32_t policy, int64_t Q, int64_t *load, int64_t *rem,
+                     int32_t *nfree, int32_t *cand, int32_t *rec_e,
+                     int32_t *rec_p, int64_t *rec_m, int32_t *nrec_out)
+{
+    const int32_t N = E / R;
+    native_state(counts, E, R, S, load, rem, nfree);
 
     /* Candidates: experts of overloaded ranks, heaviest first (count desc,
      * id asc). Plain insertion sort. */
@@ -138,58 +201,147 @@ static int greedy_at(const int32_t *counts, int32_t E, int32_t R, int32_t S,
         cand[i] = e;
     }
 
-    /* Spill loop. */
+    /* Spill loop: the amount is the smallest of the source's excess and
+     * the expert's remaining tokens. */
     int exhausted = 0;
     int32_t nrec = 0;
     for (int32_t c = 0; c < ncand && !exhausted; ++c) {
         const int32_t e = cand[c];
         const int32_t r = e / N;
         while (load[r] > Q && rem[e] > 0) {
-            /* least-loaded eligible destination; ascending scan with a
-             * strict comparison keeps the lowest rank id among ties */
-            int32_t d = -1;
-            for (int32_t x = 0; x < R; ++x) {
-                if (nfree[x] <= 0 || load[x] >= Q)
-                    continue;
-                if (d < 0 || load[x] < load[d])
-                    d = x;
-            }
+            int64_t m = load[r] - Q;
+            if (rem[e] < m)
+                m = rem[e];
+            const int32_t d = pick_destination(load, nfree, R, Q, m,
+                                               policy == 1);
             if (d < 0) {
                 exhausted = 1;
                 break;
             }
-            int64_t m = load[r] - Q;
-            if (rem[e] < m)
-                m = rem[e];
-            /* Policy 1, best fit: when the least-loaded rank could take
-             * the whole amount with room to spare, send it instead to the
-             * eligible rank whose headroom is the smallest that still
-             * holds it (the most loaded such rank; ties: lowest id). */
-            if (policy == 1 && m < Q - load[d]) {
-                int32_t b = d;
-                for (int32_t x = 0; x < R; ++x) {
-                    if (nfree[x] > 0 && load[x] < Q && Q - load[x] >= m &&
-                        load[x] > load[b])
-                        b = x;
-                }
-                d = b;
-            }
-            if (Q - load[d] < m)
-                m = Q - load[d];
-            /* lowest free spare slot of d */
-            const int32_t p = d * NS + N + (S - nfree[d]);
-            rec_e[nrec] = e;
-            rec_p[nrec] = p;
-            rec_m[nrec] = m;
-            ++nrec;
-            rem[e] -= m;
-            load[r] -= m;
-            load[d] += m;
-            nfree[d] -= 1;
+            place_chunk(e, r, d, m, Q, N, S, load, rem, nfree, rec_e, rec_p,
+                        rec_m, &nrec);
         }
     }
     *nrec_out = nrec;
     return exhausted;
+}
+
+/* Each expert's amount at quota M: a rank above M sheds its excess from
+ * its experts heaviest first (count desc, id asc), each giving what it has
+ * of what is still left (0 for experts of other ranks). The next expert is
+ * the heaviest of those after the previous one in that order. */
+static void amounts_at(const int32_t *counts, int32_t E, int32_t R,
+                       const int64_t *load, int64_t M, int64_t *amt)
+{
+    const int32_t N = E / R;
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t left = load[r] - M;
+        int32_t prev = -1;
+        for (int32_t k = 0; k < N; ++k) {
+            int32_t best = -1;
+            for (int32_t i = 0; i < N; ++i) {
+                const int32_t e = r * N + i;
+                const int after = prev < 0 || counts[e] < counts[prev] ||
+                                  (counts[e] == counts[prev] && e > prev);
+                if (!after)
+                    continue;
+                if (best < 0 || counts[e] > counts[best])
+                    best = e;
+            }
+            prev = best;
+            amt[best] = left > 0 ? (counts[best] < left ? counts[best] : left)
+                                 : 0;
+            left -= amt[best];
+        }
+    }
+}
+
+/* Policy 2 (best fit in covering order): the destination rule of policy 1,
+ * with the candidates visited in another order. With one spare slot per
+ * rank a destination takes one chunk, so the destinations are pieces that
+ * the sources' excesses must cover; a large excess spends the big pieces,
+ * and a small excess that comes last finds only big pieces, or none. So
+ * the amounts that one rank can take are placed first, smallest first,
+ * then the others, largest first. The order is fixed once, from the plain
+ * quota Q0:
+ *   - every expert of a rank whose load exceeds Q0 is a candidate;
+ *   - its amount at a quota M is given by amounts_at;
+ *   - H0 is the largest headroom Q0 - load among ranks with a spare slot
+ *     and load below Q0 (0 if there is none);
+ *   - candidates with amount at Q0 at most H0 come first, by (amount asc,
+ *     id asc); then the others, by (amount desc, id asc).
+ * At the pass's quota Q each candidate in that order places its amount at
+ * Q, chunk by chunk, into the destination policy 1 would choose. */
+static int greedy_cover_at(const int32_t *counts, int32_t E, int32_t R,
+                           int32_t S, int64_t Q0, int64_t Q, int64_t *load,
+                           int64_t *rem, int32_t *nfree, int32_t *cand,
+                           int32_t *rec_e, int32_t *rec_p, int64_t *rec_m,
+                           int32_t *nrec_out, int64_t *amt0, int64_t *amt)
+{
+    const int32_t N = E / R;
+    native_state(counts, E, R, S, load, rem, nfree);
+    amounts_at(counts, E, R, load, Q0, amt0);
+    amounts_at(counts, E, R, load, Q, amt);
+    int64_t H0 = 0;
+    for (int32_t r = 0; r < R; ++r)
+        if (S > 0 && load[r] < Q0 && Q0 - load[r] > H0)
+            H0 = Q0 - load[r];
+
+    /* candidates in covering order (insertion sort on the key above) */
+    int32_t ncand = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        if (load[e / N] <= Q0)
+            continue;
+        int32_t i = ncand++;
+        while (i > 0) {
+            const int32_t p = cand[i - 1];
+            const int gp = amt0[p] > H0, ge = amt0[e] > H0;
+            int before;
+            if (gp != ge)
+                before = gp < ge;
+            else if (amt0[p] != amt0[e])
+                before = ge ? amt0[p] > amt0[e] : amt0[p] < amt0[e];
+            else
+                before = p < e;
+            if (before)
+                break;
+            cand[i] = p;
+            --i;
+        }
+        cand[i] = e;
+    }
+
+    int exhausted = 0;
+    int32_t nrec = 0;
+    for (int32_t c = 0; c < ncand && !exhausted; ++c) {
+        const int32_t e = cand[c];
+        int64_t need = amt[e];
+        while (need > 0) {
+            const int32_t d = pick_destination(load, nfree, R, Q, need, 1);
+            if (d < 0) {
+                exhausted = 1;
+                break;
+            }
+            need -= place_chunk(e, e / N, d, need, Q, N, S, load, rem, nfree,
+                                rec_e, rec_p, rec_m, &nrec);
+        }
+    }
+    *nrec_out = nrec;
+    return exhausted;
+}
+
+/* One pass of the policy's rule at quota M (Q0: the plain quota). */
+static int pass_at(int32_t policy, const int32_t *counts, int32_t E,
+                   int32_t R, int32_t S, int64_t Q0, int64_t M, int64_t *load,
+                   int64_t *rem, int32_t *nfree, int32_t *cand,
+                   int32_t *rec_e, int32_t *rec_p, int64_t *rec_m,
+                   int32_t *nrec, int64_t *amt0, int64_t *amt)
+{
+    if (policy == 2)
+        return greedy_cover_at(counts, E, R, S, Q0, M, load, rem, nfree,
+                               cand, rec_e, rec_p, rec_m, nrec, amt0, amt);
+    return greedy_at(counts, E, R, S, policy, M, load, rem, nfree, cand,
+                     rec_e, rec_p, rec_m, nrec);
 }
 
 int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
@@ -198,7 +350,7 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
              int32_t *slot_expert, int32_t *slot_cap, int32_t *slot_off,
              int32_t *load_before, int32_t *load_after)
 {
-    if (E <= 0 || R <= 0 || S < 0 || E % R != 0)
+    if (E <= 0 || R <= 0 || S < 0 || E % R != 0 || policy < 0 || policy > 2)
         return -1;
     const int32_t N = E / R;       /* native experts per rank */
     const int32_t NS = N + S;      /* physical slots per rank */
@@ -212,9 +364,13 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
     int32_t *rec_e = calloc((size_t)(R * S + 1), sizeof(int32_t));
     int32_t *rec_p = calloc((size_t)(R * S + 1), sizeof(int32_t));
     int64_t *rec_m = calloc((size_t)(R * S + 1), sizeof(int64_t));
-    if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m) {
+    /* policy 2: each candidate's amount at Q0 and at the pass's quota */
+    int64_t *amt0 = calloc((size_t)E, sizeof(int64_t));
+    int64_t *amt = calloc((size_t)E, sizeof(int64_t));
+    if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m ||
+        !amt0 || !amt) {
         free(load); free(rem); free(nfree); free(cand);
-        free(rec_e); free(rec_p); free(rec_m);
+        free(rec_e); free(rec_p); free(rec_m); free(amt0); free(amt);
         return -1;
     }
 
@@ -240,15 +396,16 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
         const int64_t step = (Q0 + 255) / 256;
         for (int32_t j = 0; j < 64; ++j) {
             const int64_t M = Q0 + j * step;
-            if (!greedy_at(counts, E, R, S, policy, M, load, rem, nfree, cand,
-                           rec_e, rec_p, rec_m, &nrec)) {
+            if (!pass_at(policy, counts, E, R, S, Q0, M, load, rem, nfree,
+                         cand, rec_e, rec_p, rec_m, &nrec, amt0, amt)) {
                 Q = M;
                 break;
             }
         }
     }
-    const int exhausted = greedy_at(counts, E, R, S, policy, Q, load, rem,
-                                    nfree, cand, rec_e, rec_p, rec_m, &nrec);
+    const int exhausted = pass_at(policy, counts, E, R, S, Q0, Q, load, rem,
+                                  nfree, cand, rec_e, rec_p, rec_m, &nrec,
+                                  amt0, amt);
 
     /* Replica table: master first (keeps what was not spilled), then the
      * spilled replicas in creation order. */
@@ -299,7 +456,7 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
     scalars[3] = n;
 
     free(load); free(rem); free(nfree); free(cand);
-    free(rec_e); free(rec_p); free(rec_m);
+    free(rec_e); free(rec_p); free(rec_m); free(amt0); free(amt);
     return 0;
 }
 

@@ -139,6 +139,50 @@ def check_load(routing, E):
     return counts[0]
 
 
+def rank_amounts(counts, R, Q):
+    """Each expert's amount at quota Q: a rank above Q sheds its excess
+    from its experts heaviest first (count desc, id asc), each giving what
+    it has of what is still left."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    N = E // R
+    amt = np.zeros(E, np.int64)
+    for r in range(R):
+        left = int(counts[r * N:(r + 1) * N].sum()) - Q
+        for e in sorted(range(r * N, (r + 1) * N),
+                        key=lambda e: (-counts[e], e)):
+            take = max(0, min(int(counts[e]), left))
+            amt[e] = take
+            left -= take
+    return amt
+
+
+def visit_order(counts, R, S, policy, Q):
+    """Candidates (experts of ranks above the quota that fixes the order)
+    in the order the rule visits them, and the amount each must place at
+    Q. Policies 0 and 1: experts of ranks above Q, count desc, id asc.
+    Policy 2: experts of ranks above Q0 = ceil(total / R); first those
+    whose amount at Q0 is at most H0 (the largest headroom at Q0 among
+    ranks with a spare slot), by amount asc, id asc; then the others by
+    amount desc, id asc."""
+    counts = np.asarray(counts, np.int64)
+    E = counts.size
+    N = E // R
+    L = counts.reshape(R, N).sum(axis=1)
+    if policy != 2:
+        cands = sorted((e for e in range(E) if L[e // N] > Q),
+                       key=lambda e: (-counts[e], e))
+        return cands, rank_amounts(counts, R, Q)
+    Q0 = -(-int(counts.sum()) // R)
+    a0 = rank_amounts(counts, R, Q0)
+    H0 = max([Q0 - int(L[r]) for r in range(R) if S > 0 and L[r] < Q0],
+             default=0)
+    cands = [e for e in range(E) if L[e // N] > Q0]
+    small = sorted((e for e in cands if a0[e] <= H0), key=lambda e: (a0[e], e))
+    big = sorted((e for e in cands if a0[e] > H0), key=lambda e: (-a0[e], e))
+    return small + big, rank_amounts(counts, R, Q)
+
+
 def exhausts_at(counts, R, S, policy, Q):
     """Runs the planning rule at quota Q from scratch and says whether it
     stops with excess left: candidates by count desc, id asc; each chunk to
@@ -150,16 +194,16 @@ def exhausts_at(counts, R, S, policy, Q):
     N = E // R
     L = counts.reshape(R, N).sum(axis=1).astype(np.int64)
     free = np.full(R, S)
-    for e in sorted((e for e in range(E) if L[e // N] > Q),
-                    key=lambda e: (-counts[e], e)):
-        r, rem = e // N, int(counts[e])
+    order, amt = visit_order(counts, R, S, policy, Q)
+    for e in order:
+        r, rem = e // N, int(amt[e])
         while L[r] > Q and rem > 0:
             elig = [x for x in range(R) if free[x] > 0 and L[x] < Q]
             if not elig:
                 return True
             need = min(int(L[r] - Q), rem)
             d = min(elig, key=lambda x: (L[x], x))
-            if policy == 1 and need < Q - L[d]:
+            if policy >= 1 and need < Q - L[d]:
                 d = min((x for x in elig if Q - L[x] >= need),
                         key=lambda x: (Q - L[x], x))
             m = min(need, int(Q - L[d]))
@@ -306,8 +350,7 @@ def check_choices(counts, R, S, policy, pl):
     Q = pl["quota"]
     L = counts.reshape(R, N).sum(axis=1).astype(np.int64)
     free = np.full(R, S)
-    cands = sorted((e for e in range(E) if L[e // N] > Q),
-                   key=lambda e: (-counts[e], e))
+    cands, amt = visit_order(counts, R, S, policy, Q)
     stopped = False
     for e in cands:
         chunks = [(int(pl["rep_slot"][i]), int(pl["rep_cap"][i]))
@@ -315,7 +358,7 @@ def check_choices(counts, R, S, policy, pl):
         if stopped:
             assert not chunks, "nothing moves after the plan stops"
             continue
-        r, rem = e // N, int(counts[e])
+        r, rem = e // N, int(amt[e])
         while L[r] > Q and rem > 0:
             elig = [x for x in range(R) if free[x] > 0 and L[x] < Q]
             if not elig:
@@ -328,7 +371,7 @@ def check_choices(counts, R, S, policy, pl):
             need = min(int(L[r] - Q), rem)
             least = min(elig, key=lambda x: (L[x], x))
             want = least
-            if policy == 1 and need < Q - L[least]:
+            if policy >= 1 and need < Q - L[least]:
                 fits = [x for x in elig if Q - L[x] >= need]
                 want = min(fits, key=lambda x: (Q - L[x], x))
             assert d == want, f"expert {e}: chunk to rank {d}, rule says {want}"

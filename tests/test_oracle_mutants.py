@@ -62,7 +62,7 @@ MUTANTS = {
                                "residual = load[r] - Q;"),
     "quota counts experts": ("(total + R - 1) / R", "(total + E - 1) / E"),
     "no exhausted flag": ("exhausted = 1;\n                break;",
-                          "break;"),
+                          "break;", 2),
     "best fit takes the most headroom": ("load[x] > load[b])",
                                          "load[x] < load[b])"),
     "best fit ties highest id": ("load[x] > load[b])", "load[x] >= load[b])"),
@@ -73,8 +73,8 @@ MUTANTS = {
     "search skips the plain quota": ("for (int32_t j = 0; j < 64; ++j)",
                                      "for (int32_t j = 1; j < 64; ++j)"),
     "plan made at the plain quota": (
-        "const int exhausted = greedy_at(counts, E, R, S, policy, Q, load,",
-        "const int exhausted = greedy_at(counts, E, R, S, policy, Q0, load,"),
+        "const int exhausted = pass_at(policy, counts, E, R, S, Q0, Q, load,",
+        "const int exhausted = pass_at(policy, counts, E, R, S, Q0, Q0, load,"),
     "search grain 128": ("(Q0 + 255) / 256", "(Q0 + 127) / 128"),
     "search 32 steps": ("for (int32_t j = 0; j < 64; ++j)",
                         "for (int32_t j = 0; j < 32; ++j)"),
@@ -97,6 +97,28 @@ MUTANTS = {
         "        if (hit < 0) {\n            ++faults;\n            continue;\n        }",
         "        if (hit < 0) {\n            hit = rep_off[e + 1] - 1;\n"
         "            prefix -= rep_cap[hit];\n        }"),
+    "cover: small amounts largest first": (
+        "before = ge ? amt0[p] > amt0[e] : amt0[p] < amt0[e];",
+        "before = amt0[p] > amt0[e];"),
+    "cover: large amounts smallest first": (
+        "before = ge ? amt0[p] > amt0[e] : amt0[p] < amt0[e];",
+        "before = amt0[p] < amt0[e];"),
+    "cover: amount equal to H0 counted as large": (
+        "const int gp = amt0[p] > H0, ge = amt0[e] > H0;",
+        "const int gp = amt0[p] >= H0, ge = amt0[e] >= H0;"),
+    "cover: large amounts first": ("before = gp < ge;", "before = gp > ge;"),
+    "cover: H0 at the pass's quota": (
+        "if (S > 0 && load[r] < Q0 && Q0 - load[r] > H0)\n            H0 = Q0 - load[r];",
+        "if (S > 0 && load[r] < Q && Q - load[r] > H0)\n            H0 = Q - load[r];"),
+    "cover: order from the pass's amounts": (
+        "amounts_at(counts, E, R, load, Q0, amt0);",
+        "amounts_at(counts, E, R, load, Q, amt0);"),
+    "cover: amounts from the lightest expert": (
+        "                if (best < 0 || counts[e] > counts[best])\n                    best = e;\n            }\n            prev = best;",
+        "                if (best < 0 || counts[e] < counts[best])\n                    best = e;\n            }\n            prev = best;"),
+    "cover: least loaded instead of best fit": (
+        "pick_destination(load, nfree, R, Q, need, 1)",
+        "pick_destination(load, nfree, R, Q, need, 0)"),
     "replica before master": ("rep_slot[n] = (e / N) * NS + (e % N);\n"
                               "        rep_cap[n] = (int32_t)rem[e];\n"
                               "        ++n;\n",
@@ -117,6 +139,11 @@ def run_all_pins():
     for _ in range(150):
         pins.check_instance(*pins.random_instance(rng), policy=1,
                             quota_mode=1)
+    for _ in range(300):
+        pins.check_instance(*pins.random_instance(rng), policy=2)
+    for _ in range(150):
+        pins.check_instance(*pins.random_instance(rng), policy=2,
+                            quota_mode=1)
     pins.check_no_spares(np.random.default_rng(1))
     pins.check_one_rank(np.random.default_rng(2))
     pins.check_balanced()
@@ -129,9 +156,11 @@ CAUGHT = 3
 
 
 def build_mutant(name, tmp_path):
-    old, new = MUTANTS[name]
+    old, new, *times = MUTANTS[name]
+    times = times[0] if times else 1     # sites the mistake is planted at
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+    assert src.count(old) == times, \
+        f"mutation site for '{name}' found {src.count(old)} times"
     mutated = tmp_path / "mutant.c"
     mutated.write_text(src.replace(old, new))
     return oracle.build(out=str(tmp_path / "libmutant.so"), src=str(mutated),

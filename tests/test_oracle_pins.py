@@ -11,9 +11,9 @@ def test_golden(case):
     pins.check_golden(case)
 
 
-RULES = [(0, 0), (1, 0), (0, 1), (1, 1)]
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1)]
 RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
-            "best_fit_search"]
+            "best_fit_search", "cover", "cover_search"]
 
 
 @pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
@@ -45,7 +45,7 @@ def test_quota_search_large_quota():
         E = R * N
         k = int(min(E, 4))
         routing = pins.random_routing(rng, 6000, E, k, float(rng.uniform(0.8, 2)))
-        for policy in (0, 1):
+        for policy in (0, 1, 2):
             pl = pins.check_instance(routing, E, R, 1, policy=policy,
                                      quota_mode=1)
             assert pl["quota"] >= 256     # the step is above one token here
