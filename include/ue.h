@@ -78,8 +78,9 @@ typedef enum ue_status {
  *   topk k             experts per token, 1..E
  *   max_tokens         largest T of any call (T*k < 2^30)
  *   max_layers         largest L (layers or microbatches) of any call
- *   plan_policy        destination rule of the planner (see ue_plan):
- *                      UE_PLAN_LEAST_LOADED (0) or UE_PLAN_BEST_FIT (1)
+ *   plan_policy        rule of the planner (see ue_plan):
+ *                      UE_PLAN_LEAST_LOADED (0), UE_PLAN_BEST_FIT (1) or
+ *                      UE_PLAN_BEST_FIT_COVER (2)
  *   quota_mode         how the planner sets the quota (see ue_plan):
  *                      UE_QUOTA_FIXED (0) or UE_QUOTA_SEARCH (1)           */
 typedef struct ue_config {
@@ -95,9 +96,12 @@ typedef struct ue_config {
 
 enum {
     UE_PLAN_LEAST_LOADED = 0,  /* every chunk to the least-loaded rank     */
-    UE_PLAN_BEST_FIT = 1       /* a chunk the least-loaded rank would not
+    UE_PLAN_BEST_FIT = 1,      /* a chunk the least-loaded rank would not
                                   fill goes to the eligible rank with the
                                   smallest headroom that holds it          */
+    UE_PLAN_BEST_FIT_COVER = 2 /* best fit, candidates in covering order:
+                                  amounts one rank can take first, smallest
+                                  first, then the rest, largest first      */
 };
 
 enum {
@@ -186,6 +190,15 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
  *   expert remainder) is below the least-loaded rank's headroom, it goes
  *   whole to the eligible rank with the smallest headroom >= the amount
  *   (ties: lowest id) instead.
+ *   UE_PLAN_BEST_FIT_COVER places chunks as UE_PLAN_BEST_FIT does but
+ *   visits the candidates in covering order, fixed at Q0: a candidate's
+ *   amount at a quota is what its rank must shed below it that the rank's
+ *   heavier experts (count desc, id asc) do not; H0 is the largest
+ *   headroom Q0 - load among ranks with a spare slot; candidates whose
+ *   amount at Q0 is at most H0 come first (amount asc, id asc), then the
+ *   others (amount desc, id asc); each places its amount at the pass's
+ *   quota. With one spare slot per rank every destination takes one
+ *   chunk, and this order keeps the small pieces for the small amounts.
  *   Under UE_QUOTA_SEARCH the plan above is made at the quotas
  *   Q0 + j*ceil(Q0/256), j = 0..63 (Q0 = ceil(sum(counts)/R)), in order,
  *   and the first that leaves nothing over is kept; with none, Q0 stands.

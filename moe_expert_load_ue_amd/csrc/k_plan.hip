@@ -16,6 +16,13 @@
 //   the least-loaded rank's headroom, it goes whole to the eligible rank
 //   with the smallest headroom that still holds it (ties: lowest id), so
 //   partly filled ranks close up instead of many ranks each taking a bit.
+//   A third rule (best fit in covering order) keeps best fit's destinations
+//   and changes the order of the candidates: with one spare slot per rank
+//   each destination takes one chunk, so the destinations are pieces the
+//   sources' excesses must cover, and a small excess left for last finds
+//   only big pieces, or none. The amounts one rank can take at Q0 (at most
+//   the largest headroom there) go first, smallest first, then the others,
+//   largest first; the order is fixed once, at Q0.
 //   The quota search (also per context) makes the same plan at the quotas
 //   Q0 + j * ceil(Q0 / 256), j = 0..63, in order, and keeps the first that
 //   leaves nothing over (with none, Q0 stands): the pages call the
@@ -26,7 +33,8 @@
 //   A. all threads: counts and rank loads into LDS, Q0, the candidate list
 //      and the list of ranks that can receive (compacted together by one
 //      scan, then each ranked by comparison counting, four threads per
-//      item: exact, and no sort network);
+//      item: exact, and no sort network; the covering order ranks the
+//      candidates a second time, by their amounts at Q0);
 //   B. one wave per greedy pass, with the pass's state in registers. The
 //      least-loaded eligible rank is the smaller of two minima: the next
 //      entry of the receiving list, sorted once by (load, id) in part A
@@ -50,6 +58,7 @@ namespace {
 struct PlanLds {
     int32_t *cnt, *rem, *load, *cand, *sorted, *first_rec, *nrec_e;
     int32_t *dkey, *dsorted, *scount, *slimit;
+    int32_t *camt, *clim;       // covering order: amount at Q0, limit
     int32_t *rec_e, *rec_p, *rec_m, *slot_cap, *slot_exp, *rep_off;
 };
 
@@ -75,6 +84,8 @@ __device__ __forceinline__ PlanLds carve(int32_t *base, int E, int R, int S,
     s.dsorted = p; p += R;
     s.scount = p; p += E;
     s.slimit = p; p += E;
+    s.camt = p; p += E;
+    s.clim = p; p += E;
     s.rec_e = p;
     s.rec_p = p + R * S;
     s.rec_m = p + 2 * R * S;
@@ -677,6 +688,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // every kSplit-th other one; their sums meet through lane swaps)
     constexpr int kSplit = 4;
     static_assert(kSplit == 4, "quad_sum joins the four threads of a candidate");
+    const bool cover = policy == UE_PLAN_BEST_FIT_COVER;
     const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
     for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
         const int i = i0 + tid / kSplit;
@@ -700,9 +712,17 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         pos = quad_sum(pos);
         before = quad_sum(before);
         if (act && q == 0) {
-            s.sorted[pos] = e;
-            s.scount[pos] = c;
-            s.slimit[pos] = s.load[r] - before;
+            if (cover) {
+                // placed below, by its amount at Q0 instead
+                const int lim = s.load[r] - before;
+                const int a = lim - Q0;
+                s.camt[i] = a <= 0 ? 0 : (a < c ? a : c);
+                s.clim[i] = lim;
+            } else {
+                s.sorted[pos] = e;
+                s.scount[pos] = c;
+                s.slimit[pos] = s.load[r] - before;
+            }
         }
     }
     // the receiving ranks placed by their rank among the keys (distinct,
@@ -722,8 +742,48 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         if (act && q == 0) s.dsorted[pos] = static_cast<int32_t>(k);
     }
     __syncthreads();
+    if (cover) {
+        // Covering order. H0, the largest headroom at Q0 among ranks with
+        // a spare slot, comes from the smallest receiving key (the list
+        // holds every rank with a spare slot and load below the highest
+        // quota tried, sorted); amounts at Q0 up to H0 go first, smallest
+        // first, then the larger ones, largest first (ties: lowest id)
+        const int minload = nd > 0
+            ? static_cast<int>(static_cast<uint32_t>(s.dsorted[0]) >> rbits)
+            : Q0;
+        const int H0 = minload < Q0 ? Q0 - minload : 0;
+        for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
+            const int i = i0 + tid / kSplit;
+            const int q = tid % kSplit;
+            const bool act = i < ncand;
+            const int2 me = act ? cand2[i] : int2{0, 0};
+            const int e = me.x & 0xFFFF;
+            const int a = act ? s.camt[i] : 0;
+            const bool big = a > H0;
+            int pos = 0;
+            if (act) {
+#pragma unroll 4
+                for (int j = q; j < ncand; j += kSplit) {
+                    const int aj = s.camt[j];
+                    const bool bj = aj > H0;
+                    const int f = cand2[j].x & 0xFFFF;
+                    const bool earlier =
+                        bj != big ? !bj
+                                  : (aj != a ? (big ? aj > a : aj < a) : f < e);
+                    pos += earlier;
+                }
+            }
+            pos = quad_sum(pos);
+            if (act && q == 0) {
+                s.sorted[pos] = e;
+                s.scount[pos] = me.y;
+                s.slimit[pos] = s.clim[i];
+            }
+        }
+        __syncthreads();
+    }
 
-    const bool best_fit = policy == UE_PLAN_BEST_FIT;
+    const bool best_fit = policy != UE_PLAN_LEAST_LOADED;
     const int wave = tid >> 6;
     // ---- B. greedy passes. Quota search: rounds of one pass per wave over
     // the quotas in order; the first round with a quota that leaves nothing
@@ -882,7 +942,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
 
 size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave) {
     const size_t regions = per_wave ? kPlanWaves : 1;
-    return sizeof(int32_t) * (static_cast<size_t>(10) * E + 1 + 3 * R +
+    return sizeof(int32_t) * (static_cast<size_t>(12) * E + 1 + 3 * R +
                               regions * 3 * R * S + 2 * P);
 }
 

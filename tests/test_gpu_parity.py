@@ -22,9 +22,9 @@ def make_ctx(E, R, S, k, T, L=1, policy=ue.PLAN_LEAST_LOADED,
 
 # (destination rule, quota mode): the default, best fit, and each with the
 # quota search
-RULES = [(0, 0), (1, 0), (0, 1), (1, 1)]
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1)]
 RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
-            "best_fit_search"]
+            "best_fit_search", "cover", "cover_search"]
 
 
 @pytest.mark.parametrize("case", [g for g in pins.golden_cases()
@@ -193,7 +193,7 @@ def test_many_layers_ragged_wide_load_groups():
 @pytest.mark.parametrize("name", ["tiny", "large_ep", "pipeline", "dsv3"])
 def test_configs_full_size(name, fused, policy, quota_mode):
     """Every routing workload at its full size, every layer, bit-exact, as
-    three calls and as one ue_rebalance call, under both planner rules."""
+    three calls and as one ue_rebalance call, under every planner rule."""
     cfg = W.CONFIGS[name]
     say("full size", name, "fused" if fused else "calls", "policy", policy,
         "quota_mode", quota_mode)
@@ -374,6 +374,6 @@ def test_refusals_leave_outputs_untouched():
         with pytest.raises(ue.UEError):
             ue.Context(*bad, 100, 1, device=DEV)
     with pytest.raises(ue.UEError):
-        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=2)
+        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=3)
     with pytest.raises(ue.UEError):
         ue.Context(64, 8, 1, 8, 100, 1, device=DEV, quota_mode=2)

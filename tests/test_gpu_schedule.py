@@ -87,8 +87,9 @@ def as_result(ctx, outs):
     return res
 
 
-@pytest.mark.parametrize("policy,quota_mode", [(0, 0), (1, 1)],
-                         ids=["least_loaded", "best_fit_search"])
+@pytest.mark.parametrize("policy,quota_mode", [(0, 0), (1, 1), (2, 1)],
+                         ids=["least_loaded", "best_fit_search",
+                              "cover_search"])
 def test_plan_driven_sync_restore_reduce(policy, quota_mode):
     E, R, S, k, T = 32, 8, 2, 4, 3000
     rng = np.random.default_rng(5 + policy)
