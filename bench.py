@@ -97,7 +97,7 @@ def phase_times(rb, steps):
     ``steps`` calls."""
     ue = rb.ue
     ue.ue_set_timing(rb.ctx, True)
-    t = {"k_load": [], "k_plan": [], "k_reroute": []}
+    t = {"k_count": [], "k_plan": [], "k_reroute": []}
     for _ in range(steps):
         rb.step()
         ms = ue.ue_kernel_times(rb.ctx)

@@ -38,13 +38,15 @@
  *    the registered tables are not replaced meanwhile.
  *  - All shapes are int32; the number of assignments per layer, T*k, must
  *    stay below 2^30.
- *  - Workgroups of one launch combine per-tile counts through bounded waits
- *    on each other (decoupled lookback). A wait that outlasts the context's
- *    wait limit (ue_set_wait_limit) gives up, and every kernel still runs
- *    to its end; the layer is then marked poisoned: bit 30 (0x40000000,
- *    UE_POISONED) is set in that layer's `invalid` (ue_load, ue_rebalance)
- *    and `faults` (ue_reroute, ue_rebalance) words, the other bits keep
- *    their counts, and the layer's other outputs are unspecified.
+ *  - The workgroups of ue_reroute combine per-tile counts through bounded
+ *    waits on each other (decoupled lookback); no other call waits across
+ *    workgroups (ue_load and ue_rebalance count every tile on its own and
+ *    scan the counts in the planner's launch). A wait that outlasts the
+ *    context's wait limit (ue_set_wait_limit) gives up, and every kernel
+ *    still runs to its end; the layer is then marked poisoned: bit 30
+ *    (0x40000000, UE_POISONED) is set in that layer's `faults` word, the
+ *    other bits keep their counts, and the layer's other outputs are
+ *    unspecified.
  */
 #ifndef UE_H
 #define UE_H
@@ -268,12 +270,12 @@ int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
 int ue_stale_loads(ue_ctx *ctx, const void *placement, const int32_t *counts,
                    int32_t L, int32_t *rank_loads, void *stream);
 
-/* Polls one cross-workgroup wait may take before it gives up and marks
- * its layer poisoned (see the conventions above); default 4,194,304, far
- * beyond any wait of a healthy device. 0 makes every wait give up without
- * polling, so every layer with more than one tile group is marked: a way to
- * exercise the error path with every kernel still ending normally.
- * Applies to later calls on the context. */
+/* Polls one cross-workgroup wait of ue_reroute may take before it gives up
+ * and marks its layer poisoned (see the conventions above); default
+ * 4,194,304, far beyond any wait of a healthy device. 0 makes every wait
+ * give up without polling, so every layer of more than one routing tile is
+ * marked: a way to exercise the error path with every kernel still ending
+ * normally. Applies to later calls on the context. */
 int ue_set_wait_limit(ue_ctx *ctx, uint32_t polls);
 
 /* ue_rebalance without a context and without allocating: for callers
@@ -286,14 +288,14 @@ int ue_set_wait_limit(ue_ctx *ctx, uint32_t polls);
  * the library, which every device the library runs on holds until the
  * process ends. A call needs, with tiles = max(1, ceil(T*k / 2048)) and
  * groups = ceil(tiles / 8), each term rounded up to 256 bytes:
- *   8 L + 8 L groups E + 4 L + 4 L groups E + 2 L (tiles + groups) E
- * bytes (the 58-layer dsv3 rebalance, E=256, T=65536, k=8: 14.3 MB). A call
+ *   4 L groups E + 2 L (tiles + groups) E
+ * bytes (the 58-layer dsv3 rebalance, E=256, T=65536, k=8: 10.5 MB). A call
  * needing more is refused with UE_ESHAPE before anything is launched.
- * Each call first clears the ticket and lookback words it uses with a
- * fill kernel on `stream` (no memset, so the call may be captured in a
- * graph). Calls share the array: calls that overlap in time on one device
- * race and give wrong results; order them on one stream. The first call on
- * a device looks up the array's address there (hipGetSymbolAddress).
+ * Every scratch word a call reads it has written itself, so nothing is
+ * cleared between calls (and the call may be captured in a graph). Calls
+ * share the array: calls that overlap in time on one device race and give
+ * wrong results; order them on one stream. The first call on a device
+ * looks up the array's address there (hipGetSymbolAddress).
  * Calls no allocation routine. Error text: ue_last_error(NULL). */
 #define UE_STATIC_SCRATCH_BYTES (16u << 20)
 int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,

@@ -571,11 +571,29 @@ __device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
     }
 }
 
+// The scan that finishes the load: the count kernel left, per group of
+// tiles, each tile's count of every expert in the group's earlier tiles
+// (tile t of group g at row t + g of the per-tile table) and the group's
+// own counts in the row after its last tile; the scan writes each group's
+// base row (the count in all earlier groups) and the layer's counts (and
+// the ids out of range: assignments minus counted ones). Those rows are
+// what the fused reroute reads.
+struct ScanArgs {
+    uint16_t *rows;            // [max_layers][row_stride][E]
+    int32_t *group_base;       // [max_layers][max_groups][E]
+    int64_t A;                 // assignments per layer
+    int tiles, group, row_stride, max_groups;
+    int32_t *counts;           // [L][E] out
+    int32_t *invalid;          // [L] out, may be null
+};
+constexpr int kModeScan = 1;   // finish the load (ScanArgs)
+constexpr int kModePlan = 2;   // make the plan
+
 __global__ __launch_bounds__(kPlanBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
     int P, int rbits, int policy, int quota_mode, int per_wave,
     uint32_t lds_bytes, ue_placement_layout lay,
-    int32_t *__restrict__ placement) {
+    int32_t *__restrict__ placement, int mode, ScanArgs sc) {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kPlanWaves];
     __shared__ int wsum3[3 * kPlanWaves];
@@ -583,9 +601,79 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     __shared__ int s_nrecw[kPlanWaves];
     __shared__ int s_nrec, s_exhausted, s_quota, s_region;
     __shared__ uint32_t wsat[kPlanWaves];
+    __shared__ int scan_tot[kMaxExperts];   // scan: the layer's counts
 
     const int layer = blockIdx.x;
     const int tid = threadIdx.x;
+
+    if (mode & kModeScan) {
+        // Group g's own counts are in the row after its last tile (row
+        // min(tiles, (g + 1) * group) + g); each group's base is the
+        // exclusive prefix of those over earlier groups, and the layer's
+        // counts their sum.
+        const int G = sc.group;
+        const int ng = (sc.tiles + G - 1) / G;
+        const uint16_t *rows =
+            sc.rows + static_cast<int64_t>(layer) * sc.row_stride * E;
+        int32_t *gb = sc.group_base + static_cast<int64_t>(layer) * sc.max_groups * E;
+        auto total_row = [&](int g) {
+            const int tend = (g + 1) * G < sc.tiles ? (g + 1) * G : sc.tiles;
+            return static_cast<int64_t>(tend + g) * E;
+        };
+        // PT threads per expert (E <= kPlanBlock): thread (j, e) sums its
+        // chunk of consecutive groups, the chunks' sums meet in LDS, and
+        // each thread then writes the running base of its own groups. A
+        // thread holds up to 8 group counts in registers; longer chunks
+        // read their counts a second time (from cache).
+        const int PT = kPlanBlock / E;
+        const int j = tid / E, e = tid - j * E;
+        const int cs = (ng + PT - 1) / PT;
+        const int g0 = j < PT ? j * cs : ng;
+        const int g1 = g0 + cs < ng ? g0 + cs : ng;
+        int y[8];
+        auto load8 = [&](int b) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                y[q] = b + q < g1 ? static_cast<int>(rows[total_row(b + q) + e]) : 0;
+        };
+        int tot = 0;
+        for (int b = g0; b < g1; b += 8) {
+            load8(b);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) tot += y[q];
+        }
+        if (j < PT) lds[tid] = tot;
+        __syncthreads();
+        if (j < PT) {
+            int run = 0;
+            for (int jj = 0; jj < j; ++jj) run += lds[jj * E + e];
+            if (j == 0) {
+                int all = 0;
+                for (int jj = 0; jj < PT; ++jj) all += lds[jj * E + e];
+                scan_tot[e] = all;
+                sc.counts[static_cast<int64_t>(layer) * E + e] = all;
+            }
+            for (int b = g0; b < g1; b += 8) {
+                if (cs > 8) load8(b);
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (b + q < g1) gb[static_cast<int64_t>(b + q) * E + e] = run;
+                    run += y[q];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (mode & kModeScan) {
+        int part = 0;
+        for (int x = tid; x < E; x += kPlanBlock) part += scan_tot[x];
+        int total;
+        plan_block_sum(part, wsum, total);
+        if (tid == 0 && sc.invalid)
+            sc.invalid[layer] = static_cast<int32_t>(sc.A - total);
+        if (!(mode & kModePlan)) return;
+    }
+    const bool scanned = (mode & kModeScan) != 0;
     const int32_t *cin = counts + static_cast<int64_t>(layer) * E;
     int32_t *out = placement + static_cast<int64_t>(layer) * lay.words;
     PlanLds s = carve(lds, E, R, S, P, per_wave ? kPlanWaves : 1);
@@ -601,7 +689,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     int part = 0;
     uint32_t sat = 0;    // the count, a negative one as 2^30
     for (int e = tid; e < E; e += kPlanBlock) {
-        const int c = cin[e];
+        const int c = scanned ? scan_tot[e] : cin[e];
         s.cnt[e] = c;
         s.rem[e] = c;
         s.nrec_e[e] = 0;
@@ -942,8 +1030,12 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
 
 size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave) {
     const size_t regions = per_wave ? kPlanWaves : 1;
-    return sizeof(int32_t) * (static_cast<size_t>(12) * E + 1 + 3 * R +
-                              regions * 3 * R * S + 2 * P);
+    const size_t plan = sizeof(int32_t) * (static_cast<size_t>(12) * E + 1 +
+                                           3 * R + regions * 3 * R * S + 2 * P);
+    // the load's scan first uses the same LDS for one partial sum per
+    // thread
+    const size_t scan = static_cast<size_t>(kPlanBlock) * sizeof(int32_t);
+    return plan > scan ? plan : scan;
 }
 
 // The limit only rises (the largest need so far), so a context or call
@@ -961,15 +1053,40 @@ hipError_t plan_prepare(size_t lds_bytes) {
     return e;
 }
 
-hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
-                       int32_t *placement, hipStream_t s) {
+static hipError_t launch(const ue_ctx &c, const int32_t *counts, int L,
+                         int32_t *placement, int mode, const ScanArgs &sc,
+                         hipStream_t s) {
     hipLaunchKernelGGL(k_plan, dim3(L), dim3(kPlanBlock), c.plan_lds, s,
                        counts, c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
                        static_cast<int>(c.cfg.plan_policy),
                        static_cast<int>(c.cfg.quota_mode),
                        c.plan_per_wave ? 1 : 0,
-                       static_cast<uint32_t>(c.plan_lds), c.lay, placement);
+                       static_cast<uint32_t>(c.plan_lds), c.lay, placement,
+                       mode, sc);
     return hipGetLastError();
+}
+
+hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
+                       int32_t *placement, hipStream_t s) {
+    return launch(c, counts, L, placement, kModePlan, ScanArgs{}, s);
+}
+
+hipError_t launch_scan(const ue_ctx &c, int L, int64_t A, int32_t *counts,
+                       int32_t *invalid, int32_t *placement, hipStream_t s) {
+    int tiles = static_cast<int>((A + kLoadTile - 1) / kLoadTile);
+    if (tiles < 1) tiles = 1;
+    ScanArgs sc;
+    sc.rows = c.tile_off;
+    sc.group_base = c.group_base;
+    sc.A = A;
+    sc.tiles = tiles;
+    sc.group = load_group_tiles(c, tiles, L);
+    sc.row_stride = c.max_rr_tiles + c.max_load_groups;
+    sc.max_groups = c.max_load_groups;
+    sc.counts = counts;
+    sc.invalid = invalid;
+    return launch(c, counts, L, placement,
+                  kModeScan | (placement ? kModePlan : 0), sc, s);
 }
 
 }  // namespace ue

@@ -64,7 +64,6 @@ struct RerouteArgs {
     uint64_t *tick;            // [max_layers] own ticket and epoch
     const int32_t *group_base; // [max_layers][max_groups][E] from the load
     const uint16_t *tile_off;  // [max_layers][max_tiles + max_groups][E]
-    const int32_t *load_status;// [max_layers] the load's poisoned flags
     int32_t *rank_counts, *faults;
 };
 
@@ -465,11 +464,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     // ---- 3. count of each expert in earlier tiles ---------------------------
     // (after a load it came with the prefixes, and the expert records are
     // complete once the scan has written their first field)
-    // (after a load, a wait of the load that gave up left wrong prefixes:
-    // the layer is reported as poisoned in the same way)
+    // (after a load nothing waited: the prefixes are the scan's)
     int poisoned = 0;
     if (kAfterLoad) {
-        poisoned = g.load_status[layer] != 0;
         __syncthreads();
     } else {
         uint64_t *st = g.state + static_cast<int64_t>(layer) * g.max_tiles * E;
@@ -665,7 +662,6 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.tick = c.rr_tick;
     g.group_base = c.group_base;
     g.tile_off = c.tile_off;
-    g.load_status = c.load_status;
     g.load_group = load_group_tiles(c, tiles, L);
     g.max_groups = c.max_load_groups;
     g.rank_counts = rank_counts;

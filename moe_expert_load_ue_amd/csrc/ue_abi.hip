@@ -121,9 +121,11 @@ int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
     c.reroute_lds = reroute_lds_bytes(E, R, c.P, k);
     // the quota search keeps each pass's chunks when they fit in LDS
     c.plan_per_wave = cfg.quota_mode == UE_QUOTA_SEARCH &&
-                      plan_lds_bytes(E, R, S, c.P, true) + 256 <= info.lds_cap;
+                      plan_lds_bytes(E, R, S, c.P, true) + kPlanStaticLds <=
+                          info.lds_cap;
     c.plan_lds = plan_lds_bytes(E, R, S, c.P, c.plan_per_wave);
-    if (c.plan_lds + 256 > info.lds_cap || c.reroute_lds + 256 > info.lds_cap ||
+    if (c.plan_lds + kPlanStaticLds > info.lds_cap ||
+        c.reroute_lds + 256 > info.lds_cap ||
         load_lds_bytes(E) + 256 > info.lds_cap)
         return UE_EUNSUPPORTED;
     // kernels that need more than 64 KiB of dynamic LDS have their limit
@@ -188,8 +190,6 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         off = round_up(off + bytes, 256);
         return o;
     };
-    const size_t o_lstate = take(sizeof(uint64_t) * Lmax * ld_groups * E);
-    const size_t o_ltick = take(sizeof(uint64_t) * Lmax);
     // the load's prefixes: a base row per group of tiles and a 16-bit row
     // per tile plus one per group (row t + g for tile t of group g, and row
     // t + g + 1 after the group's last tile t), so below tiles + groups;
@@ -199,7 +199,6 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         take(sizeof(uint16_t) * Lmax * (rr_tiles + ld_groups) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
-    const size_t o_lstat = take(sizeof(int32_t) * Lmax);
     c->ws_bytes = off;
     he = hipMalloc(&c->ws, c->ws_bytes);
     if (he != hipSuccess) {
@@ -214,13 +213,10 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         return UE_EHIP;
     }
     char *b = static_cast<char *>(c->ws);
-    c->load_state = reinterpret_cast<uint64_t *>(b + o_lstate);
-    c->load_tick = reinterpret_cast<uint64_t *>(b + o_ltick);
     c->group_base = reinterpret_cast<int32_t *>(b + o_gbase);
     c->tile_off = reinterpret_cast<uint16_t *>(b + o_toff);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
-    c->load_status = reinterpret_cast<int32_t *>(b + o_lstat);
     *out = c;
     return UE_OK;
 }
@@ -304,9 +300,12 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
     const int64_t A = static_cast<int64_t>(T) * ctx->k;
     hipStream_t s = static_cast<hipStream_t>(stream);
     tbegin(ctx, s);
-    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid, s);
+    hipError_t he = ue::launch_count(*ctx, routing, L, A, s);
+    if (he != hipSuccess) return hip_fail(ctx, he, "k_count launch");
     tmark(ctx, s);
-    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_load launch");
+    he = ue::launch_scan(*ctx, L, A, counts, invalid, nullptr, s);
+    tmark(ctx, s);
+    return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_plan (scan) launch");
 }
 
 int ue_plan(ue_ctx *ctx, const int32_t *counts, int32_t L, void *placement,
@@ -369,10 +368,11 @@ int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
     const int64_t A = static_cast<int64_t>(T) * ctx->k;
     hipStream_t s = static_cast<hipStream_t>(stream);
     tbegin(ctx, s);
-    hipError_t he = ue::launch_load(*ctx, routing, L, A, counts, invalid, s);
-    if (he != hipSuccess) return hip_fail(ctx, he, "k_load launch");
+    hipError_t he = ue::launch_count(*ctx, routing, L, A, s);
+    if (he != hipSuccess) return hip_fail(ctx, he, "k_count launch");
     tmark(ctx, s);
-    he = ue::launch_plan(*ctx, counts, L, static_cast<int32_t *>(placement), s);
+    he = ue::launch_scan(*ctx, L, A, counts, invalid,
+                         static_cast<int32_t *>(placement), s);
     if (he != hipSuccess) return hip_fail(ctx, he, "k_plan launch");
     tmark(ctx, s);
     he = ue::launch_reroute_after_load(

@@ -40,28 +40,24 @@ struct ue_ctx {
     ue_placement_layout lay{};
     int max_rr_tiles = 0;   // reroute tiles of the largest layer
 
-    // One device allocation holds the whole workspace: per-tile lookback
-    // words and, per layer, a tile ticket and a call epoch for each of the
-    // two scanning kernels. Tickets return to zero at the end of every
-    // launch and epochs only grow, so nothing is cleared between calls.
+    // One device allocation holds the whole workspace: the per-tile table
+    // the load fills and the fused reroute reads, and the standalone
+    // reroute's lookback words with, per layer, a tile ticket and a call
+    // epoch. Tickets return to zero at the end of every launch and epochs
+    // only grow, so nothing is cleared between calls.
     void *ws = nullptr;
     size_t ws_bytes = 0;
     int max_load_groups = 0;       // load tile groups of the largest layer
-    uint64_t *load_state = nullptr;// [max_layers][max_load_groups][E]
-    uint64_t *load_tick = nullptr; // [max_layers] {epoch:32 | ticket:32}
     // the load's per-tile prefixes, in two parts: per group of tiles, the
     // count of each expert in all earlier groups, and per tile the count
     // in the group's earlier tiles (16 bits; each group also has a row
     // after its last tile: the group's own counts). Tile t of group g has
-    // row t + g.
+    // row t + g. The count kernel first writes each tile's own counts
+    // there; the scan rewrites them in place.
     int32_t *group_base = nullptr; // [max_layers][max_load_groups][E]
     uint16_t *tile_off = nullptr;  // [max_layers][max_rr_tiles + max_load_groups][E]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
-    // per layer, written by the load's last group on every call: nonzero
-    // when a lookback wait of that call gave up (the fused reroute reports
-    // it in faults)
-    int32_t *load_status = nullptr;// [max_layers]
     // polls of one cross-workgroup wait before it gives up
     uint32_t wait_limit = 1u << 22;
 
@@ -91,18 +87,23 @@ struct ue_ctx {
 namespace ue {
 
 // Launchers (each returns a hipError_t from the launch).
-hipError_t launch_load(const ue_ctx &c, const int32_t *routing, int L,
-                       int64_t A, int32_t *counts, int32_t *invalid,
-                       hipStream_t s);
+// The load is two launches: launch_count writes every tile's counts into
+// the per-tile table, launch_scan finishes it (group bases, in-group
+// offsets, counts, invalid) and, with a placement, plans in the same
+// launch.
+hipError_t launch_count(const ue_ctx &c, const int32_t *routing, int L,
+                        int64_t A, hipStream_t s);
+hipError_t launch_scan(const ue_ctx &c, int L, int64_t A, int32_t *counts,
+                       int32_t *invalid, int32_t *placement, hipStream_t s);
 hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        int32_t *placement, hipStream_t s);
 hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
                           const int32_t *placement, int L, int64_t A,
                           int32_t *phys, int32_t *rank_counts, int32_t *perm,
                           int32_t *inv_perm, int32_t *faults, hipStream_t s);
-// Reroute that takes each tile's expert prefix from the load kernel's
-// published words instead of its own lookback (the routing must be the one
-// the immediately preceding launch_load counted).
+// Reroute that takes each tile's expert prefix from the rows the load's
+// scan just wrote instead of its own lookback (the routing must be the one
+// the immediately preceding launch_count / launch_scan counted).
 hipError_t launch_reroute_after_load(const ue_ctx &c, const int32_t *routing,
                                      const int32_t *placement, int L,
                                      int64_t A, int32_t *phys,
@@ -136,6 +137,8 @@ int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
 
 // Error text of the calling thread's last ue_rebalance_static call.
 const char *static_last_error();
+// Static LDS of the planner kernel (dynamic LDS comes on top of it).
+constexpr size_t kPlanStaticLds = 5120;
 
 size_t load_lds_bytes(int E);
 // Tiles per load workgroup for a launch over L layers of `tiles` tiles

@@ -3,18 +3,17 @@
 // Some callers cannot allocate device memory where they rebalance (code
 // under stream capture, tight serving loops, harnesses that forbid it).
 // This entry point runs the same three kernels as ue_rebalance with the
-// same results, but needs no context: its scratch (the load's per-layer
-// tickets, lookback words, group bases, per-tile offsets and poisoned
-// flags) lives in one file-scope device array of kStaticScratch bytes,
-// which every device the library runs on holds until the process ends.
-// Its device address is taken once per device, on the first call there,
-// and only that address is handed to kernels.
+// same results, but needs no context: its scratch (the load's per-tile
+// table: group bases and per-tile offsets) lives in one file-scope device
+// array of kStaticScratch bytes, which every device the library runs on
+// holds until the process ends. Its device address is taken once per
+// device, on the first call there, and only that address is handed to
+// kernels.
 //
-// Calls of any shape share the array, so each call first clears the
-// ticket and lookback words it uses, with a fill kernel on the call's
-// stream (capturable, unlike a memset node); the bases, offsets and flags
-// are written before they are read. Calls that overlap in time on one
-// device race on the array.
+// Calls of any shape share the array. Every word a call reads was written
+// earlier in the same call (the count kernel writes each tile's row, the
+// scan the rest), so nothing is cleared between calls. Calls that overlap
+// in time on one device race on the array.
 #include <cstdarg>
 #include <cstdio>
 #include <mutex>
@@ -77,15 +76,6 @@ int device_slot(int dev, const DeviceSlot *&out) {
                : set_err(d.status, "scratch set-up on device %d failed", dev);
 }
 
-__global__ __launch_bounds__(ue::kBlock) void k_clear_words(uint64_t *p,
-                                                            int64_t n) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * ue::kBlock;
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * ue::kBlock +
-                     threadIdx.x;
-         i < n; i += stride)
-        p[i] = 0ull;
-}
-
 bool aligned4(const void *p) {
     return (reinterpret_cast<uintptr_t>(p) & 3u) == 0;
 }
@@ -99,12 +89,8 @@ size_t scratch_need(const ue_config *cfg, int32_t L, int32_t T) {
     if (tiles < 1) tiles = 1;
     const int64_t groups = (tiles + ue::kLoadGroup - 1) / ue::kLoadGroup;
     const size_t E = static_cast<size_t>(cfg->num_experts);
-    // ticket words and lookback words first (the part each call clears),
-    // then flags, group bases and 16-bit tile offsets
-    return up256(sizeof(uint64_t) * L) +
-           up256(sizeof(uint64_t) * L * groups * E) +
-           up256(sizeof(int32_t) * L) +
-           up256(sizeof(int32_t) * L * groups * E) +
+    // group bases, then the 16-bit per-tile rows
+    return up256(sizeof(int32_t) * L * groups * E) +
            up256(sizeof(uint16_t) * L * (tiles + groups) * E);
 }
 
@@ -165,11 +151,6 @@ int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,
         off += up256(bytes);
         return p;
     };
-    c.load_tick = reinterpret_cast<uint64_t *>(take(sizeof(uint64_t) * L));
-    c.load_state = reinterpret_cast<uint64_t *>(
-        take(sizeof(uint64_t) * L * groups * E));
-    const size_t clear_words = off / sizeof(uint64_t);
-    c.load_status = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * L));
     c.group_base = reinterpret_cast<int32_t *>(
         take(sizeof(int32_t) * L * groups * E));
     c.tile_off = reinterpret_cast<uint16_t *>(
@@ -178,16 +159,10 @@ int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,
     c.rr_tick = nullptr;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    int blocks = static_cast<int>((clear_words + ue::kBlock - 1) / ue::kBlock);
-    blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
-    hipLaunchKernelGGL(k_clear_words, dim3(blocks), dim3(ue::kBlock), 0, s,
-                       reinterpret_cast<uint64_t *>(b),
-                       static_cast<int64_t>(clear_words));
-    he = hipGetLastError();
+    he = ue::launch_count(c, routing, L, A, s);
     if (he == hipSuccess)
-        he = ue::launch_load(c, routing, L, A, counts, invalid, s);
-    if (he == hipSuccess)
-        he = ue::launch_plan(c, counts, L, static_cast<int32_t *>(placement), s);
+        he = ue::launch_scan(c, L, A, counts, invalid,
+                             static_cast<int32_t *>(placement), s);
     if (he == hipSuccess)
         he = ue::launch_reroute_after_load(
             c, routing, static_cast<const int32_t *>(placement), L, A, phys,

@@ -273,7 +273,7 @@ def test_kernel_times():
     t = ue.ue_kernel_times(ctx)
     assert len(t) == 3 and all(v > 0 for v in t)
     ue.ue_load(ctx, routing)
-    assert len(ue.ue_kernel_times(ctx)) == 1
+    assert len(ue.ue_kernel_times(ctx)) == 2     # count, scan
     ue.ue_set_timing(ctx, False)
 
 

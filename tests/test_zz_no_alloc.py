@@ -2,7 +2,7 @@
 device array) against ue_rebalance on the same routing, every output
 bit-exact, over calls in a row on one device: the 58-layer dsv3 rebalance,
 then a smaller ragged input under another rule, then dsv3 again (each call
-clears what the previous one left). A call whose scratch would exceed the
+reads only scratch it wrote itself). A call whose scratch would exceed the
 array is refused before anything is written."""
 import numpy as np
 import pytest
@@ -65,7 +65,7 @@ def test_static_rebalance_matches_context_calls():
 
 
 def test_static_rebalance_refuses_oversized_calls():
-    """128 layers of dsv3 size need about 31 MB of scratch: refused with
+    """128 layers of dsv3 size need about 23 MB of scratch: refused with
     UE_ESHAPE, every output left as it was."""
     d = W.CONFIGS["dsv3"]
     L, T = 128, d.tokens
