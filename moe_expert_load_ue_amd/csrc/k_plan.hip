@@ -378,86 +378,6 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
     cand.init(s.sorted, ncand);
     ccount.init(s.scount, ncand);
     climit.init(s.slimit, ncand);
-    if (RPL == 1 && S == 1) {
-        // One spare slot per rank and at most 64 ranks: a rank that takes a
-        // chunk has no slot left, so nothing is held; the list sits one
-        // entry per lane, with the prefix sums of the headrooms of the
-        // entries not taken out of order (below 2^31: at most R * Q). An
-        // amount is placed with one ballot: the run from di ends at the
-        // first lane whose headroom sum since di reaches it; the lanes
-        // before it fill to Q and that lane takes the rest, or under best
-        // fit, when the rest is below its headroom, the rest goes to the
-        // most loaded entry from there on that holds it (lowest id among
-        // equal loads), which leaves the list and the sums. No lane
-        // reaching it means the list runs out. Candidates are read 64 at a
-        // time and those with nothing to move are skipped with the ballot.
-        const bool inl = lane < nd;
-        const uint32_t key = inl ? static_cast<uint32_t>(s.dsorted[lane]) : 0u;
-        const int L = static_cast<int>(key >> rbits);
-        const int h = inl ? Q - L : 0;
-        int hsum = wave_inclusive_sum(h);
-        bool gone = false;
-        for (int c0 = 0; c0 < ncand && !exhausted; c0 += 64) {
-            const int ci = c0 + lane;
-            const bool cv = ci < ncand;
-            const int over_l = cv ? s.slimit[ci] - Q : 0;
-            const int cnt_l = cv ? s.scount[ci] : 0;
-            const int rem_l = over_l <= 0 ? 0 : (cnt_l < over_l ? cnt_l : over_l);
-            const int e_l = cv ? s.sorted[ci] : 0;
-            uint64_t todo = __ballot(rem_l > 0);
-            while (todo) {
-                const int j = __builtin_ctzll(todo);
-                todo &= todo - 1;
-                const int rem = __builtin_amdgcn_readlane(rem_l, j);
-                const int e = __builtin_amdgcn_readlane(e_l, j);
-                const int base = di > 0 ? __builtin_amdgcn_readlane(hsum, di - 1) : 0;
-                const bool live = inl && !gone && lane >= di;
-                const uint64_t hit = __ballot(live && hsum - base >= rem);
-                const int hl = hit ? __builtin_ctzll(hit) : 64;
-                const int hh = hit ? __builtin_amdgcn_readlane(h, hl) : 0;
-                const int need =
-                    hit ? rem - (__builtin_amdgcn_readlane(hsum, hl) - hh - base) : 0;
-                const bool bf = hit && best_fit && need < hh;
-                const bool put = live && (lane < hl || (lane == hl && !bf));
-                const uint64_t puts = __ballot(put);
-                if (write && put) {
-                    const int at = nrec + static_cast<int>(mask_rank(puts));
-                    s.rec_e[at] = e;
-                    s.rec_p[at] = static_cast<int>(key & rmask) * NS + N;
-                    s.rec_m[at] = lane == hl ? need : h;
-                }
-                nrec += __builtin_popcountll(puts);
-                if (!hit) {
-                    exhausted = 1;
-                    break;
-                }
-                if (!bf) {
-                    di = hl + 1;
-                    continue;
-                }
-                di = hl;
-                const bool fits = inl && !gone && lane >= di && L <= Q - need;
-                const uint64_t bq = __ballot(fits);      // the hit lane fits
-                const int Lw = __builtin_amdgcn_readlane(L, 63 - __builtin_clzll(bq));
-                const int bi = __builtin_ctzll(__ballot(fits && L == Lw));
-                const int db = static_cast<int>(
-                    static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(key), bi)) &
-                    rmask);
-                if (write && lane == 0) {
-                    s.rec_e[nrec] = e;
-                    s.rec_p[nrec] = db * NS + N;
-                    s.rec_m[nrec] = need;
-                }
-                ++nrec;
-                const int hb = __builtin_amdgcn_readlane(h, bi);
-                hsum -= lane >= bi ? hb : 0;
-                gone = gone || lane == bi;
-            }
-        }
-        nrec_out = nrec;
-        exhausted_out = exhausted;
-        return;
-    }
     for (int c = 0; c < ncand && !exhausted; ++c) {
         const int e = cand.get(c);
         const int cnt = ccount.get(c);
@@ -553,6 +473,151 @@ __device__ void spill_loop(PlanLds &s, int ncand, int nd_all, int R, int S,
     exhausted_out = exhausted;
 }
 
+// The spill loop at quota Q for one spare slot per rank and at most 64 RPL
+// ranks, run by one wave with the receiving list held in registers: entry
+// x = 64 i + lane in slot i of every lane. A rank that takes a chunk has no
+// slot left, so nothing is held and an entry leaves the list once used. Each
+// entry keeps the prefix sum of the headrooms (Q - load) of the entries up
+// to it that were not taken out of order (below 2^31: at most R * Q). An
+// amount is placed with one ballot per slot: the run from di ends at the
+// first entry whose headroom sum since di reaches it; the entries before it
+// fill to Q and that entry takes the rest, or under best fit, when the rest
+// is below its headroom, the rest goes to the most loaded entry from there
+// on that holds it (lowest id among equal loads), which leaves the list and
+// the sums. No entry reaching it means the list runs out. Candidates are
+// read 64 at a time and those with nothing to move are skipped with a
+// ballot. The same placements as spill_loop with S = 1, without LDS reads
+// inside the loop.
+template <int RPL>
+__device__ __forceinline__ void spill_one_slot(PlanLds &s, int ncand, int nd_all,
+                                               int N, int NS, int Q, int rbits,
+                                               bool best_fit, bool write,
+                                               int &nrec_out, int &exhausted_out) {
+    const int lane = threadIdx.x & 63;
+    const int nd = count_below(s.dsorted, nd_all,
+                               static_cast<uint32_t>(Q) << rbits);
+    const uint32_t rmask = (1u << rbits) - 1u;
+    constexpr int kNone = 64 * RPL;
+    // per slot: key, load, headroom and headroom prefix of the lane's entry;
+    // avail (wave-uniform): bit l of slot i set while entry 64 i + l is in
+    // the list and was not taken out of order
+    int keyi[RPL], L[RPL], h[RPL], hsum[RPL];
+    uint64_t avail[RPL];
+    {
+        int carry = 0;
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int x = 64 * i + lane;
+            const bool in = x < nd;
+            keyi[i] = in ? s.dsorted[x] : 0;
+            L[i] = static_cast<int>(static_cast<uint32_t>(keyi[i]) >> rbits);
+            h[i] = in ? Q - L[i] : 0;
+            hsum[i] = wave_inclusive_sum(h[i]) + carry;
+            carry = __builtin_amdgcn_readlane(hsum[i], 63);
+            avail[i] = __ballot(in);
+        }
+    }
+    // lanes below t of a slot (t may fall outside [0, 64))
+    auto below = [](int t) -> uint64_t {
+        return t <= 0 ? 0ull : (t >= 64 ? ~0ull : ((1ull << t) - 1ull));
+    };
+    // passing entry di: entries before it leave avail
+    auto pass_to = [&](int d) {
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) avail[i] &= ~below(d - 64 * i);
+    };
+    // di: first entry not yet passed; base: the headroom prefix before it
+    int di = 0, base = 0, nrec = 0, exhausted = 0;
+    for (int c0 = 0; c0 < ncand && !exhausted; c0 += 64) {
+        const int ci = c0 + lane;
+        const bool cv = ci < ncand;
+        const int over_l = cv ? s.slimit[ci] - Q : 0;
+        const int cnt_l = cv ? s.scount[ci] : 0;
+        const int rem_l = over_l <= 0 ? 0 : (cnt_l < over_l ? cnt_l : over_l);
+        const int e_l = cv ? s.sorted[ci] : 0;
+        uint64_t todo = __ballot(rem_l > 0);
+        while (todo) {
+            const int j = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int rem = __builtin_amdgcn_readlane(rem_l, j);
+            const int e = __builtin_amdgcn_readlane(e_l, j);
+            // the hit entry: the first live one whose sum since di reaches
+            // rem; hh its headroom, hs its prefix
+            int hl = kNone, hh = 0, hs = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const uint64_t b = __ballot(hsum[i] - base >= rem) & avail[i];
+                if (hl == kNone && b != 0) {
+                    const int l = __builtin_ctzll(b);
+                    hl = 64 * i + l;
+                    hh = __builtin_amdgcn_readlane(h[i], l);
+                    hs = __builtin_amdgcn_readlane(hsum[i], l);
+                }
+            }
+            const bool hit = hl != kNone;
+            const int need = hit ? rem - (hs - hh - base) : 0;
+            const bool bf = hit && best_fit && need < hh;
+            // entries placed now: full headroom before the hit entry, the
+            // rest on the hit entry (unless best fit sends it elsewhere)
+            const int end = bf ? hl : hl + 1;
+            int placed = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const int hi = hl - 64 * i;
+                const uint64_t puts = avail[i] & below(end - 64 * i);
+                if (write && ((puts >> lane) & 1ull)) {
+                    const int at = nrec + placed + static_cast<int>(mask_rank(puts));
+                    s.rec_e[at] = e;
+                    s.rec_p[at] = static_cast<int>(static_cast<uint32_t>(keyi[i]) & rmask) * NS + N;
+                    s.rec_m[at] = lane == hi ? need : h[i];
+                }
+                placed += __builtin_popcountll(puts);
+            }
+            nrec += placed;
+            if (!hit) {
+                exhausted = 1;
+                break;
+            }
+            di = end;
+            base = bf ? hs - hh : hs;
+            pass_to(di);
+            if (!bf) continue;
+            // the list ascends, so the largest fitting load is the last
+            // fitting entry's; the hit entry fits, so one exists
+            const int thr = Q - need;
+            int Lw = -1;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const uint64_t b = __ballot(L[i] <= thr) & avail[i];
+                if (b != 0) Lw = __builtin_amdgcn_readlane(L[i], 63 - __builtin_clzll(b));
+            }
+            int bi = kNone, kb = 0, hb = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const uint64_t b = __ballot(L[i] == Lw) & avail[i];
+                if (bi == kNone && b != 0) {
+                    const int l = __builtin_ctzll(b);
+                    bi = 64 * i + l;
+                    kb = __builtin_amdgcn_readlane(keyi[i], l);
+                    hb = __builtin_amdgcn_readlane(h[i], l);
+                    avail[i] &= ~(1ull << l);
+                }
+            }
+            if (write && lane == 0) {
+                s.rec_e[nrec] = e;
+                s.rec_p[nrec] = static_cast<int>(static_cast<uint32_t>(kb) & rmask) * NS + N;
+                s.rec_m[nrec] = need;
+            }
+            ++nrec;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i)
+                hsum[i] -= 64 * i + lane >= bi ? hb : 0;
+        }
+    }
+    nrec_out = nrec;
+    exhausted_out = exhausted;
+}
+
 // One greedy pass at quota Q by the calling wave, dispatched on the number
 // of ranks each lane may hold.
 __device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
@@ -560,6 +625,14 @@ __device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
                            bool write, int &nrec, int &exhausted) {
     nrec = 0;
     exhausted = 0;
+    if (S == 1 && R <= 256) {
+        switch ((R + 63) / 64) {
+            case 1: spill_one_slot<1>(s, ncand, nd_all, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+            case 2: spill_one_slot<2>(s, ncand, nd_all, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+            default: spill_one_slot<4>(s, ncand, nd_all, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
+        }
+        return;
+    }
     switch ((R + 63) / 64) {
         case 1: spill_loop<1>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
         case 2: spill_loop<2>(s, ncand, nd_all, R, S, N, NS, Q, rbits, best_fit, write, nrec, exhausted); break;
