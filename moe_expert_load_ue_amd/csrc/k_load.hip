@@ -35,7 +35,7 @@ struct CountArgs {
     int64_t A;                 // assignments per layer
     int E, tiles, group, row_stride;
     bool vec4;
-    uint16_t *rows;            // [max_layers][max_tiles + max_groups][E]
+    uint16_t *rows;            // [L][row_stride = tiles + groups][E]
 };
 
 // Two experts share a histogram word, 16 bits each: a copy takes at most
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kBlock) void k_count(CountArgs g) {
     __syncthreads();
     // the group's rows: each tile's count in the group's earlier tiles
     // (below G * kLoadTile, so 16 bits), then the group's own counts
-    static_assert(kLoadGroupWide * kLoadTile <= 65535, "16-bit tile offsets");
+    static_assert(kLoadGroup * kLoadTile <= 65535, "16-bit tile offsets");
     uint16_t *rows = g.rows + (static_cast<int64_t>(layer) * g.row_stride +
                                tile_first + grp) * E;
     for (int e = tid; e < E; e += kBlock) {
@@ -148,33 +148,38 @@ static size_t load_lds_bytes_for(int E, int G) {
            sizeof(uint16_t) * static_cast<size_t>(G) * E;
 }
 
-size_t load_lds_bytes(int E) { return load_lds_bytes_for(E, kLoadGroupWide); }
+size_t load_lds_bytes(int E) { return load_lds_bytes_for(E, kLoadGroup); }
 
-int load_group_tiles(const ue_ctx &c, int tiles, int L) {
-    // groups of kLoadGroup tiles: one counting workgroup each
-    (void)c;
-    (void)tiles;
+LoadShape load_shape(int64_t A, int L) {
     (void)L;
-    return kLoadGroup;
+    LoadShape sh;
+    int64_t tiles = (A + kLoadTile - 1) / kLoadTile;
+    if (tiles < 1) tiles = 1;
+    sh.tiles = static_cast<int>(tiles);
+    sh.group = kLoadGroup;
+    sh.groups = static_cast<int>((tiles + kLoadGroup - 1) / kLoadGroup);
+    return sh;
+}
+
+int64_t load_group_rows_cap(int64_t A, int L) {
+    return static_cast<int64_t>(L) * load_shape(A, L).groups;
 }
 
 hipError_t launch_count(const ue_ctx &c, const int32_t *routing, int L,
                         int64_t A, hipStream_t s) {
-    int tiles = static_cast<int>((A + kLoadTile - 1) / kLoadTile);
-    if (tiles < 1) tiles = 1;
+    const LoadShape sh = load_shape(A, L);
     CountArgs g;
     g.routing = routing;
     g.A = A;
     g.E = c.E;
-    g.tiles = tiles;
-    g.group = load_group_tiles(c, tiles, L);
-    g.row_stride = c.max_rr_tiles + c.max_load_groups;
+    g.tiles = sh.tiles;
+    g.group = sh.group;
+    g.row_stride = sh.tiles + sh.groups;
     g.vec4 = (A % 4 == 0) && (reinterpret_cast<uintptr_t>(routing) % 16 == 0);
     g.rows = c.tile_off;
-    const int groups = (tiles + g.group - 1) / g.group;
-    static_assert(kLoadGroup == 8, "one instantiation");
-    hipLaunchKernelGGL(k_count<kLoadGroup>, dim3(groups, L), dim3(kBlock),
-                       load_lds_bytes_for(c.E, kLoadGroup), s, g);
+    const dim3 grid(sh.groups, L);
+    const size_t lds = load_lds_bytes_for(c.E, sh.group);
+    hipLaunchKernelGGL(k_count<kLoadGroup>, grid, dim3(kBlock), lds, s, g);
     return hipGetLastError();
 }
 

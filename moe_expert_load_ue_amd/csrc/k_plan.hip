@@ -620,7 +620,7 @@ __device__ __forceinline__ void spill_one_slot(PlanLds &s, int ncand, int nd_all
 
 // One greedy pass at quota Q by the calling wave, dispatched on the number
 // of ranks each lane may hold.
-__device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
+__device__ __forceinline__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
                            int N, int NS, int Q, int rbits, bool best_fit,
                            bool write, int &nrec, int &exhausted) {
     nrec = 0;
@@ -652,12 +652,20 @@ __device__ void spill_pass(PlanLds &s, int ncand, int nd_all, int R, int S,
 // the ids out of range: assignments minus counted ones). Those rows are
 // what the fused reroute reads.
 struct ScanArgs {
-    uint16_t *rows;            // [max_layers][row_stride][E]
-    int32_t *group_base;       // [max_layers][max_groups][E]
+    uint16_t *rows;            // [L][row_stride = tiles + groups][E]
+    int32_t *group_base;       // [L][groups][E]
     int64_t A;                 // assignments per layer
-    int tiles, group, row_stride, max_groups;
+    int tiles, group, row_stride, groups;
     int32_t *counts;           // [L][E] out
     int32_t *invalid;          // [L] out, may be null
+    // When the plan is made in the same launch from these counts, the
+    // dispatch totals the reroute would find follow from the plan alone:
+    // every assignment of a valid id falls in a replica's capacity (the
+    // capacities of an expert's replicas add up to its count), so a rank
+    // receives what the plan's slots on it hold (its load after the plan)
+    // and the faults are the ids out of range. Written here when not null.
+    int32_t *rank_counts;      // [L][R] out, may be null
+    int32_t *faults;           // [L] out, may be null
 };
 constexpr int kModeScan = 1;   // finish the load (ScanArgs)
 constexpr int kModePlan = 2;   // make the plan
@@ -688,7 +696,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         const int ng = (sc.tiles + G - 1) / G;
         const uint16_t *rows =
             sc.rows + static_cast<int64_t>(layer) * sc.row_stride * E;
-        int32_t *gb = sc.group_base + static_cast<int64_t>(layer) * sc.max_groups * E;
+        int32_t *gb = sc.group_base + static_cast<int64_t>(layer) * sc.groups * E;
         auto total_row = [&](int g) {
             const int tend = (g + 1) * G < sc.tiles ? (g + 1) * G : sc.tiles;
             return static_cast<int64_t>(tend + g) * E;
@@ -754,6 +762,11 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // mismatch marks the block (exhausted = -1) rather than pass silently
     if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) {
         if (tid == 0) out[lay.exhausted] = -1;
+        // the table is not written: every assignment is marked a fault
+        for (int r = tid; r < R && sc.rank_counts; r += kPlanBlock)
+            sc.rank_counts[static_cast<int64_t>(layer) * R + r] = 0;
+        if (tid == 0 && sc.faults)
+            sc.faults[layer] = static_cast<int32_t>(sc.A) | kPoisonBit;
         return;
     }
 
@@ -796,6 +809,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
                     (i >= lay.slot_expert && i < lay.slot_expert + P);
                 out[i] = neg1 ? -1 : 0;
             }
+            // no replica at all: every assignment is a fault
+            for (int r = tid; r < R && sc.rank_counts; r += kPlanBlock)
+                sc.rank_counts[static_cast<int64_t>(layer) * R + r] = 0;
+            if (tid == 0 && sc.faults) sc.faults[layer] = static_cast<int32_t>(sc.A);
             return;
         }
     }
@@ -1050,6 +1067,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     for (int r = tid; r < R; r += kPlanBlock) {
         const int l = s.load[r];
         out[lay.load_after + r] = l;
+        if (sc.rank_counts) sc.rank_counts[static_cast<int64_t>(layer) * R + r] = l;
         v[2] += (l > Q) ? (l - Q) : 0;   // Q: the quota used
     }
     plan_block_sum3(v, wsum3, pre, tot);
@@ -1089,6 +1107,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // the block's alignment padding is written too, so a block is fully
     // defined by its counts
     for (int i = lay.load_after + R + tid; i < lay.words; i += kPlanBlock) out[i] = 0;
+    if (tid == 0 && sc.faults)
+        sc.faults[layer] = static_cast<int32_t>(sc.A - total);
     if (tid == 0) {
         out[lay.rep_off + E] = n_rep;
         out[lay.slot_off + P] = tot[1];
@@ -1145,19 +1165,21 @@ hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
 }
 
 hipError_t launch_scan(const ue_ctx &c, int L, int64_t A, int32_t *counts,
-                       int32_t *invalid, int32_t *placement, hipStream_t s) {
-    int tiles = static_cast<int>((A + kLoadTile - 1) / kLoadTile);
-    if (tiles < 1) tiles = 1;
+                       int32_t *invalid, int32_t *placement,
+                       int32_t *rank_counts, int32_t *faults, hipStream_t s) {
+    const LoadShape sh = load_shape(A, L);
     ScanArgs sc;
     sc.rows = c.tile_off;
     sc.group_base = c.group_base;
     sc.A = A;
-    sc.tiles = tiles;
-    sc.group = load_group_tiles(c, tiles, L);
-    sc.row_stride = c.max_rr_tiles + c.max_load_groups;
-    sc.max_groups = c.max_load_groups;
+    sc.tiles = sh.tiles;
+    sc.group = sh.group;
+    sc.row_stride = sh.tiles + sh.groups;
+    sc.groups = sh.groups;
     sc.counts = counts;
     sc.invalid = invalid;
+    sc.rank_counts = placement ? rank_counts : nullptr;
+    sc.faults = placement ? faults : nullptr;
     return launch(c, counts, L, placement,
                   kModeScan | (placement ? kModePlan : 0), sc, s);
 }

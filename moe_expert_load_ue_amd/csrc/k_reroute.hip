@@ -38,7 +38,9 @@
 //   5. the tile with the last ticket knows every expert's total; per-rank
 //      counts are the overlaps of [0, total) with the replicas' capacity
 //      intervals, and faults are the ids out of range plus the assignments
-//      beyond an expert's capacity or outside [0, T*k).
+//      beyond an expert's capacity or outside [0, T*k). (After a load the
+//      plan was made from the same counts, so these follow from the plan:
+//      the planner's launch writes them and no tile does this step.)
 // No fences and no global atomics on data.
 #include <algorithm>
 #include <mutex>
@@ -54,7 +56,7 @@ struct RerouteArgs {
     const int32_t *placement;
     int32_t A;                 // assignments per layer (< 2^30)
     int E, R, NS, P, k, ebits, tiles, max_tiles;
-    int load_group, max_groups;// the load's tiles per group; groups
+    int load_group, load_groups;// the load's tiles per group; groups
     int bm_words;              // words per expert bitmap (0: no bitmap path)
     uint32_t spin_limit;       // bound on one lookback wait
     uint32_t lds_bytes;        // dynamic LDS the launch provides
@@ -62,8 +64,8 @@ struct RerouteArgs {
     int32_t *phys, *perm, *inv_perm;
     uint64_t *state;           // [max_layers][max_tiles][E] own lookback
     uint64_t *tick;            // [max_layers] own ticket and epoch
-    const int32_t *group_base; // [max_layers][max_groups][E] from the load
-    const uint16_t *tile_off;  // [max_layers][max_tiles + max_groups][E]
+    const int32_t *group_base; // [L][load_groups][E] from the load
+    const uint16_t *tile_off;  // [L][tiles + load_groups][E]
     int32_t *rank_counts, *faults;
 };
 
@@ -209,9 +211,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     auto load_prefix = [&](int t, int32_t *pre, int32_t *cnt) {
         const int grp = t / g.load_group;
         const int32_t *gb = g.group_base +
-                            (static_cast<int64_t>(layer) * g.max_groups + grp) * E;
+                            (static_cast<int64_t>(layer) * g.load_groups + grp) * E;
         const uint16_t *to = g.tile_off +
-                             (static_cast<int64_t>(layer) * (g.max_tiles + g.max_groups) +
+                             (static_cast<int64_t>(layer) * (g.tiles + g.load_groups) +
                               t + grp) * E;
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
@@ -549,7 +551,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
-    if (tile != g.tiles - 1) return;
+    // (after a load the planner's launch wrote them from the same counts)
+    if (kAfterLoad || tile != g.tiles - 1) return;
     // the per-rank histogram takes region A once the staged entries are read
     __syncthreads();
     int32_t *rank_hist = area;
@@ -662,8 +665,9 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.tick = c.rr_tick;
     g.group_base = c.group_base;
     g.tile_off = c.tile_off;
-    g.load_group = load_group_tiles(c, tiles, L);
-    g.max_groups = c.max_load_groups;
+    const LoadShape sh = load_shape(A, L);
+    g.load_group = sh.group;
+    g.load_groups = sh.groups;
     g.rank_counts = rank_counts;
     g.faults = faults;
     if (after_load) {

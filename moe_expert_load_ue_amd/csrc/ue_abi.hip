@@ -179,9 +179,9 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     const int Lmax = cfg->max_layers;
     int64_t rr_tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
     if (rr_tiles < 1) rr_tiles = 1;
-    const int64_t ld_groups = (rr_tiles + ue::kLoadGroup - 1) / ue::kLoadGroup;
+    const int64_t ld_rows = ue::load_group_rows_cap(A, Lmax);
     c->max_rr_tiles = static_cast<int>(rr_tiles);
-    c->max_load_groups = static_cast<int>(ld_groups);
+    c->load_group_rows = static_cast<int>(ld_rows);
 
     // Workspace carve-up, each piece 256-byte aligned.
     size_t off = 0;
@@ -192,11 +192,10 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     };
     // the load's prefixes: a base row per group of tiles and a 16-bit row
     // per tile plus one per group (row t + g for tile t of group g, and row
-    // t + g + 1 after the group's last tile t), so below tiles + groups;
-    // groups of kLoadGroup tiles are the most numerous
-    const size_t o_gbase = take(sizeof(int32_t) * Lmax * ld_groups * E);
+    // t + g + 1 after the group's last tile t), so tiles + groups per layer
+    const size_t o_gbase = take(sizeof(int32_t) * ld_rows * E);
     const size_t o_toff =
-        take(sizeof(uint16_t) * Lmax * (rr_tiles + ld_groups) * E);
+        take(sizeof(uint16_t) * (Lmax * rr_tiles + ld_rows) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
     c->ws_bytes = off;
@@ -303,7 +302,8 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
     hipError_t he = ue::launch_count(*ctx, routing, L, A, s);
     if (he != hipSuccess) return hip_fail(ctx, he, "k_count launch");
     tmark(ctx, s);
-    he = ue::launch_scan(*ctx, L, A, counts, invalid, nullptr, s);
+    he = ue::launch_scan(*ctx, L, A, counts, invalid, nullptr, nullptr,
+                         nullptr, s);
     tmark(ctx, s);
     return he == hipSuccess ? UE_OK : hip_fail(ctx, he, "k_plan (scan) launch");
 }
@@ -372,7 +372,8 @@ int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
     if (he != hipSuccess) return hip_fail(ctx, he, "k_count launch");
     tmark(ctx, s);
     he = ue::launch_scan(*ctx, L, A, counts, invalid,
-                         static_cast<int32_t *>(placement), s);
+                         static_cast<int32_t *>(placement), rank_counts,
+                         faults, s);
     if (he != hipSuccess) return hip_fail(ctx, he, "k_plan launch");
     tmark(ctx, s);
     he = ue::launch_reroute_after_load(

@@ -26,7 +26,6 @@ constexpr int kRerouteTile = kBlock * kRerouteItems;
 constexpr int kLoadItems = kRerouteItems;
 constexpr int kLoadTile = kRerouteTile;
 constexpr int kLoadGroup = 16384 / kLoadTile;   // tiles per load workgroup
-constexpr int kLoadGroupWide = 2 * kLoadGroup;  // ... when groups are many
 
 }  // namespace ue
 
@@ -47,15 +46,17 @@ struct ue_ctx {
     // only grow, so nothing is cleared between calls.
     void *ws = nullptr;
     size_t ws_bytes = 0;
-    int max_load_groups = 0;       // load tile groups of the largest layer
+    int load_group_rows = 0;       // group rows of the load's tables, all layers
     // the load's per-tile prefixes, in two parts: per group of tiles, the
     // count of each expert in all earlier groups, and per tile the count
     // in the group's earlier tiles (16 bits; each group also has a row
     // after its last tile: the group's own counts). Tile t of group g has
     // row t + g. The count kernel first writes each tile's own counts
     // there; the scan rewrites them in place.
-    int32_t *group_base = nullptr; // [max_layers][max_load_groups][E]
-    uint16_t *tile_off = nullptr;  // [max_layers][max_rr_tiles + max_load_groups][E]
+    // the load's tables of one call (LoadShape): per layer, `groups` base
+    // rows and `tiles + groups` 16-bit rows, layers one after another
+    int32_t *group_base = nullptr; // [load_group_rows][E]
+    uint16_t *tile_off = nullptr;  // [max_layers * max_rr_tiles + load_group_rows][E]
     uint64_t *scan_state = nullptr;// [max_layers][max_rr_tiles][E]
     uint64_t *rr_tick = nullptr;   // [max_layers] {epoch:32 | ticket:32}
     // polls of one cross-workgroup wait before it gives up
@@ -90,11 +91,13 @@ namespace ue {
 // The load is two launches: launch_count writes every tile's counts into
 // the per-tile table, launch_scan finishes it (group bases, in-group
 // offsets, counts, invalid) and, with a placement, plans in the same
-// launch.
+// launch and writes the rank counts and faults of the reroute that
+// follows (launch_reroute_after_load then leaves them alone).
 hipError_t launch_count(const ue_ctx &c, const int32_t *routing, int L,
                         int64_t A, hipStream_t s);
 hipError_t launch_scan(const ue_ctx &c, int L, int64_t A, int32_t *counts,
-                       int32_t *invalid, int32_t *placement, hipStream_t s);
+                       int32_t *invalid, int32_t *placement,
+                       int32_t *rank_counts, int32_t *faults, hipStream_t s);
 hipError_t launch_plan(const ue_ctx &c, const int32_t *counts, int L,
                        int32_t *placement, hipStream_t s);
 hipError_t launch_reroute(const ue_ctx &c, const int32_t *routing,
@@ -141,9 +144,20 @@ const char *static_last_error();
 constexpr size_t kPlanStaticLds = 5120;
 
 size_t load_lds_bytes(int E);
-// Tiles per load workgroup for a launch over L layers of `tiles` tiles
-// (the fused reroute finds its tile's prefix rows with it).
-int load_group_tiles(const ue_ctx &c, int tiles, int L);
+// The load's split of one call over L layers of A assignments: tiles of
+// kLoadTile assignments, groups of `group` consecutive tiles (one counting
+// workgroup each). The count, the scan and the fused reroute all take it
+// from here. (Fewer tiles per group when layers are few gives the count
+// more workgroups, but the planner's scan then reads and writes more
+// group rows in its one workgroup per layer, which costs more than the
+// count gains.)
+struct LoadShape {
+    int tiles, group, groups;
+};
+LoadShape load_shape(int64_t A, int L);
+// Group rows (over all layers) that any call of up to L layers of up to A
+// assignments needs.
+int64_t load_group_rows_cap(int64_t A, int L);
 // per_wave: one chunk-record region per wave (the quota search keeps each
 // pass's chunks, so the chosen one needs no second pass).
 size_t plan_lds_bytes(int E, int R, int S, int P, bool per_wave);

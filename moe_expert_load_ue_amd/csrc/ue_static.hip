@@ -85,13 +85,11 @@ size_t up256(size_t v) { return (v + 255) / 256 * 256; }
 // Scratch bytes of one call (the formula stated beside the entry point).
 size_t scratch_need(const ue_config *cfg, int32_t L, int32_t T) {
     const int64_t A = static_cast<int64_t>(T) * cfg->topk;
-    int64_t tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
-    if (tiles < 1) tiles = 1;
-    const int64_t groups = (tiles + ue::kLoadGroup - 1) / ue::kLoadGroup;
+    const ue::LoadShape sh = ue::load_shape(A, L);
     const size_t E = static_cast<size_t>(cfg->num_experts);
     // group bases, then the 16-bit per-tile rows
-    return up256(sizeof(int32_t) * L * groups * E) +
-           up256(sizeof(uint16_t) * L * (tiles + groups) * E);
+    return up256(sizeof(int32_t) * L * sh.groups * E) +
+           up256(sizeof(uint16_t) * L * (sh.tiles + sh.groups) * E);
 }
 
 }  // namespace
@@ -138,11 +136,10 @@ int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,
                        L, T, need, kStaticScratch);
 
     const int64_t A = static_cast<int64_t>(T) * c.k;
-    int64_t tiles = (A + ue::kRerouteTile - 1) / ue::kRerouteTile;
-    if (tiles < 1) tiles = 1;
-    const int64_t groups = (tiles + ue::kLoadGroup - 1) / ue::kLoadGroup;
+    const ue::LoadShape sh = ue::load_shape(A, L);
+    const int64_t tiles = sh.tiles, groups = sh.groups;
     c.max_rr_tiles = static_cast<int>(tiles);
-    c.max_load_groups = static_cast<int>(groups);
+    c.load_group_rows = static_cast<int>(L * groups);
     const size_t E = static_cast<size_t>(c.E);
     unsigned char *b = d->ptr;
     size_t off = 0;
@@ -162,7 +159,8 @@ int ue_rebalance_static(const ue_config *cfg, const int32_t *routing,
     he = ue::launch_count(c, routing, L, A, s);
     if (he == hipSuccess)
         he = ue::launch_scan(c, L, A, counts, invalid,
-                             static_cast<int32_t *>(placement), s);
+                             static_cast<int32_t *>(placement), rank_counts,
+                             faults, s);
     if (he == hipSuccess)
         he = ue::launch_reroute_after_load(
             c, routing, static_cast<const int32_t *>(placement), L, A, phys,
