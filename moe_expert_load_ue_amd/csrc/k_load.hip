@@ -42,11 +42,14 @@ struct CountArgs {
 // kLoadTile / kSub ids, far below 2^16, so neither half carries into the
 // other, and the eight copies of a word still sum without carrying
 // (kLoadTile < 2^16).
+// Branch-free: an id out of range adds 0 to its lane's copy of the first
+// word, so every lane issues the same instructions.
 static_assert(kLoadTile < 65536, "16-bit tile counters");
 __device__ __forceinline__ void count_one(int id, int E, int sub,
                                           uint32_t *hist) {
-    if (static_cast<uint32_t>(id) < static_cast<uint32_t>(E))
-        atomicAdd(&hist[(id >> 1) * kSub + sub], 1u << ((id & 1) << 4));
+    const bool ok = static_cast<uint32_t>(id) < static_cast<uint32_t>(E);
+    atomicAdd(&hist[(ok ? (id >> 1) * kSub : 0) + sub],
+              ok ? 1u << ((id & 1) << 4) : 0u);
 }
 
 template <int G>
