@@ -77,6 +77,20 @@ class Rebalance:
         self.ue.ue_rebalance(self.ctx, self.routing, **self.out)
 
 
+def settle(fn, seconds=0.3):
+    """Runs ``fn`` back to back for about ``seconds`` (untimed), so that the
+    timed steps see the device at the clock it holds under a steady load:
+    on a fresh device the first few milliseconds of a workload ran up to 10%
+    slower than the same calls later in the run."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_steps(fn, steps, warmup):
     import torch
     for _ in range(warmup):
@@ -156,10 +170,12 @@ def bench_rebalance(ue, W, dev, steps, warmup):
     torch.cuda.synchronize()
     assert int(rb.out["faults"].sum()) == 0 and int(rb.out["invalid"].sum()) == 0
     log(f"dsv3: timing {steps} steps after {warmup} warmup")
+    settle(rb.step)
     ms = time_steps(rb.step, steps, warmup)
     phases = phase_times(rb, max(steps, 10))
     rb.cold = cold_times(rb)
     single = Rebalance(ue, cfg, routing[:1].contiguous(), dev)
+    settle(single.step)
     ms_one = time_steps(single.step, 50, 10)
     return cfg, rb, ms, phases, ms_one
 
@@ -248,6 +264,7 @@ def bench_rule(ue, cfg, routing, dev, steps, warmup, policy, quota_mode):
     """The same rebalance under another planner rule: time and the balance
     it reaches."""
     rb = Rebalance(ue, cfg, routing, dev, policy, quota_mode)
+    settle(rb.step)
     ms = time_steps(rb.step, steps, warmup)
     phases = phase_times(rb, max(steps, 10))
     return {"us_per_rebalance": round(ms * 1000.0, 2),
@@ -364,9 +381,7 @@ def bench_large_ep(ue, W, dev, policy=0, quota_mode=0):
     cfg = W.CONFIGS["large_ep"]
     routing = W.make_routing(cfg, device=dev)
     rb = Rebalance(ue, cfg, routing, dev, policy, quota_mode)
-    for _ in range(20):
-        rb.step()
-    torch.cuda.synchronize()
+    settle(rb.step)
     reps = 200
     ev = [events(2) for _ in range(reps)]
     for i in range(reps):
@@ -378,8 +393,9 @@ def bench_large_ep(ue, W, dev, policy=0, quota_mode=0):
     phases = phase_times(rb, 50)
     return {"workload": "large_ep: E=256 k=8 R=256 (1 native + 1 spare) "
                         "T=262144, 1 layer",
-            "planner": ("best fit" if policy == ue.PLAN_BEST_FIT
-                        else "least loaded") +
+            "planner": {ue.PLAN_LEAST_LOADED: "least loaded",
+                        ue.PLAN_BEST_FIT: "best fit",
+                        ue.PLAN_BEST_FIT_COVER: "best fit, covering order"}[policy] +
                        (", quota search" if quota_mode else ""),
             "us_per_rebalance_p10_p50_p90": [round(t[reps // 10], 2),
                                              round(t[reps // 2], 2),
@@ -456,6 +472,7 @@ def bench_stream(ue, W, dev):
              sync_bytes),
             ("grad_reduce", lambda: ctx.grad_reduce(rep_off, rep_buf),
              red_bytes)):
+        settle(fn)
         ms = time_steps(fn, 30, 5)
         gbs = nbytes / (ms * 1e-3) / 1e9
         res[name] = {"ms": round(ms, 4), "bytes": nbytes,
@@ -487,6 +504,7 @@ def bench_gather(ue, W, dev):
     out = torch.empty((cfg.assignments, cfg.hidden), dtype=torch.bfloat16,
                       device=dev)
     inv = rb.out["inv_perm"][0]
+    settle(lambda: rb.ctx.gather_rows(x, inv, out=out))
     ms = time_steps(lambda: rb.ctx.gather_rows(x, inv, out=out), 20, 3)
     nbytes = 2 * cfg.hidden * (cfg.tokens + cfg.assignments)
     gbs = nbytes / (ms * 1e-3) / 1e9

@@ -244,8 +244,11 @@ int ue_reroute(ue_ctx *ctx, const int32_t *routing, const void *placement,
  * microbatch and layer; this entry point is that path as three launches
  * with no host work between them. The reroute reuses the per-tile expert
  * prefixes the load kernel publishes, so it reads the routing once more but
- * never waits on another workgroup. Arguments are validated before the first
- * launch; a refusal leaves every output untouched. */
+ * never waits on another workgroup; and since the plan is made from these
+ * very counts, rank_counts and faults follow from it (the plan's loads
+ * after, and the ids out of range) and the planner's launch writes them.
+ * Arguments are validated before the first launch; a refusal leaves every
+ * output untouched. */
 int ue_rebalance(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
                  int32_t *counts, int32_t *invalid, void *placement,
                  int32_t *phys, int32_t *rank_counts, int32_t *perm,

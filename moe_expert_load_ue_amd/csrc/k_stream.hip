@@ -18,10 +18,12 @@
 // packed fp32 instructions): the fp32 gradient then lies within one
 // rounding of the exact sum even where replicas cancel the master, at no
 // cost in bandwidth. The gather reads each token
-// row once and writes it to the k dispatch positions of that token. Loads
-// are nontemporal; so are the stores of the reduction, while those of the
-// sync and the gather are plain (measured 1.3% and 2.5% faster for their
-// 1 : 2 and 1 : 8 mixes). The sync and the reduction run one workgroup
+// row once and writes it to the k dispatch positions of that token. The
+// reduction's and the gather's loads are nontemporal, the sync's plain
+// (measured faster in its one-workgroup-per-chunk form); the reduction's
+// stores are nontemporal, those of the sync and the gather plain (measured
+// 1.3% and 2.5% faster for their 1 : 2 and 1 : 8 mixes). The sync and the
+// reduction run one workgroup
 // per chunk, launched once, rather than a persistent grid (see the
 // launchers).
 #include "ue_internal.h"

@@ -172,16 +172,16 @@ def test_one_spare_slot_up_to_256_ranks(policy, quota_mode):
         compare_with_oracle(res, routing, E, R, 1)
 
 
-def test_many_layers_ragged_wide_load_groups():
-    """130 layers of 63 tiles each, the last one ragged: enough load groups
-    (130 x 4 of 16 tiles) for the 16-tile groups on a 256-CU device, with a
-    partial last group and a partial last tile in every layer."""
+def test_many_layers_ragged_load_groups():
+    """130 layers of 63 tiles each, the last one ragged: 130 x 8 load groups
+    of 8 tiles, with a partial last group (7 tiles) and a partial last tile
+    in every layer."""
     rng = np.random.default_rng(4321)
     E, R, S, k, T, L = 64, 8, 2, 8, 16001, 130
     routing = np.stack([pins.random_routing(rng, T, E, k,
                                             float(rng.uniform(0.5, 2.0)))
                         for _ in range(L)])
-    say(f"wide load groups: E={E} R={R} S={S} k={k} T={T} L={L}")
+    say(f"ragged load groups: E={E} R={R} S={S} k={k} T={T} L={L}")
     ctx = make_ctx(E, R, S, k, T, L)
     for fused in (False, True):
         res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
