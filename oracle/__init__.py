@@ -123,7 +123,8 @@ def plan(counts: np.ndarray, n_ranks: int, n_spare: int,
     ``policy`` 0: least-loaded destination; 1: best fit for a chunk the
     least-loaded rank would not fill; 2: best fit with the candidates in
     covering order (amounts one rank can take first, smallest first, then
-    the rest, largest first; fixed at the plain quota). ``quota_mode`` 0:
+    the rest, largest first; fixed at the plain quota); 3: best fit with
+    the candidates by ascending amount at the plain quota. ``quota_mode`` 0:
     Q = ceil(total / R); 1: the lowest of 64 raised quotas at which
     nothing is left."""
     c = np.ascontiguousarray(counts, dtype=np.int32).reshape(-1)

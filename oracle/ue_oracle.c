@@ -35,11 +35,12 @@
  *    the replica whose capacity prefix covers j (master first, then replicas
  *    in creation order);
  *    the dispatch permutation is the stable counting sort by physical slot.
- *  Three variants, each one step different (see Step 2): best fit for a
+ *  Four variants, each one step different (see Step 2): best fit for a
  *  remainder the least-loaded rank would not fill; best fit with the
  *  candidates visited in covering order (amounts one rank can take first,
- *  smallest first, then the rest, largest first); and a quota search that
- *  raises Q in small steps until the plan is no longer exhausted.
+ *  smallest first, then the rest, largest first); best fit with the
+ *  candidates visited by ascending amount; and a quota search that raises
+ *  Q in small steps until the plan is no longer exhausted.
  *
  * Everything is integer; there is nothing to round.
  */
@@ -76,6 +77,8 @@ int64_t orc_load(const int32_t *routing, int64_t n_assign, int32_t n_experts,
  * room to spare, the chunk goes to the eligible rank with the smallest
  * headroom that still takes all of it, ties to the lowest id. policy 2:
  * policy 1's destinations, candidates in covering order (greedy_cover_at).
+ * policy 3: policy 1's destinations, candidates by ascending amount
+ * (greedy_cover_at with `ascending`).
  *
  * quota_mode 0: Q = ceil(sum(counts) / R). quota_mode 1 (quota search):
  * with one spare slot a rank takes one chunk, so a chunk that leaves a
@@ -271,9 +274,16 @@ static void amounts_at(const int32_t *counts, int32_t E, int32_t R,
  *   - candidates with amount at Q0 at most H0 come first, by (amount asc,
  *     id asc); then the others, by (amount desc, id asc).
  * At the pass's quota Q each candidate in that order places its amount at
- * Q, chunk by chunk, into the destination policy 1 would choose. */
+ * Q, chunk by chunk, into the destination policy 1 would choose.
+ *
+ * Policy 3 (best fit, ascending amounts; `ascending` set): the same, with
+ * every candidate in one order, (amount at Q0 asc, id asc). The large
+ * amounts then also go smallest first: each takes the big pieces that
+ * remain after the smaller ones, and the largest amounts, which need many
+ * pieces in any order, come last and split over what is left. */
 static int greedy_cover_at(const int32_t *counts, int32_t E, int32_t R,
-                           int32_t S, int64_t Q0, int64_t Q, int64_t *load,
+                           int32_t S, int ascending, int64_t Q0, int64_t Q,
+                           int64_t *load,
                            int64_t *rem, int32_t *nfree, int32_t *cand,
                            int32_t *rec_e, int32_t *rec_p, int64_t *rec_m,
                            int32_t *nrec_out, int64_t *amt0, int64_t *amt)
@@ -297,7 +307,9 @@ static int greedy_cover_at(const int32_t *counts, int32_t E, int32_t R,
             const int32_t p = cand[i - 1];
             const int gp = amt0[p] > H0, ge = amt0[e] > H0;
             int before;
-            if (gp != ge)
+            if (ascending)
+                before = amt0[p] != amt0[e] ? amt0[e] > amt0[p] : p < e;
+            else if (gp != ge)
                 before = gp < ge;
             else if (amt0[p] != amt0[e])
                 before = ge ? amt0[p] > amt0[e] : amt0[p] < amt0[e];
@@ -337,9 +349,10 @@ static int pass_at(int32_t policy, const int32_t *counts, int32_t E,
                    int32_t *rec_e, int32_t *rec_p, int64_t *rec_m,
                    int32_t *nrec, int64_t *amt0, int64_t *amt)
 {
-    if (policy == 2)
-        return greedy_cover_at(counts, E, R, S, Q0, M, load, rem, nfree,
-                               cand, rec_e, rec_p, rec_m, nrec, amt0, amt);
+    if (policy >= 2)
+        return greedy_cover_at(counts, E, R, S, policy == 3, Q0, M, load,
+                               rem, nfree, cand, rec_e, rec_p, rec_m, nrec,
+                               amt0, amt);
     return greedy_at(counts, E, R, S, policy, M, load, rem, nfree, cand,
                      rec_e, rec_p, rec_m, nrec);
 }
@@ -350,7 +363,7 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
              int32_t *slot_expert, int32_t *slot_cap, int32_t *slot_off,
              int32_t *load_before, int32_t *load_after)
 {
-    if (E <= 0 || R <= 0 || S < 0 || E % R != 0 || policy < 0 || policy > 2)
+    if (E <= 0 || R <= 0 || S < 0 || E % R != 0 || policy < 0 || policy > 3)
         return -1;
     const int32_t N = E / R;       /* native experts per rank */
     const int32_t NS = N + S;      /* physical slots per rank */
@@ -364,7 +377,7 @@ int orc_plan(const int32_t *counts, int32_t E, int32_t R, int32_t S,
     int32_t *rec_e = calloc((size_t)(R * S + 1), sizeof(int32_t));
     int32_t *rec_p = calloc((size_t)(R * S + 1), sizeof(int32_t));
     int64_t *rec_m = calloc((size_t)(R * S + 1), sizeof(int64_t));
-    /* policy 2: each candidate's amount at Q0 and at the pass's quota */
+    /* policies 2, 3: each candidate's amount at Q0 and at the pass's quota */
     int64_t *amt0 = calloc((size_t)E, sizeof(int64_t));
     int64_t *amt = calloc((size_t)E, sizeof(int64_t));
     if (!load || !rem || !nfree || !cand || !rec_e || !rec_p || !rec_m ||

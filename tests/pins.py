@@ -164,17 +164,22 @@ def visit_order(counts, R, S, policy, Q):
     Policy 2: experts of ranks above Q0 = ceil(total / R); first those
     whose amount at Q0 is at most H0 (the largest headroom at Q0 among
     ranks with a spare slot), by amount asc, id asc; then the others by
-    amount desc, id asc."""
+    amount desc, id asc. Policy 3: experts of ranks above Q0 by amount at
+    Q0 asc, id asc."""
     counts = np.asarray(counts, np.int64)
     E = counts.size
     N = E // R
     L = counts.reshape(R, N).sum(axis=1)
-    if policy != 2:
+    if policy not in (2, 3):
         cands = sorted((e for e in range(E) if L[e // N] > Q),
                        key=lambda e: (-counts[e], e))
         return cands, rank_amounts(counts, R, Q)
     Q0 = -(-int(counts.sum()) // R)
     a0 = rank_amounts(counts, R, Q0)
+    if policy == 3:
+        cands = sorted((e for e in range(E) if L[e // N] > Q0),
+                       key=lambda e: (a0[e], e))
+        return cands, rank_amounts(counts, R, Q)
     H0 = max([Q0 - int(L[r]) for r in range(R) if S > 0 and L[r] < Q0],
              default=0)
     cands = [e for e in range(E) if L[e // N] > Q0]

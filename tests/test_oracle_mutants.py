@@ -116,6 +116,13 @@ MUTANTS = {
     "cover: amounts from the lightest expert": (
         "                if (best < 0 || counts[e] > counts[best])\n                    best = e;\n            }\n            prev = best;",
         "                if (best < 0 || counts[e] < counts[best])\n                    best = e;\n            }\n            prev = best;"),
+    "ascending: amounts largest first": (
+        "before = amt0[p] != amt0[e] ? amt0[e] > amt0[p] : p < e;",
+        "before = amt0[p] != amt0[e] ? amt0[e] < amt0[p] : p < e;"),
+    "ascending: ties to the higher id": (
+        "before = amt0[p] != amt0[e] ? amt0[e] > amt0[p] : p < e;",
+        "before = amt0[p] != amt0[e] ? amt0[e] > amt0[p] : p > e;"),
+    "ascending: covering order instead": ("if (ascending)\n", "if (0)\n"),
     "cover: least loaded instead of best fit": (
         "pick_destination(load, nfree, R, Q, need, 1)",
         "pick_destination(load, nfree, R, Q, need, 0)"),
@@ -143,6 +150,11 @@ def run_all_pins():
         pins.check_instance(*pins.random_instance(rng), policy=2)
     for _ in range(150):
         pins.check_instance(*pins.random_instance(rng), policy=2,
+                            quota_mode=1)
+    for _ in range(300):
+        pins.check_instance(*pins.random_instance(rng), policy=3)
+    for _ in range(150):
+        pins.check_instance(*pins.random_instance(rng), policy=3,
                             quota_mode=1)
     pins.check_no_spares(np.random.default_rng(1))
     pins.check_one_rank(np.random.default_rng(2))

@@ -11,9 +11,10 @@ def test_golden(case):
     pins.check_golden(case)
 
 
-RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1)]
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1), (3, 0), (3, 1)]
 RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
-            "best_fit_search", "cover", "cover_search"]
+            "best_fit_search", "cover", "cover_search", "ascending",
+            "ascending_search"]
 
 
 @pytest.mark.parametrize("policy,quota_mode", RULES, ids=RULE_IDS)
