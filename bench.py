@@ -242,9 +242,10 @@ def bench_stale(ue, W, dev, policy=0, quota_mode=0):
 # planner rules besides the default: (destination rule, quota mode)
 RULES = {"best_fit": (1, 0), "least_loaded_search": (0, 1),
          "best_fit_search": (1, 1), "best_fit_cover": (2, 0),
-         "best_fit_cover_search": (2, 1)}
+         "best_fit_cover_search": (2, 1), "best_fit_ascending": (3, 0),
+         "best_fit_ascending_search": (3, 1)}
 # the rule the balance target (max/mean <= 1.05) is reported for
-BALANCE_RULE = "best_fit_cover_search"
+BALANCE_RULE = "best_fit_ascending_search"
 BALANCE_TARGET = 1.05
 
 
@@ -395,7 +396,9 @@ def bench_large_ep(ue, W, dev, policy=0, quota_mode=0):
                         "T=262144, 1 layer",
             "planner": {ue.PLAN_LEAST_LOADED: "least loaded",
                         ue.PLAN_BEST_FIT: "best fit",
-                        ue.PLAN_BEST_FIT_COVER: "best fit, covering order"}[policy] +
+                        ue.PLAN_BEST_FIT_COVER: "best fit, covering order",
+                        ue.PLAN_BEST_FIT_ASCENDING:
+                            "best fit, ascending order"}[policy] +
                        (", quota search" if quota_mode else ""),
             "us_per_rebalance_p10_p50_p90": [round(t[reps // 10], 2),
                                              round(t[reps // 2], 2),
@@ -447,6 +450,7 @@ def balance_summary(line):
     return {"target_max_over_mean": BALANCE_TARGET,
             "default_rule_least_loaded": worst("least_loaded"),
             BALANCE_RULE: worst(BALANCE_RULE),
+            "best_fit_cover_search": worst("best_fit_cover_search"),
             "best_fit_search": worst("best_fit_search")}
 
 

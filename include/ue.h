@@ -81,8 +81,9 @@ typedef enum ue_status {
  *   max_tokens         largest T of any call (T*k < 2^30)
  *   max_layers         largest L (layers or microbatches) of any call
  *   plan_policy        rule of the planner (see ue_plan):
- *                      UE_PLAN_LEAST_LOADED (0), UE_PLAN_BEST_FIT (1) or
- *                      UE_PLAN_BEST_FIT_COVER (2)
+ *                      UE_PLAN_LEAST_LOADED (0), UE_PLAN_BEST_FIT (1),
+ *                      UE_PLAN_BEST_FIT_COVER (2) or
+ *                      UE_PLAN_BEST_FIT_ASCENDING (3)
  *   quota_mode         how the planner sets the quota (see ue_plan):
  *                      UE_QUOTA_FIXED (0) or UE_QUOTA_SEARCH (1)           */
 typedef struct ue_config {
@@ -101,9 +102,11 @@ enum {
     UE_PLAN_BEST_FIT = 1,      /* a chunk the least-loaded rank would not
                                   fill goes to the eligible rank with the
                                   smallest headroom that holds it          */
-    UE_PLAN_BEST_FIT_COVER = 2 /* best fit, candidates in covering order:
+    UE_PLAN_BEST_FIT_COVER = 2, /* best fit, candidates in covering order:
                                   amounts one rank can take first, smallest
                                   first, then the rest, largest first      */
+    UE_PLAN_BEST_FIT_ASCENDING = 3 /* best fit, candidates by their amount
+                                  at Q0, smallest first                   */
 };
 
 enum {
@@ -201,6 +204,10 @@ int ue_load(ue_ctx *ctx, const int32_t *routing, int32_t L, int32_t T,
  *   others (amount desc, id asc); each places its amount at the pass's
  *   quota. With one spare slot per rank every destination takes one
  *   chunk, and this order keeps the small pieces for the small amounts.
+ *   UE_PLAN_BEST_FIT_ASCENDING is the same with every candidate in the
+ *   first group: all amounts at Q0 ascending (ties: lowest id), so the
+ *   large amounts too go smallest first and the largest, which needs the
+ *   most pieces, is placed last, into what the others left.
  *   Under UE_QUOTA_SEARCH the plan above is made at the quotas
  *   Q0 + j*ceil(Q0/256), j = 0..63 (Q0 = ceil(sum(counts)/R)), in order,
  *   and the first that leaves nothing over is kept; with none, Q0 stands.

@@ -43,7 +43,8 @@ class ue_config(ctypes.Structure):
                 ("plan_policy", ctypes.c_int32),
                 ("quota_mode", ctypes.c_int32)]
 
-PLAN_LEAST_LOADED, PLAN_BEST_FIT, PLAN_BEST_FIT_COVER = 0, 1, 2
+PLAN_LEAST_LOADED, PLAN_BEST_FIT, PLAN_BEST_FIT_COVER, PLAN_BEST_FIT_ASCENDING = \
+    0, 1, 2, 3
 QUOTA_FIXED, QUOTA_SEARCH = 0, 1
 
 

@@ -22,7 +22,10 @@
 //   sources' excesses must cover, and a small excess left for last finds
 //   only big pieces, or none. The amounts one rank can take at Q0 (at most
 //   the largest headroom there) go first, smallest first, then the others,
-//   largest first; the order is fixed once, at Q0.
+//   largest first; the order is fixed once, at Q0. A fourth rule (best fit
+//   in ascending order) takes every amount at Q0 smallest first, so that
+//   of the amounts too large for one rank the largest, which needs the
+//   most pieces, is placed last.
 //   The quota search (also per context) makes the same plan at the quotas
 //   Q0 + j * ceil(Q0 / 256), j = 0..63, in order, and keeps the first that
 //   leaves nothing over (with none, Q0 stands): the pages call the
@@ -48,6 +51,7 @@
 //      scan.
 // Everything is integer and deterministic; the result does not depend on
 // scheduling.
+#include <climits>
 #include <mutex>
 
 #include "ue_internal.h"
@@ -866,7 +870,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // every kSplit-th other one; their sums meet through lane swaps)
     constexpr int kSplit = 4;
     static_assert(kSplit == 4, "quad_sum joins the four threads of a candidate");
-    const bool cover = policy == UE_PLAN_BEST_FIT_COVER;
+    const bool cover = policy == UE_PLAN_BEST_FIT_COVER ||
+                       policy == UE_PLAN_BEST_FIT_ASCENDING;
     const int2 *cand2 = reinterpret_cast<const int2 *>(s.cand);
     for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
         const int i = i0 + tid / kSplit;
@@ -925,11 +930,13 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         // a spare slot, comes from the smallest receiving key (the list
         // holds every rank with a spare slot and load below the highest
         // quota tried, sorted); amounts at Q0 up to H0 go first, smallest
-        // first, then the larger ones, largest first (ties: lowest id)
+        // first, then the larger ones, largest first (ties: lowest id).
+        // The ascending order is the same with no amount counted as large
         const int minload = nd > 0
             ? static_cast<int>(static_cast<uint32_t>(s.dsorted[0]) >> rbits)
             : Q0;
-        const int H0 = minload < Q0 ? Q0 - minload : 0;
+        const int H0 = policy == UE_PLAN_BEST_FIT_ASCENDING
+            ? INT_MAX : (minload < Q0 ? Q0 - minload : 0);
         for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
             const int i = i0 + tid / kSplit;
             const int q = tid % kSplit;

@@ -80,7 +80,8 @@ int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
         cfg.max_layers < 1 ||
         (cfg.plan_policy != UE_PLAN_LEAST_LOADED &&
          cfg.plan_policy != UE_PLAN_BEST_FIT &&
-         cfg.plan_policy != UE_PLAN_BEST_FIT_COVER) ||
+         cfg.plan_policy != UE_PLAN_BEST_FIT_COVER &&
+         cfg.plan_policy != UE_PLAN_BEST_FIT_ASCENDING) ||
         (cfg.quota_mode != UE_QUOTA_FIXED &&
          cfg.quota_mode != UE_QUOTA_SEARCH))
         return UE_EUNSUPPORTED;

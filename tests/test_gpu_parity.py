@@ -20,11 +20,12 @@ def make_ctx(E, R, S, k, T, L=1, policy=ue.PLAN_LEAST_LOADED,
                       plan_policy=policy, quota_mode=quota_mode)
 
 
-# (destination rule, quota mode): the default, best fit, and each with the
-# quota search
-RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1)]
+# (destination rule, quota mode): the default, best fit, best fit in
+# covering order and in ascending order, each also with the quota search
+RULES = [(0, 0), (1, 0), (0, 1), (1, 1), (2, 0), (2, 1), (3, 0), (3, 1)]
 RULE_IDS = ["least_loaded", "best_fit", "least_loaded_search",
-            "best_fit_search", "cover", "cover_search"]
+            "best_fit_search", "cover", "cover_search", "ascending",
+            "ascending_search"]
 
 
 @pytest.mark.parametrize("case", [g for g in pins.golden_cases()
@@ -374,6 +375,6 @@ def test_refusals_leave_outputs_untouched():
         with pytest.raises(ue.UEError):
             ue.Context(*bad, 100, 1, device=DEV)
     with pytest.raises(ue.UEError):
-        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=3)
+        ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=4)
     with pytest.raises(ue.UEError):
         ue.Context(64, 8, 1, 8, 100, 1, device=DEV, quota_mode=2)

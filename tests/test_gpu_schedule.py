@@ -87,9 +87,10 @@ def as_result(ctx, outs):
     return res
 
 
-@pytest.mark.parametrize("policy,quota_mode", [(0, 0), (1, 1), (2, 1)],
+@pytest.mark.parametrize("policy,quota_mode",
+                         [(0, 0), (1, 1), (2, 1), (3, 1)],
                          ids=["least_loaded", "best_fit_search",
-                              "cover_search"])
+                              "cover_search", "ascending_search"])
 def test_plan_driven_sync_restore_reduce(policy, quota_mode):
     E, R, S, k, T = 32, 8, 2, 4, 3000
     rng = np.random.default_rng(5 + policy)

@@ -17,8 +17,9 @@ from moe_expert_load_ue_amd import workloads as W
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
-RULES = [(0, 0), (1, 1), (2, 1)]
-RULE_IDS = ["least_loaded", "best_fit_search", "cover_search"]
+RULES = [(0, 0), (1, 1), (2, 1), (3, 1)]
+RULE_IDS = ["least_loaded", "best_fit_search", "cover_search",
+            "ascending_search"]
 
 
 def oracle_plans(counts, cfg, policy, quota_mode):

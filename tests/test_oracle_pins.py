@@ -38,7 +38,7 @@ def test_invariants_larger(policy, quota_mode):
 
 def test_quota_search_large_quota():
     """Quotas in the thousands (steps of ceil(Q0/256) > 1): the kept quota
-    is on the grid and every lower step exhausts, for both rules."""
+    is on the grid and every lower step exhausts, for every rule."""
     rng = np.random.default_rng(8)
     for it in range(12):
         R = int(rng.choice([4, 8, 16]))
@@ -46,7 +46,7 @@ def test_quota_search_large_quota():
         E = R * N
         k = int(min(E, 4))
         routing = pins.random_routing(rng, 6000, E, k, float(rng.uniform(0.8, 2)))
-        for policy in (0, 1, 2):
+        for policy in (0, 1, 2, 3):
             pl = pins.check_instance(routing, E, R, 1, policy=policy,
                                      quota_mode=1)
             assert pl["quota"] >= 256     # the step is above one token here
