@@ -122,8 +122,13 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
 // that loads the replica table once and loops over tiles measured no
 // faster: the hardware already overlaps one workgroup's table reads with
 // others' work, while the LDS per workgroup sets how many share a CU.)
+// After a load the kernel is held to 8 waves per SIMD (64 VGPRs), which it
+// meets without spilling: left to itself the compiler takes 68 and 7 waves,
+// 5% slower at dsv3 size. The standalone instance would spill at 64 and is
+// left free.
 template <bool kAfterLoad>
-__global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(RerouteArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kWaves], wany[kWaves];
     __shared__ uint32_t s_ticket, s_epoch;
@@ -263,11 +268,14 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
     // capacity prefix of each replica within its expert, from LDS; replica
     // r of expert e then covers j in [r == rep_off[e] ? 0 : rep_hi[r-1],
-    // rep_hi[r]). After a load the tile's first j of each expert (its
-    // prefix) is already known, so the same pass finds the replica that
-    // covers it: how many of the tile's assignments it still takes, its
-    // slot and the dispatch position of that first j (fields y, z, w of
-    // the expert's record; x, the tile's own order, follows the scan).
+    // rep_hi[r]). The prefix saturates at A: every j is below A, so a
+    // larger end covers the same j, and the prefix stays non-decreasing
+    // (searchable by bisection) whatever the capacities. After a load the
+    // tile's first j of each expert (its prefix) is already known, so the
+    // same pass finds the replica that covers it: how many of the tile's
+    // assignments it still takes, its slot and the dispatch position of
+    // that first j (fields y, z, w of the expert's record; x, the tile's
+    // own order, follows the scan).
 #pragma unroll
     for (int q = 0; q < kPerThread; ++q) {
         const int e = tid + q * kBlock;
@@ -278,7 +286,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         const int hi = rep_off[e + 1];
         for (int i = rep_off[e]; i < hi; ++i) {
             const int lo = run;
-            run += rep_hi[i];
+            const int cap = rep_hi[i];
+            run = cap < A - run ? run + cap : A;
             rep_hi[i] = run;
             if (kAfterLoad && !found && j0 < run) {
                 found = true;
@@ -296,21 +305,27 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     }
     // Physical slot and dispatch position of assignment j of expert e, or
     // -1 for both if no replica covers j (only a plan made for other counts
-    // leaves such assignments).
-    auto locate = [&](int e, int j, int &p, int &pos) {
+    // leaves such assignments); end is set to the covering replica's
+    // capacity prefix. The replica is the first of the expert's whose
+    // prefix exceeds j, found by bisection: an expert split into many
+    // pieces costs a few steps, not one per piece.
+    auto locate = [&](int e, int j, int &p, int &pos, int &end) {
         p = -1;
         pos = -1;
-        int lo = 0;
-        for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-            const int hi = rep_hi[r];
-            if (j < hi) {
-                if (rep_slot[r] >= 0) {
-                    p = rep_slot[r];
-                    pos = slot_off[p] + (j - lo);
-                }
-                return;
+        end = 0;
+        const int first = rep_off[e], last = rep_off[e + 1];
+        int lo = first, hi = last;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (rep_hi[mid] > j) hi = mid;
+            else lo = mid + 1;
+        }
+        if (lo < last) {
+            end = rep_hi[lo];
+            if (rep_slot[lo] >= 0) {
+                p = rep_slot[lo];
+                pos = slot_off[p] + (j - (lo > first ? rep_hi[lo - 1] : 0));
             }
-            lo = hi;
         }
     };
     const uint32_t epoch = s_epoch;
@@ -484,19 +499,9 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
     if (!kAfterLoad) {
         for (int e = tid; e < E; e += kBlock) {
             const int j0 = einfo[e].w;
-            int q, pos0;
-            locate(e, j0, q, pos0);
-            int lim = 0;
-            if (q >= 0) {
-                // the covering replica's end: the first capacity prefix
-                // above j0
-                for (int r = rep_off[e]; r < rep_off[e + 1]; ++r) {
-                    if (j0 < rep_hi[r]) {
-                        lim = rep_hi[r] - j0;
-                        break;
-                    }
-                }
-            }
+            int q, pos0, end;
+            locate(e, j0, q, pos0, end);
+            const int lim = q >= 0 ? end - j0 : 0;
             ehalf[8 * e + 1] =
                 static_cast<uint16_t>(lim < kRerouteTile ? lim : kRerouteTile);
             einfo[e].y = q;
@@ -527,7 +532,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
                 p = f.y;
                 pos = f.z + jt;
             } else {
-                locate(id, f.w + jt, p, pos);
+                int end;
+                locate(id, f.w + jt, p, pos, end);
             }
         }
         const bool ok = p >= 0 && pos >= 0 && pos < A;
@@ -553,7 +559,8 @@ __global__ __launch_bounds__(kBlock) void k_reroute(RerouteArgs g) {
         const int4 f = einfo[e];
         const int jt = s2 - (f.x & 0xFFFF);
         int p = f.y, pos = f.z + jt;
-        if (jt >= (f.x >> 16)) locate(e, f.w + jt, p, pos);
+        int end;
+        if (jt >= (f.x >> 16)) locate(e, f.w + jt, p, pos, end);
         if (p >= 0 && pos >= 0 && pos < A)
             *at(perm_l, pos) = tile0 + static_cast<int>(v & 2047u);
     }
