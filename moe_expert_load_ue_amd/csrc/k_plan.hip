@@ -674,11 +674,28 @@ struct ScanArgs {
 constexpr int kModeScan = 1;   // finish the load (ScanArgs)
 constexpr int kModePlan = 2;   // make the plan
 
+// The quota search spread over `split` workgroups per layer (1: not
+// spread). Each runs part A and then kSplitWaves passes, one per SIMD, at
+// quotas j = p * kSplitWaves + wave (p: its place among the layer's): with 16 waves on four SIMDs the
+// passes of one workgroup contend for issue, one per SIMD they do not.
+// Each publishes, per pass, the number of chunks (or -1 when the pass ran
+// out) and a successful pass's chunks; the last workgroup of the layer to
+// finish (a counter per layer, reset by that workgroup) keeps the first
+// quota that works and goes on alone: with the plan from there, or with
+// the remaining quotas in rounds as above. No workgroup waits on another.
+constexpr int kSplitWaves = 4;
+struct SplitArgs {
+    int split;
+    int32_t *rec;      // [slots][3][R*S] chunks (expert, slot, amount)
+    int32_t *flag;     // [slots] chunks of a pass that works, else -1
+    uint32_t *cnt;     // [layers] workgroups done; 0 between calls
+};
+
 __global__ __launch_bounds__(kPlanBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
     int P, int rbits, int policy, int quota_mode, int per_wave,
     uint32_t lds_bytes, ue_placement_layout lay,
-    int32_t *__restrict__ placement, int mode, ScanArgs sc) {
+    int32_t *__restrict__ placement, int mode, ScanArgs sc, SplitArgs sp) {
     extern __shared__ __align__(16) int32_t lds[];
     __shared__ int wsum[kPlanWaves];
     __shared__ int wsum3[3 * kPlanWaves];
@@ -687,8 +704,14 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     __shared__ int s_nrec, s_exhausted, s_quota, s_region;
     __shared__ uint32_t wsat[kPlanWaves];
     __shared__ int scan_tot[kMaxExperts];   // scan: the layer's counts
+    __shared__ int s_last, s_first;
 
-    const int layer = blockIdx.x;
+    // workgroups of one layer: the first writes everything before the
+    // plan (the others compute the same values), the last to finish makes
+    // the plan itself
+    const int split = sp.split;
+    const int layer = static_cast<int>(blockIdx.x) / split;
+    const int wg_part = static_cast<int>(blockIdx.x) - layer * split;
     const int tid = threadIdx.x;
 
     if (mode & kModeScan) {
@@ -736,13 +759,14 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
                 int all = 0;
                 for (int jj = 0; jj < PT; ++jj) all += lds[jj * E + e];
                 scan_tot[e] = all;
-                sc.counts[static_cast<int64_t>(layer) * E + e] = all;
+                if (wg_part == 0) sc.counts[static_cast<int64_t>(layer) * E + e] = all;
             }
             for (int b = g0; b < g1; b += 8) {
                 if (cs > 8) load8(b);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    if (b + q < g1) gb[static_cast<int64_t>(b + q) * E + e] = run;
+                    if (b + q < g1 && wg_part == 0)
+                        gb[static_cast<int64_t>(b + q) * E + e] = run;
                     run += y[q];
                 }
             }
@@ -754,7 +778,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         for (int x = tid; x < E; x += kPlanBlock) part += scan_tot[x];
         int total;
         plan_block_sum(part, wsum, total);
-        if (tid == 0 && sc.invalid)
+        if (tid == 0 && sc.invalid && wg_part == 0)
             sc.invalid[layer] = static_cast<int32_t>(sc.A - total);
         if (!(mode & kModePlan)) return;
     }
@@ -765,6 +789,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // the carve-up must fit the launch's LDS (checked, not assumed); a
     // mismatch marks the block (exhausted = -1) rather than pass silently
     if (static_cast<size_t>(carve_end(s, P) - lds) * 4 > lds_bytes) {
+        if (wg_part != 0) return;
         if (tid == 0) out[lay.exhausted] = -1;
         // the table is not written: every assignment is marked a fault
         for (int r = tid; r < R && sc.rank_counts; r += kPlanBlock)
@@ -806,6 +831,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
             // not planned: an empty table (no replica, every later reroute
             // assignment a fault), marked exhausted = -1; uniform across
             // the block, so every thread leaves here
+            if (wg_part != 0) return;
             for (int i = tid; i < lay.words; i += kPlanBlock) {
                 const bool neg1 =
                     i == lay.exhausted ||
@@ -829,7 +855,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         int l = 0;
         for (int i = 0; i < N; ++i) l += s.cnt[r * N + i];
         s.load[r] = l;
-        out[lay.load_before + r] = l;
+        if (wg_part == 0) out[lay.load_before + r] = l;
     }
     __syncthreads();
 
@@ -982,8 +1008,90 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     int Q = Q0;
     int j0 = 0;
     bool rec = !search;
+    bool chosen = false;
+    if (search && split > 1) {
+        // the first kSplitWaves * split quotas, spread over the layer's
+        // workgroups (records per wave: the host spreads only then)
+        int nrec_w = 0, exh_w = 1;
+        if (wave < kSplitWaves) {
+            PlanLds sw = s;
+            sw.rec_e = s.rec_e + wave * 3 * RS;
+            sw.rec_p = sw.rec_e + RS;
+            sw.rec_m = sw.rec_e + 2 * RS;
+            spill_pass(sw, ncand, nd, R, S, N, NS,
+                       Q0 + (wg_part * kSplitWaves + wave) * step, rbits,
+                       best_fit, true, nrec_w, exh_w);
+        }
+        if ((tid & 63) == 0 && wave < kSplitWaves) {
+            s_works[wave] = !exh_w;
+            s_nrecw[wave] = nrec_w;
+        }
+        __syncthreads();
+        // publish: chunk counts, and the chunks of the passes that work
+        const int64_t slot0 = static_cast<int64_t>(blockIdx.x) * kSplitWaves;
+        for (int w = 0; w < kSplitWaves; ++w) {
+            if (!s_works[w]) continue;
+            const int n = s_nrecw[w];
+            const int32_t *src = s.rec_e + w * 3 * RS;
+            int32_t *dst = sp.rec + (slot0 + w) * 3 * RS;
+            for (int i = tid; i < n; i += kPlanBlock) {
+                dst[i] = src[i];
+                dst[RS + i] = src[RS + i];
+                dst[2 * RS + i] = src[2 * RS + i];
+            }
+        }
+        if (tid < kSplitWaves)
+            sp.flag[slot0 + tid] = s_works[tid] ? s_nrecw[tid] : -1;
+        // one device-scope fence per workgroup on each side, after the
+        // barrier that orders the workgroup's own stores and loads: each
+        // such fence writes back or invalidates a whole L2, so one per
+        // wave would cost a multiple of the plan
+        __syncthreads();
+        if (tid == 0) {
+            __threadfence();
+            s_last = atomicAdd(sp.cnt + layer, 1u) == static_cast<uint32_t>(split - 1);
+            if (s_last) __threadfence();
+        }
+        __syncthreads();
+        if (!s_last) return;
+        const int nq = kSplitWaves * split;
+        const int64_t lslot0 = static_cast<int64_t>(layer) * nq;
+        static_assert(kSplitWaves * 16 <= 64, "one wave reads every flag");
+        if (tid < 64) {
+            // the flags read at once, one per lane; the first that works
+            const bool works = tid < nq && sp.flag[lslot0 + tid] >= 0;
+            const uint64_t b = __ballot(works);
+            if (tid == 0) {
+                sp.cnt[layer] = 0;
+                s_first = b ? __builtin_ctzll(b) : -1;
+            }
+        }
+        __syncthreads();
+        const int first = s_first;
+        if (first >= 0) {
+            const int n = sp.flag[lslot0 + first];
+            const int32_t *src = sp.rec + (lslot0 + first) * 3 * RS;
+            for (int i = tid; i < n; i += kPlanBlock) {
+                s.rec_e[i] = src[i];
+                s.rec_p[i] = src[RS + i];
+                s.rec_m[i] = src[2 * RS + i];
+            }
+            if (tid == 0) {
+                s_nrec = n;
+                s_exhausted = 0;
+                s_quota = Q0 + first * step;
+                s_region = 0;
+            }
+            Q = Q0 + first * step;
+            chosen = true;
+        } else {
+            j0 = nq;
+            rec = j0 >= kQuotaSteps;
+        }
+        __syncthreads();
+    }
 #pragma unroll 1
-    while (true) {
+    while (!chosen) {
         int nrec_w = 0, exh_w = 0;
         PlanLds sw = s;
         if (!rec && per_wave) {
@@ -1156,13 +1264,28 @@ hipError_t plan_prepare(size_t lds_bytes) {
 static hipError_t launch(const ue_ctx &c, const int32_t *counts, int L,
                          int32_t *placement, int mode, const ScanArgs &sc,
                          hipStream_t s) {
-    hipLaunchKernelGGL(k_plan, dim3(L), dim3(kPlanBlock), c.plan_lds, s,
+    // spread the quota search when its passes are long (more than 64
+    // receiving ranks: at 64 or fewer a pass takes a few microseconds, and
+    // the exchange costs what the spread saves) and the layers' workgroups
+    // then fit the device one per CU, with pass slots for all of them
+    SplitArgs sp{1, c.plan_xrec, c.plan_xflag, c.plan_xcnt};
+    if ((mode & kModePlan) && c.plan_xrec && c.R > 64 &&
+        c.cfg.quota_mode == UE_QUOTA_SEARCH) {
+        for (const int cand : {16, 4}) {
+            if (static_cast<int64_t>(L) * cand <= c.num_cu &&
+                static_cast<int64_t>(L) * cand * kSplitWaves <= c.plan_xslots) {
+                sp.split = cand;
+                break;
+            }
+        }
+    }
+    hipLaunchKernelGGL(k_plan, dim3(L * sp.split), dim3(kPlanBlock), c.plan_lds, s,
                        counts, c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
                        static_cast<int>(c.cfg.plan_policy),
                        static_cast<int>(c.cfg.quota_mode),
                        c.plan_per_wave ? 1 : 0,
                        static_cast<uint32_t>(c.plan_lds), c.lay, placement,
-                       mode, sc);
+                       mode, sc, sp);
     return hipGetLastError();
 }
 

@@ -199,6 +199,14 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
         take(sizeof(uint16_t) * (Lmax * rr_tiles + ld_rows) * E);
     const size_t o_state = take(sizeof(uint64_t) * Lmax * rr_tiles * E);
     const size_t o_tick = take(sizeof(uint64_t) * Lmax);
+    // the spread quota search's exchange (only with the search and the
+    // chunks of every pass kept)
+    const bool spread = c->plan_per_wave && c->R > 64;
+    const int xslots = spread ? 4 * c->num_cu : 0;
+    const size_t o_xrec =
+        take(sizeof(int32_t) * 3 * static_cast<size_t>(xslots) * c->R * c->S);
+    const size_t o_xflag = take(sizeof(int32_t) * xslots);
+    const size_t o_xcnt = take(spread ? sizeof(uint32_t) * Lmax : 0);
     c->ws_bytes = off;
     he = hipMalloc(&c->ws, c->ws_bytes);
     if (he != hipSuccess) {
@@ -217,6 +225,12 @@ int ue_create(const ue_config *cfg, ue_ctx **out) {
     c->tile_off = reinterpret_cast<uint16_t *>(b + o_toff);
     c->scan_state = reinterpret_cast<uint64_t *>(b + o_state);
     c->rr_tick = reinterpret_cast<uint64_t *>(b + o_tick);
+    if (spread) {
+        c->plan_xrec = reinterpret_cast<int32_t *>(b + o_xrec);
+        c->plan_xflag = reinterpret_cast<int32_t *>(b + o_xflag);
+        c->plan_xcnt = reinterpret_cast<uint32_t *>(b + o_xcnt);
+        c->plan_xslots = xslots;
+    }
     *out = c;
     return UE_OK;
 }

@@ -64,6 +64,14 @@ struct ue_ctx {
 
     size_t plan_lds = 0;
     bool plan_per_wave = false;   // planner keeps every pass's chunks
+    // the quota search spread over several workgroups per layer: per pass
+    // slot (4 per workgroup, at most 4 * num_cu) its chunks and their
+    // number, and per layer a count of workgroups done (zero between
+    // calls); null when the search is not spread (then one per layer)
+    int32_t *plan_xrec = nullptr;    // [plan_xslots][3][R*S]
+    int32_t *plan_xflag = nullptr;   // [plan_xslots]
+    uint32_t *plan_xcnt = nullptr;   // [max_layers]
+    int plan_xslots = 0;
     size_t reroute_lds = 0;
 
     // Registered expert state (device pointer tables).

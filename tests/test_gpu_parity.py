@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import moe_expert_load_ue_amd as ue
+import oracle
 import pins
 from gpu_helpers import compare_with_oracle, gpu_rebalance, say
 from moe_expert_load_ue_amd import workloads as W
@@ -378,3 +379,57 @@ def test_refusals_leave_outputs_untouched():
         ue.Context(64, 8, 1, 8, 100, 1, device=DEV, plan_policy=4)
     with pytest.raises(ue.UEError):
         ue.Context(64, 8, 1, 8, 100, 1, device=DEV, quota_mode=2)
+
+
+def _layer_from_loads(rng, loads):
+    """k = 1 routing whose expert e (one per rank) gets loads[e] tokens,
+    in random token order."""
+    ids = np.repeat(np.arange(len(loads), dtype=np.int32), loads)
+    rng.shuffle(ids)
+    return ids.reshape(-1, 1)
+
+
+@pytest.mark.parametrize("policy", [0, 1, 2, 3],
+                         ids=["least_loaded", "best_fit", "cover", "ascending"])
+@pytest.mark.parametrize("L", [3, 20])
+def test_spread_search_late_and_no_quota(policy, L):
+    """The quota search with more than 64 ranks, spread over several
+    workgroups per layer (16 each for a few layers: 64 quotas at once; 4
+    each for up to 64 layers: 16 quotas, then rounds in the last one).
+    Layers built so that the first quota that works is step 18 (88 ranks
+    just above it, 20 far above, 20 empty), or none of the 64 does (100
+    ranks above the highest quota tried, 28 empty: more sources than spare
+    slots), or random skew; bit-exact against the oracle."""
+    rng = np.random.default_rng(55 + L + 7 * policy)
+    R = 128
+    late = np.array([1070] * 88 + [1690] * 20 + [0] * 20)
+    T = int(late.sum())
+    none = np.array([T // 100] * 100 + [0] * 28)
+    none[0] += T - int(none.sum())
+    layers = []
+    for i in range(L):
+        kind = i % 3
+        if kind == 0:
+            loads = rng.permutation(late)
+        elif kind == 1:
+            loads = rng.permutation(none)
+        else:
+            r = pins.random_routing(rng, T, R, 1, float(rng.uniform(0.5, 3)))
+            loads = np.bincount(r.reshape(-1), minlength=R)
+        layers.append(_layer_from_loads(rng, loads))
+    routing = np.stack(layers)
+    # the cases are what they claim (checked on the oracle first)
+    for i in range(min(L, 2)):
+        c = np.bincount(routing[i].reshape(-1), minlength=R).astype(np.int32)
+        pl = oracle.plan(c, R, 1, policy, 1)
+        Q0 = -(-int(c.sum()) // R)
+        if i % 3 == 0:
+            assert pl["quota"] == Q0 + 18 * (-(-Q0 // 256))
+            assert not pl["exhausted"]
+        else:
+            assert pl["exhausted"] and pl["quota"] == Q0
+    say(f"spread search: R={R} L={L} T={T} policy={policy}")
+    ctx = make_ctx(R, R, 1, 1, T, L, policy, ue.QUOTA_SEARCH)
+    for fused in (True, False):
+        res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
+        compare_with_oracle(res, routing, R, R, 1)
