@@ -691,6 +691,10 @@ struct SplitArgs {
     uint32_t *cnt;     // [layers] workgroups done; 0 between calls
 };
 
+// kSpread: the quota search may be spread (sp.split > 1); the other
+// instance is the plain one-workgroup-per-layer planner, compiled without
+// any of it.
+template <bool kSpread>
 __global__ __launch_bounds__(kPlanBlock) void k_plan(
     const int32_t *__restrict__ counts, int E, int R, int S, int N, int NS,
     int P, int rbits, int policy, int quota_mode, int per_wave,
@@ -709,9 +713,10 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     // workgroups of one layer: the first writes everything before the
     // plan (the others compute the same values), the last to finish makes
     // the plan itself
-    const int split = sp.split;
-    const int layer = static_cast<int>(blockIdx.x) / split;
-    const int wg_part = static_cast<int>(blockIdx.x) - layer * split;
+    const int split = kSpread ? sp.split : 1;
+    const int layer = kSpread ? static_cast<int>(blockIdx.x) / split
+                              : static_cast<int>(blockIdx.x);
+    const int wg_part = kSpread ? static_cast<int>(blockIdx.x) - layer * split : 0;
     const int tid = threadIdx.x;
 
     if (mode & kModeScan) {
@@ -963,26 +968,29 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
             : Q0;
         const int H0 = policy == UE_PLAN_BEST_FIT_ASCENDING
             ? INT_MAX : (minload < Q0 ? Q0 - minload : 0);
+        // one key per candidate orders all three levels at once: the
+        // group (the amounts one rank can take first), the amount within
+        // it (ascending, or descending among the large ones; amounts are
+        // below 2^30), then the id (below 2^16); a branch-free compare
+        // keeps both reads of each step in flight together
+        auto ckey = [&](int a_, int f_) -> uint64_t {
+            const uint32_t k_ = a_ > H0
+                ? 0x80000000u | static_cast<uint32_t>(0x3FFFFFFF - a_)
+                : static_cast<uint32_t>(a_);
+            return (static_cast<uint64_t>(k_) << 16) | static_cast<uint32_t>(f_);
+        };
         for (int i0 = 0; i0 < ncand; i0 += kPlanBlock / kSplit) {
             const int i = i0 + tid / kSplit;
             const int q = tid % kSplit;
             const bool act = i < ncand;
             const int2 me = act ? cand2[i] : int2{0, 0};
             const int e = me.x & 0xFFFF;
-            const int a = act ? s.camt[i] : 0;
-            const bool big = a > H0;
+            const uint64_t mk = ckey(act ? s.camt[i] : 0, e);
             int pos = 0;
             if (act) {
 #pragma unroll 4
-                for (int j = q; j < ncand; j += kSplit) {
-                    const int aj = s.camt[j];
-                    const bool bj = aj > H0;
-                    const int f = cand2[j].x & 0xFFFF;
-                    const bool earlier =
-                        bj != big ? !bj
-                                  : (aj != a ? (big ? aj > a : aj < a) : f < e);
-                    pos += earlier;
-                }
+                for (int j = q; j < ncand; j += kSplit)
+                    pos += ckey(s.camt[j], cand2[j].x & 0xFFFF) < mk;
             }
             pos = quad_sum(pos);
             if (act && q == 0) {
@@ -1009,7 +1017,7 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
     int j0 = 0;
     bool rec = !search;
     bool chosen = false;
-    if (search && split > 1) {
+    if (kSpread && search && split > 1) {
         // the first kSplitWaves * split quotas, spread over the layer's
         // workgroups (records per wave: the host spreads only then)
         int nrec_w = 0, exh_w = 1;
@@ -1253,10 +1261,15 @@ hipError_t plan_prepare(size_t lds_bytes) {
     static size_t granted = 0;
     std::lock_guard<std::mutex> lock(mu);
     if (lds_bytes <= granted) return hipSuccess;
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_plan),
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_plan<false>),
         hipFuncAttributeMaxDynamicSharedMemorySize,
         static_cast<int>(lds_bytes));
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_plan<true>),
+            hipFuncAttributeMaxDynamicSharedMemorySize,
+            static_cast<int>(lds_bytes));
     if (e == hipSuccess) granted = lds_bytes;
     return e;
 }
@@ -1279,7 +1292,8 @@ static hipError_t launch(const ue_ctx &c, const int32_t *counts, int L,
             }
         }
     }
-    hipLaunchKernelGGL(k_plan, dim3(L * sp.split), dim3(kPlanBlock), c.plan_lds, s,
+    auto kernel = sp.split > 1 ? k_plan<true> : k_plan<false>;
+    hipLaunchKernelGGL(kernel, dim3(L * sp.split), dim3(kPlanBlock), c.plan_lds, s,
                        counts, c.E, c.R, c.S, c.N, c.NS, c.P, c.rbits,
                        static_cast<int>(c.cfg.plan_policy),
                        static_cast<int>(c.cfg.quota_mode),
