@@ -68,6 +68,7 @@ hipError_t device_info(int dev, DeviceInfo &out) {
     out.lds_cap = prop.sharedMemPerBlock;
     if (prop.sharedMemPerBlockOptin > out.lds_cap)
         out.lds_cap = prop.sharedMemPerBlockOptin;
+    out.lds_per_cu = prop.maxSharedMemoryPerMultiProcessor;
     return hipSuccess;
 }
 
@@ -120,6 +121,7 @@ int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
     l.words = static_cast<int>(round_up(w, 64));   // 256-byte blocks
 
     c.reroute_lds = reroute_lds_bytes(E, R, c.P, k);
+    c.count_lds = count_lds_bytes(E, info.lds_per_cu, info.lds_cap);
     // the quota search keeps each pass's chunks when they fit in LDS
     c.plan_per_wave = cfg.quota_mode == UE_QUOTA_SEARCH &&
                       plan_lds_bytes(E, R, S, c.P, true) + kPlanStaticLds <=

@@ -64,6 +64,7 @@ struct ue_ctx {
 
     size_t plan_lds = 0;
     bool plan_per_wave = false;   // planner keeps every pass's chunks
+    size_t count_lds = 0;         // LDS the count asks for (see k_load)
     // the quota search spread over several workgroups per layer: per pass
     // slot (4 per workgroup, at most 4 * num_cu) its chunks and their
     // number, and per layer a count of workgroups done (zero between
@@ -138,6 +139,7 @@ hipError_t launch_gather_rows(const ue_ctx &c, const void *x,
 struct DeviceInfo {
     int num_cu = 0;
     size_t lds_cap = 0;      // dynamic LDS one workgroup may have
+    size_t lds_per_cu = 0;   // LDS of one CU
 };
 hipError_t device_info(int dev, DeviceInfo &out);
 // Validates a configuration and fills the shape fields of `c` (sizes,
@@ -152,6 +154,10 @@ const char *static_last_error();
 constexpr size_t kPlanStaticLds = 5120;
 
 size_t load_lds_bytes(int E);
+// LDS the count kernel asks for: its need, or a quarter of a CU's LDS
+// when that is more (and allowed), so that at most four of its workgroups
+// share a CU
+size_t count_lds_bytes(int E, size_t lds_per_cu, size_t lds_cap);
 // The load's split of one call over L layers of A assignments: tiles of
 // kLoadTile assignments, groups of `group` consecutive tiles (one counting
 // workgroup each). The count, the scan and the fused reroute all take it
