@@ -162,11 +162,14 @@ size_t load_lds_bytes(int E) { return load_lds_bytes_for(E, kLoadGroup); }
 // CU, held there by the LDS each asks for, count 58 dsv3 layers in 23.6
 // instead of 25.2 us (three per CU: 27.5 us; same box). The request stays
 // within the 64 KiB a launch gets without raising the kernel's limit.
-constexpr int kCountPerCU = 4;
+size_t quarter_cu_lds(size_t lds_per_cu, size_t lds_cap) {
+    const size_t share = lds_per_cu / 4;
+    return (share <= 65536 && share <= lds_cap) ? share : 0;
+}
 size_t count_lds_bytes(int E, size_t lds_per_cu, size_t lds_cap) {
     const size_t need = load_lds_bytes(E);
-    const size_t share = lds_per_cu / kCountPerCU;
-    return (share > need && share <= 65536 && share <= lds_cap) ? share : need;
+    const size_t share = quarter_cu_lds(lds_per_cu, lds_cap);
+    return share > need ? share : need;
 }
 
 LoadShape load_shape(int64_t A, int L) {

@@ -268,8 +268,11 @@ hipError_t launch_weight_sync(const ue_ctx &c, const int32_t *rep_off,
     // grid striding over the matrices spreads them out); at the 32-expert,
     // 64-replica shape this measured 5.6 TB/s against 5.0 persistent (and
     // 5.1 with 4 KiB chunks, 5.5 with 8 KiB)
+    // (at most four workgroups per CU, held there by the LDS each asks
+    // for and does not use: 5.66 against 5.63 TB/s for the sync, 6.26
+    // against 6.09 for the reduction, same box; the gather gains nothing)
     hipLaunchKernelGGL(k_weight_sync, dim3(one_shot_grid(g.total)),
-                       dim3(kBlock), 0, s, g);
+                       dim3(kBlock), c.stream_lds, s, g);
     return hipGetLastError();
 }
 
@@ -281,7 +284,7 @@ hipError_t launch_grad_reduce(const ue_ctx &c, const int32_t *rep_off,
     if (g.total == 0) return hipSuccess;
     // one 16 KiB chunk per workgroup, each launched once (as the sync)
     hipLaunchKernelGGL(k_grad_reduce, dim3(one_shot_grid(g.total)),
-                       dim3(kBlock), 0, s, g);
+                       dim3(kBlock), c.stream_lds, s, g);
     return hipGetLastError();
 }
 

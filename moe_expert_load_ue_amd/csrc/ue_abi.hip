@@ -122,6 +122,7 @@ int init_shape(const ue_config &cfg, int dev, const DeviceInfo &info,
 
     c.reroute_lds = reroute_lds_bytes(E, R, c.P, k);
     c.count_lds = count_lds_bytes(E, info.lds_per_cu, info.lds_cap);
+    c.stream_lds = quarter_cu_lds(info.lds_per_cu, info.lds_cap);
     // the quota search keeps each pass's chunks when they fit in LDS
     c.plan_per_wave = cfg.quota_mode == UE_QUOTA_SEARCH &&
                       plan_lds_bytes(E, R, S, c.P, true) + kPlanStaticLds <=

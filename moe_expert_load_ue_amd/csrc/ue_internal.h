@@ -65,6 +65,7 @@ struct ue_ctx {
     size_t plan_lds = 0;
     bool plan_per_wave = false;   // planner keeps every pass's chunks
     size_t count_lds = 0;         // LDS the count asks for (see k_load)
+    size_t stream_lds = 0;        // LDS the sync and reduction ask for (k_stream)
     // the quota search spread over several workgroups per layer: per pass
     // slot (4 per workgroup, at most 4 * num_cu) its chunks and their
     // number, and per layer a count of workgroups done (zero between
@@ -154,9 +155,13 @@ const char *static_last_error();
 constexpr size_t kPlanStaticLds = 5120;
 
 size_t load_lds_bytes(int E);
-// LDS the count kernel asks for: its need, or a quarter of a CU's LDS
-// when that is more (and allowed), so that at most four of its workgroups
-// share a CU
+// A quarter of a CU's LDS when a launch may ask for it without raising a
+// kernel's limit (at most 64 KiB and within the per-workgroup cap), else
+// 0: asked for by a streaming launch, it holds at most four of its
+// workgroups on a CU
+size_t quarter_cu_lds(size_t lds_per_cu, size_t lds_cap);
+// LDS the count kernel asks for: its need, or the quarter share when that
+// is more
 size_t count_lds_bytes(int E, size_t lds_per_cu, size_t lds_cap);
 // The load's split of one call over L layers of A assignments: tiles of
 // kLoadTile assignments, groups of `group` consecutive tiles (one counting
