@@ -560,16 +560,32 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     __syncthreads();
     // perm in the tile's (expert, j) order: each entry's dispatch position
     // again from its expert's fast path (or the replica walk)
-    for (int s2 = tid; s2 < n_valid; s2 += kBlock) {
-        const uint32_t v = stage[s2];
-        const int e = static_cast<int>(v >> 11);
-        const int4 f = einfo[e];
-        const int jt = s2 - (f.x & 0xFFFF);
-        int p = f.y, pos = f.z + jt;
-        int end;
-        if (jt >= (f.x >> 16)) locate(e, f.w + jt, p, pos, end);
-        if (p >= 0 && pos >= 0 && pos < A)
-            *at(perm_l, pos) = tile0 + static_cast<int>(v & 2047u);
+    // (kPermBatch entries per thread at a time, their LDS reads in flight
+    // together: 2.5 us off the 58-layer dsv3 launch against one at a time;
+    // eight at a time needs 64 VGPRs and spills at 8 waves per SIMD)
+    constexpr int kPermBatch = 4;
+    for (int s0 = tid; s0 < n_valid; s0 += kPermBatch * kBlock) {
+        uint32_t v[kPermBatch];
+        int4 f[kPermBatch];
+#pragma unroll
+        for (int u = 0; u < kPermBatch; ++u) {
+            const int s2 = s0 + u * kBlock;
+            v[u] = s2 < n_valid ? stage[s2] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kPermBatch; ++u) f[u] = einfo[v[u] >> 11];
+#pragma unroll
+        for (int u = 0; u < kPermBatch; ++u) {
+            const int s2 = s0 + u * kBlock;
+            if (s2 >= n_valid) break;
+            const int e = static_cast<int>(v[u] >> 11);
+            const int jt = s2 - (f[u].x & 0xFFFF);
+            int p = f[u].y, pos = f[u].z + jt;
+            int end;
+            if (jt >= (f[u].x >> 16)) locate(e, f[u].w + jt, p, pos, end);
+            if (p >= 0 && pos >= 0 && pos < A)
+                *at(perm_l, pos) = tile0 + static_cast<int>(v[u] & 2047u);
+        }
     }
 
     // ---- 5. last tile: per-rank counts and faults ----------------------------
