@@ -392,10 +392,18 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
             uint8_t *prow8 = bpre8 + e * W;
             int run = 0;
             for (int i0 = 0; i0 < W; i0 += 8) {
+                // eight words loaded unconditionally (four paired reads,
+                // one wait), then the ones past the row masked: a
+                // conditional load per word made the compiler wait on each
+                // before the next. The over-read (at most 7 words past the
+                // last expert's row, none at W = 8) stays in region A,
+                // whose prefix arrays follow the words.
                 uint32_t bits[8];
 #pragma unroll
+                for (int j = 0; j < 8; ++j) bits[j] = row[i0 + j];
+#pragma unroll
                 for (int j = 0; j < 8; ++j)
-                    bits[j] = i0 + j < W ? row[i0 + j] : 0u;
+                    if (i0 + j >= W) bits[j] = 0u;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     if (i0 + j < W) {
