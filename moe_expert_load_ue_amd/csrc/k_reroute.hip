@@ -80,6 +80,20 @@ __device__ __forceinline__ T *at(T *p, int i) {
                                  static_cast<uint32_t>(i) * sizeof(T));
 }
 
+// Largest number of tokens that kRerouteTile consecutive assignments touch.
+// (a tile of whole tokens when k divides the tile size, since tiles start
+// at multiples of it)
+__host__ __device__ constexpr int tile_tokens(int k) {
+    return kRerouteTile % k == 0 ? kRerouteTile / k
+                                 : (kRerouteTile - 1) / k + 2;
+}
+
+// The common shape (top-8 routing, at most one expert per thread) has its
+// own instance: k, the bitmap's words per expert and the per-expert loops
+// are then constants, and the token arithmetic of every item folds.
+constexpr int kFastK = 8;
+constexpr int kFastWords = (tile_tokens(kFastK) + 31) / 32;
+
 // Bitmap path: expert e's token bitmap is words [e*Wp, e*Wp + W), with an
 // odd stride Wp so that neighbouring experts fall in other banks; the
 // popcount prefix of each word follows in a second array: one byte per
@@ -126,7 +140,7 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
 // it uses 59), which it meets without spilling: left to itself the
 // compiler took 68 and 7 waves, 5% slower at dsv3 size. The standalone
 // instance would spill at 64 and is left free.
-template <bool kAfterLoad>
+template <bool kAfterLoad, bool kFast>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(RerouteArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
@@ -144,7 +158,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int W = g.bm_words;
+    const int W = kFast ? kFastWords : g.bm_words;
     const int Wp = bm_stride(W);
 
     int32_t *area = lds;
@@ -174,7 +188,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     int32_t *__restrict__ perm_l = g.perm + base;
     int32_t *__restrict__ inv_l = g.inv_perm ? g.inv_perm + base : nullptr;
     const int A = g.A;
-    constexpr int kPerThread = kMaxExperts / kBlock;
+    constexpr int kPerThread = kFast ? 1 : kMaxExperts / kBlock;
     int32_t ids[kRerouteItems];
     int32_t pre_reg[kPerThread], cnt_reg[kPerThread];
     int tile = 0;
@@ -183,7 +197,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     // (Spreading a step's tokens 32 apart, to keep a hot expert's bitmap
     // ORs off one LDS word, measured slower: the accesses no longer
     // coalesce.)
-    const int k = g.k;
+    const int k = kFast ? kFastK : g.k;
     auto lane_base = [&](int t) {
         return t * kRerouteTile + w * 64 * kRerouteItems + lane;
     };
@@ -230,28 +244,55 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
             cnt[q] = o1 - o0;
         }
     };
+    const int32_t *pl = g.placement + static_cast<int64_t>(layer) * g.lay.words;
+    // The table is read as the planner wrote it, with every index clamped,
+    // so a corrupt block can only produce faults. Two rounds of both tables
+    // at a time, every read of a round pair issued before the first write.
+    // The first pair is read before the tile's ids and prefixes: loads
+    // complete in order, so the table's writes then wait for the table
+    // alone, and the ids arrive while the capacity prefixes are formed.
+    // (The reads are unconditional, at indices clamped into each table,
+    // and the writes drop what lies beyond: a conditional read lets the
+    // compiler wait on it inside its own branch.)
+    int vo[2], vq[2], vs[2], vc[2];
+    auto table_read = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = i0 + u * kBlock + tid;
+            const int ie = i <= E ? i : E, ip = i < P ? i : P - 1;
+            vo[u] = pl[g.lay.rep_off + ie];
+            vq[u] = pl[g.lay.rep_slot + ip];
+            vs[u] = pl[g.lay.slot_off + ip];
+            vc[u] = pl[g.lay.rep_cap + ip];
+        }
+    };
+    auto table_write = [&](int i0) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int i = i0 + u * kBlock + tid;
+            if (i <= E) rep_off[i] = vo[u] < 0 ? 0 : (vo[u] > P ? P : vo[u]);
+            if (i < P) {
+                rep_slot[i] = (vq[u] >= 0 && vq[u] < P) ? vq[u] : -1;
+                slot_off[i] = vs[u];
+                rep_hi[i] = vc[u] > 0 ? vc[u] : 0;  // capacity, until the prefix below
+            }
+        }
+    };
+    table_read(0);
     if (kAfterLoad) {
         tile = item % static_cast<int>(gridDim.x);
         if (tile >= g.tiles) return;
-        load_ids(tile, ids);
         load_prefix(tile, pre_reg, cnt_reg);
+        load_ids(tile, ids);
         if (tid == 0) s_epoch = 0;
     } else if (tid == 0) {
         take_ticket(g.tick + layer, g.tiles, s_ticket, s_epoch);
     }
-    const int32_t *pl = g.placement + static_cast<int64_t>(layer) * g.lay.words;
-    // The table is read as the planner wrote it, with every index clamped,
-    // so a corrupt block can only produce faults.
-    for (int e = tid; e <= E; e += kBlock) {
-        const int v = pl[g.lay.rep_off + e];
-        rep_off[e] = v < 0 ? 0 : (v > P ? P : v);
-    }
-    for (int p = tid; p < P; p += kBlock) {
-        const int q = pl[g.lay.rep_slot + p];
-        rep_slot[p] = (q >= 0 && q < P) ? q : -1;
-        slot_off[p] = pl[g.lay.slot_off + p];
-        const int cap = pl[g.lay.rep_cap + p];
-        rep_hi[p] = cap > 0 ? cap : 0;     // capacity, until the prefix below
+    table_write(0);
+    const int tab_n = E + 1 > P ? E + 1 : P;
+    for (int i0 = 2 * kBlock; i0 < tab_n; i0 += 2 * kBlock) {
+        table_read(i0);
+        table_write(i0);
     }
     const bool bitmap = W > 0;
     uint32_t *bm = reinterpret_cast<uint32_t *>(area);          // [E][Wp]
@@ -346,6 +387,10 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     // ---- 1. ranks within the tile ------------------------------------------
     int32_t rank[kRerouteItems];
     int dup = 0;
+    // the lane's first token in the tile; in the fast instance the token of
+    // item i is tl_lane + i * 64 / k, found again at the read-back instead
+    // of being held in rank[] across the popcount pass
+    int tl_lane = 0;
     if (bitmap) {
         // token of item i relative to the tile's first token, stepped
         // without a division per item
@@ -355,6 +400,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
         int tl = static_cast<int>(qa) - t_first;
         int rm = static_cast<int>(static_cast<uint32_t>(aL) - qa * uk);
         const int q64 = 64 / k, r64 = 64 % k;
+        tl_lane = tl;
         // Branch-free: an id out of range ORs nothing into expert 0's
         // word, so every lane issues the same instructions. After a load
         // the OR returns nothing (a repeated expert shows up below as a
@@ -363,7 +409,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
-            rank[i] = tl;                  // the token, until the read-back
+            if (!kFast) rank[i] = tl;      // the token, until the read-back
             const uint32_t bit = id >= 0 ? 1u << (tl & 31) : 0u;
             uint32_t *word = bm + (id >= 0 ? id : 0) * Wp + (tl >> 5);
             if (kAfterLoad) {
@@ -420,10 +466,18 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
         else __syncthreads();
     }
     if (!use_match) {
+        // (the fast instance forms each word's address again here: held
+        // from the ORs across the popcount pass, the eight addresses
+        // pushed it past 64 VGPRs; the empty asm hides that they equal
+        // the ORs' addresses)
+        if (kFast) {
+#pragma unroll
+            for (int i = 0; i < kRerouteItems; ++i) asm volatile("" : "+v"(ids[i]));
+        }
 #pragma unroll
         for (int i = 0; i < kRerouteItems; ++i) {
             const int id = ids[i];
-            const int tl = rank[i];
+            const int tl = kFast ? tl_lane + i * (64 / kFastK) : rank[i];
             const int e = id >= 0 ? id : 0;
             const int word = e * Wp + (tl >> 5);
             const uint32_t below = (1u << (tl & 31)) - 1u;
@@ -639,14 +693,6 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
                           (poisoned ? kPoisonBit : 0);
 }
 
-// Largest number of tokens that kRerouteTile consecutive assignments touch.
-// (a tile of whole tokens when k divides the tile size, since tiles start
-// at multiples of it)
-int tile_tokens(int k) {
-    return kRerouteTile % k == 0 ? kRerouteTile / k
-                                 : (kRerouteTile - 1) / k + 2;
-}
-
 }  // namespace
 
 int reroute_bitmap_words(int E, int k) {
@@ -670,13 +716,15 @@ hipError_t reroute_prepare(size_t lds_bytes) {
     static size_t granted = 0;
     std::lock_guard<std::mutex> lock(mu);
     if (lds_bytes <= granted) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&k_reroute<false>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds_bytes));
-    if (e == hipSuccess)
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_reroute<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                static_cast<int>(lds_bytes));
+    const void *fns[] = {reinterpret_cast<const void *>(&k_reroute<false, false>),
+                         reinterpret_cast<const void *>(&k_reroute<true, false>),
+                         reinterpret_cast<const void *>(&k_reroute<false, true>),
+                         reinterpret_cast<const void *>(&k_reroute<true, true>)};
+    hipError_t e = hipSuccess;
+    for (const void *f : fns)
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    static_cast<int>(lds_bytes));
     if (e == hipSuccess) granted = lds_bytes;
     return e;
 }
@@ -716,13 +764,18 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.load_groups = sh.groups;
     g.rank_counts = rank_counts;
     g.faults = faults;
-    if (after_load) {
-        hipLaunchKernelGGL(k_reroute<true>, dim3(tiles, L), dim3(kBlock),
-                           c.reroute_lds, s, g);
-    }
+    // the fast instance: top-8 routing, every expert's bitmap at its full
+    // size, at most one expert per thread
+    const bool fast = c.k == kFastK && g.bm_words == kFastWords && c.E <= kBlock;
+    const dim3 grid(tiles, L);
+    if (after_load && fast)
+        hipLaunchKernelGGL((k_reroute<true, true>), grid, dim3(kBlock), c.reroute_lds, s, g);
+    else if (after_load)
+        hipLaunchKernelGGL((k_reroute<true, false>), grid, dim3(kBlock), c.reroute_lds, s, g);
+    else if (fast)
+        hipLaunchKernelGGL((k_reroute<false, true>), grid, dim3(kBlock), c.reroute_lds, s, g);
     else
-        hipLaunchKernelGGL(k_reroute<false>, dim3(tiles, L), dim3(kBlock),
-                           c.reroute_lds, s, g);
+        hipLaunchKernelGGL((k_reroute<false, false>), grid, dim3(kBlock), c.reroute_lds, s, g);
     return hipGetLastError();
 }
 
