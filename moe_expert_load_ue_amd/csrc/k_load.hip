@@ -52,7 +52,7 @@ __device__ __forceinline__ void count_one(int id, int E, int sub,
               ok ? 1u << ((id & 1) << 4) : 0u);
 }
 
-template <int G, int kAhead>
+template <int G>
 __global__ __launch_bounds__(kBlock) void k_count(CountArgs g) {
     extern __shared__ __align__(16) int32_t lds[];
     const int E = g.E;
@@ -70,16 +70,14 @@ __global__ __launch_bounds__(kBlock) void k_count(CountArgs g) {
     const int ntiles = g.tiles - tile_first < G ? g.tiles - tile_first : G;
     // The loads of a full tile are issued kAhead tiles before it is
     // counted (a rolling set of registers), the first ones before the
-    // histograms are cleared. One tile ahead is the fastest when the
-    // launch fills the device: with every workgroup resident at once, more
-    // loads in flight only crowd the memory system (58 dsv3 layers: 24.9 us
-    // at one tile ahead, 26.1 at two, 27.0 at three or four, 27.5 at eight,
-    // same box). A launch of at most one workgroup per CU (a few layers)
-    // is latency-bound instead, and issues every tile's loads at once
-    // (kAhead = G).
+    // histograms are cleared. One tile ahead is the fastest: with every
+    // workgroup of the launch resident at once, more loads in flight only
+    // crowd the memory system (58 dsv3 layers: 24.9 us at one tile ahead,
+    // 26.1 at two, 27.0 at three or four, 27.5 at eight, same box).
     // Plain (temporal) loads: the fused reroute reads the same routing
     // right after and finds it in the device-wide cache (nontemporal loads
     // here cost the reroute 20 us).
+    constexpr int kAhead = 1;
     i32x4 r[kAhead][kLoadItems / 4];
     auto full = [&](int s) {
         const int64_t t0 = static_cast<int64_t>(tile_first + s) * kLoadTile;
@@ -204,11 +202,7 @@ hipError_t launch_count(const ue_ctx &c, const int32_t *routing, int L,
     const dim3 grid(sh.groups, L);
     const size_t need = load_lds_bytes_for(c.E, sh.group);
     const size_t lds = c.count_lds > need ? c.count_lds : need;
-    // at most one workgroup per CU: every tile's loads in flight at once
-    if (static_cast<int64_t>(sh.groups) * L <= c.num_cu)
-        hipLaunchKernelGGL((k_count<kLoadGroup, kLoadGroup>), grid, dim3(kBlock), lds, s, g);
-    else
-        hipLaunchKernelGGL((k_count<kLoadGroup, 1>), grid, dim3(kBlock), lds, s, g);
+    hipLaunchKernelGGL(k_count<kLoadGroup>, grid, dim3(kBlock), lds, s, g);
     return hipGetLastError();
 }
 

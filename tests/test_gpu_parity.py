@@ -310,6 +310,50 @@ def test_plan_from_other_counts_faults():
     assert int(out["faults"][0]) == T * k - (T // 2) * k
 
 
+@pytest.mark.parametrize("E,k", [(256, 8), (512, 8), (256, 7)],
+                         ids=["top8_instance", "top8_over_256_experts",
+                              "general_instance"])
+def test_top8_and_general_reroute_instances(E, k):
+    """The reroute has an instance for top-8 routing with at most 256
+    experts (constant bitmap shape, one expert per thread) and a general
+    one. Each, as three calls and fused: ids out of range, a token that
+    repeats an expert (its tile ranks by matching), a ragged last tile;
+    then a plan made from the first half of the tokens applied to all of
+    them through the standalone reroute, so that assignments past the
+    plan's capacities and positions are faults, against the oracle's
+    reroute of the oracle's plan of the same half."""
+    rng = np.random.default_rng(8000 + E + k)
+    R, S, T, L = 64, 1, 9001, 2
+    routing = np.stack([pins.random_routing(rng, T, E, k, 1.3)
+                        for _ in range(L)])
+    routing[0, 17, 2] = E + 3
+    routing[1, 4000, 0] = -5
+    routing[1, 8999, 1] = routing[1, 8999, 4]
+    say(f"reroute instances: E={E} k={k}")
+    ctx = make_ctx(E, R, S, k, T, L)
+    for fused in (False, True):
+        res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
+        compare_with_oracle(res, routing, E, R, S)
+    half = np.ascontiguousarray(routing[:, : T // 2])
+    counts = ue.ue_load(ctx, torch.from_numpy(half).to(DEV))
+    placement = ue.ue_plan(ctx, counts)
+    fill = pins.PERM_FILL
+    perm = torch.full((L, T * k), fill, dtype=torch.int32, device=DEV)
+    out = ue.ue_reroute(ctx, torch.from_numpy(routing).to(DEV), placement,
+                        perm=perm)
+    torch.cuda.synchronize()
+    half_counts, _ = oracle.load(half, E)
+    for layer in range(L):
+        pl = oracle.plan(half_counts[layer], R, S)
+        rr = oracle.reroute(routing[layer].reshape(-1), pl, perm_fill=fill)
+        assert rr["faults"] > 0
+        assert int(out["faults"][layer]) == rr["faults"], layer
+        for key in ("phys", "inv_perm", "rank_counts"):
+            assert np.array_equal(out[key][layer].cpu().numpy().reshape(-1),
+                                  rr[key].reshape(-1)), (layer, key)
+        assert np.array_equal(perm[layer].cpu().numpy(), rr["perm"]), layer
+
+
 def test_deterministic_repeats():
     cfg = W.CONFIGS["large_ep"]
     routing = W.make_routing(cfg, device=DEV)
