@@ -56,7 +56,7 @@ struct RerouteArgs {
     const int32_t *placement;
     int32_t A;                 // assignments per layer (< 2^30)
     int E, R, NS, P, k, ebits, tiles, max_tiles;
-    int load_group, load_groups;// the load's tiles per group; groups
+    int load_groups;           // the load's groups (of kLoadGroup tiles)
     int bm_words;              // words per expert bitmap (0: no bitmap path)
     uint32_t spin_limit;       // bound on one lookback wait
     uint32_t lds_bytes;        // dynamic LDS the launch provides
@@ -71,13 +71,15 @@ struct RerouteArgs {
 
 // Element i of a per-layer array, with the byte offset formed in 32 bits
 // (every offset here is below 2^32 since T*k < 2^30): the address is then
-// a uniform 64-bit base plus one 32-bit register.
+// a uniform 64-bit base plus one 32-bit register, which the loads and
+// stores take as it is (a product formed in 64 bits would need a 64-bit
+// add per access).
 template <typename T>
 __device__ __forceinline__ T *at(T *p, int i) {
     using B = typename std::conditional<std::is_const<T>::value, const char,
                                         char>::type;
-    return reinterpret_cast<T *>(reinterpret_cast<B *>(p) +
-                                 static_cast<uint32_t>(i) * sizeof(T));
+    const uint32_t off = static_cast<uint32_t>(i) * static_cast<uint32_t>(sizeof(T));
+    return reinterpret_cast<T *>(reinterpret_cast<B *>(p) + off);
 }
 
 // Largest number of tokens that kRerouteTile consecutive assignments touch.
@@ -106,6 +108,18 @@ __host__ __device__ __forceinline__ bool bm_pre8(int W) { return W <= 8; }
 __host__ __device__ __forceinline__ int bitmap_ints(int E, int W) {
     const int n = E * bm_stride(W);
     return n + (bm_pre8(W) ? (E * W + 3) / 4 : (n + 1) / 2);
+}
+
+// How many of the n consecutive dispatch positions from pos0 the fast path
+// of an expert's record may take: the run stops before the first position
+// outside [0, A) (only a plan made for other counts has such positions),
+// so that every position the fast path gives is valid and the permutation
+// pass needs no check for it; the rest go through the replica walk, which
+// checks each one.
+__device__ __forceinline__ int in_range_run(int pos0, int n, int A) {
+    if (pos0 < 0) return 0;
+    const int room = A - pos0;
+    return n < room ? n : (room > 0 ? room : 0);
 }
 
 // Largest bitmap region (ints); beyond it, the configuration ranks by
@@ -228,7 +242,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     // its group's base plus the tile's 16-bit offset in the group, and the
     // next row's offset (the next tile's, or the group's own count)
     auto load_prefix = [&](int t, int32_t *pre, int32_t *cnt) {
-        const int grp = t / g.load_group;
+        const int grp = t / kLoadGroup;    // the load's split (load_shape)
         const int32_t *gb = g.group_base +
                             (static_cast<int64_t>(layer) * g.load_groups + grp) * E;
         const uint16_t *to = g.tile_off +
@@ -237,9 +251,9 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
 #pragma unroll
         for (int q = 0; q < kPerThread; ++q) {
             const int e = tid + q * kBlock;
-            const int b = e < E ? gb[e] : 0;
-            const int o0 = e < E ? to[e] : 0;
-            const int o1 = e < E ? to[E + e] : 0;
+            const int b = e < E ? *at(gb, e) : 0;
+            const int o0 = e < E ? *at(to, e) : 0;
+            const int o1 = e < E ? *at(to, E + e) : 0;
             pre[q] = b + o0;
             cnt[q] = o1 - o0;
         }
@@ -260,10 +274,10 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
         for (int u = 0; u < 2; ++u) {
             const int i = i0 + u * kBlock + tid;
             const int ie = i <= E ? i : E, ip = i < P ? i : P - 1;
-            vo[u] = pl[g.lay.rep_off + ie];
-            vq[u] = pl[g.lay.rep_slot + ip];
-            vs[u] = pl[g.lay.slot_off + ip];
-            vc[u] = pl[g.lay.rep_cap + ip];
+            vo[u] = *at(pl, g.lay.rep_off + ie);
+            vq[u] = *at(pl, g.lay.rep_slot + ip);
+            vs[u] = *at(pl, g.lay.slot_off + ip);
+            vc[u] = *at(pl, g.lay.rep_cap + ip);
         }
     };
     auto table_write = [&](int i0) {
@@ -352,7 +366,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
                 if (sl >= 0) {
                     slot = sl;
                     pos0 = slot_off[sl] + (j0 - lo);
-                    lim = run - j0;
+                    lim = in_range_run(pos0, run - j0, A);
                 }
             }
         }
@@ -579,7 +593,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
             const int j0 = einfo[e].w;
             int q, pos0, end;
             locate(e, j0, q, pos0, end);
-            const int lim = q >= 0 ? end - j0 : 0;
+            const int lim = q >= 0 ? in_range_run(pos0, end - j0, A) : 0;
             ehalf[8 * e + 1] =
                 static_cast<uint16_t>(lim < kRerouteTile ? lim : kRerouteTile);
             einfo[e].y = q;
@@ -652,10 +666,13 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
             const int e = static_cast<int>(v[u] >> 11);
             const int jt = s2 - (f[u].x & 0xFFFF);
             int p = f[u].y, pos = f[u].z + jt;
-            int end;
-            if (jt >= (f[u].x >> 16)) locate(e, f[u].w + jt, p, pos, end);
-            if (p >= 0 && pos >= 0 && pos < A)
-                *at(perm_l, pos) = tile0 + static_cast<int>(v[u] & 2047u);
+            bool ok = true;
+            if (jt >= (f[u].x >> 16)) {
+                int end;
+                locate(e, f[u].w + jt, p, pos, end);
+                ok = p >= 0 && pos >= 0 && pos < A;
+            }
+            if (ok) *at(perm_l, pos) = tile0 + static_cast<int>(v[u] & 2047u);
         }
     }
 
@@ -769,7 +786,7 @@ static hipError_t launch(const ue_ctx &c, bool after_load,
     g.group_base = c.group_base;
     g.tile_off = c.tile_off;
     const LoadShape sh = load_shape(A, L);
-    g.load_group = sh.group;
+    if (sh.group != kLoadGroup) return hipErrorInvalidValue;   // never: one split
     g.load_groups = sh.groups;
     g.rank_counts = rank_counts;
     g.faults = faults;
