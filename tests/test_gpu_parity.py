@@ -354,6 +354,27 @@ def test_top8_and_general_reroute_instances(E, k):
         assert np.array_equal(perm[layer].cpu().numpy(), rr["perm"]), layer
 
 
+@pytest.mark.parametrize("E,R,k,T", [(250, 25, 8, 70001), (1024, 64, 8, 40001),
+                                     (64, 8, 8, 300000)],
+                         ids=["E250_35_groups", "E1024_20_groups",
+                              "E64_147_groups"])
+def test_scan_of_many_load_groups(E, R, k, T):
+    """Layers whose load groups are too many for one batch of the scan's
+    loads per thread: the scan then takes the experts in pairs (one 32-bit
+    load per pair and group), with ragged last groups, threads whose chunk
+    is empty, and at E = 1024 two threads per pair; counts, bases (through
+    the reroute) and plans against the oracle, standalone and fused."""
+    rng = np.random.default_rng(9000 + E)
+    S, L = 1, 2
+    routing = np.stack([pins.random_routing(rng, T, E, k, 1.1)
+                        for _ in range(L)])
+    say(f"many load groups: E={E} R={R} k={k} T={T}")
+    ctx = make_ctx(E, R, S, k, T, L)
+    for fused in (False, True):
+        res = gpu_rebalance(ctx, torch.from_numpy(routing), fused=fused)
+        compare_with_oracle(res, routing, E, R, S)
+
+
 def test_deterministic_repeats():
     cfg = W.CONFIGS["large_ep"]
     routing = W.make_routing(cfg, device=DEV)
