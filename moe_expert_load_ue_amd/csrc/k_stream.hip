@@ -77,20 +77,42 @@ __global__ __launch_bounds__(kBlock) void k_weight_sync(StreamArgs g) {
         const int64_t end = (off + kSyncChunk < g.mat_bytes[m])
                                 ? off + kSyncChunk : g.mat_bytes[m];
         if (end - off == kSyncChunk) {
+            // The replicas' buffer pointers are read kRepBatch at a time
+            // before any of their stores: such a read is a vector load,
+            // and its wait covers every vector memory operation in flight,
+            // stores included, so a read between two replicas' stores
+            // would hold the second replica's stores until the first
+            // replica's have landed.
+            constexpr int kRepBatch = 4;
             u32x4 v[kSyncVec];
-            const u32x4 *s = reinterpret_cast<const u32x4 *>(src + off);
+            for (int r0 = lo; r0 < hi; r0 += kRepBatch) {
+                u32x4 *d[kRepBatch];
 #pragma unroll
-            for (int i = 0; i < kSyncVec; ++i)
-                v[i] = s[i * kBlock + tid];
-            for (int r = lo; r < hi; ++r) {
-                const int b = g.rep_buf[r];
-                if (static_cast<uint32_t>(b) >= static_cast<uint32_t>(g.n_buffers))
-                    continue;
-                u32x4 *d = reinterpret_cast<u32x4 *>(
-                    static_cast<char *>(g.spare[b * g.n_mats + m]) + off);
+                for (int u = 0; u < kRepBatch; ++u) {
+                    const int b = r0 + u < hi ? g.rep_buf[r0 + u] : -1;
+                    d[u] = static_cast<uint32_t>(b) < static_cast<uint32_t>(g.n_buffers)
+                        ? reinterpret_cast<u32x4 *>(
+                              static_cast<char *>(g.spare[b * g.n_mats + m]) + off)
+                        : nullptr;
+                }
+                if (r0 == lo) {
+                    const u32x4 *s = reinterpret_cast<const u32x4 *>(src + off);
 #pragma unroll
-                for (int i = 0; i < kSyncVec; ++i)
-                    d[i * kBlock + tid] = v[i];
+                    for (int i = 0; i < kSyncVec; ++i)
+                        v[i] = s[i * kBlock + tid];
+                    // the stores need the master's piece: wait for it here,
+                    // once, so that no wait is placed between two
+                    // replicas' stores (one there would also hold the second
+                    // replica's stores until the first replica's land)
+                    __builtin_amdgcn_s_waitcnt(0);
+                }
+#pragma unroll
+                for (int u = 0; u < kRepBatch; ++u) {
+                    if (d[u] == nullptr) continue;
+#pragma unroll
+                    for (int i = 0; i < kSyncVec; ++i)
+                        d[u][i * kBlock + tid] = v[i];
+                }
             }
         } else {
             // last, partial chunk: whole vectors, then 2-byte elements
@@ -193,6 +215,46 @@ __global__ __launch_bounds__(kBlock) void k_gather_rows(
     const int wave = (blockIdx.x * kBlock + threadIdx.x) >> 6;
     const int nwaves = (gridDim.x * kBlock) >> 6;
     const int64_t nvec = row_bytes / 16;
+    if (nvec == 64 * kGatherVec && k <= 64) {
+        // One pass per row (as at 4,096 bf16 columns): the next row's
+        // loads and destinations are issued before this row's stores, so
+        // that its load latency overlaps them (a wait after the stores
+        // would also wait for them).
+        u32x4 cur[kGatherVec];
+        int cur_pos = -1;
+        auto load_row = [&](int t, u32x4 *v, int &my_pos) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(
+                x + static_cast<int64_t>(t) * row_bytes);
+#pragma unroll
+            for (int i = 0; i < kGatherVec; ++i)
+                v[i] = __builtin_nontemporal_load(src + i * 64 + lane);
+            my_pos = lane < k ? inv_perm[static_cast<int64_t>(t) * k + lane] : -1;
+        };
+        if (wave < T) load_row(wave, cur, cur_pos);
+        for (int t = wave; t < T; t += nwaves) {
+            // this row's piece and destinations have arrived (and the
+            // previous row's stores have landed): wait here, once, before
+            // the next row's loads are issued, so that no wait falls
+            // between those loads and this row's stores
+            __builtin_amdgcn_s_waitcnt(0);
+            u32x4 nxt[kGatherVec];
+            int nxt_pos = -1;
+            if (t + nwaves < T) load_row(t + nwaves, nxt, nxt_pos);
+            for (int j = 0; j < k; ++j) {
+                const int pos = __builtin_amdgcn_readlane(cur_pos, j);
+                if (static_cast<uint64_t>(pos) >= static_cast<uint64_t>(n_pos))
+                    continue;
+                u32x4 *dst = reinterpret_cast<u32x4 *>(
+                    out + static_cast<int64_t>(pos) * row_bytes);
+#pragma unroll
+                for (int i = 0; i < kGatherVec; ++i) dst[i * 64 + lane] = cur[i];
+            }
+#pragma unroll
+            for (int i = 0; i < kGatherVec; ++i) cur[i] = nxt[i];
+            cur_pos = nxt_pos;
+        }
+        return;
+    }
     for (int t = wave; t < T; t += nwaves) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(
             x + static_cast<int64_t>(t) * row_bytes);
