@@ -6,26 +6,25 @@
 // gradients are reduced into the master gradients during backward. The
 // UltraEP news write-up (section on how balancing in 300 microseconds
 // works) moves expert state by persistent tile streaming; on one device
-// that becomes persistent workgroups streaming 16-byte vectors through
-// registers.
+// that becomes workgroups streaming 16-byte vectors through registers.
 //
-// Work items are (expert, matrix, chunk) triples taken grid-stride by a
-// persistent grid sized to the device. Weight sync loads each master chunk
-// once and stores it to every replica (read-once fan-out). Gradient
-// reduction loads the master chunk and each replica chunk in table order
-// and adds them left to right with the running sum held in binary64, then
-// rounds it once to binary32 (round to nearest even; no reassociation, no
-// packed fp32 instructions): the fp32 gradient then lies within one
-// rounding of the exact sum even where replicas cancel the master, at no
-// cost in bandwidth. The gather reads each token
-// row once and writes it to the k dispatch positions of that token. The
-// reduction's and the gather's loads are nontemporal, the sync's plain
-// (measured faster in its one-workgroup-per-chunk form); the reduction's
-// stores are nontemporal, those of the sync and the gather plain (measured
-// 1.3% and 2.5% faster for their 1 : 2 and 1 : 8 mixes). The sync and the
-// reduction run one workgroup
-// per chunk, launched once, rather than a persistent grid (see the
-// launchers).
+// Work items are (expert, matrix, chunk) triples. The sync and the
+// reduction launch one workgroup per chunk, once (the kernels still loop
+// grid-stride for grids capped below the item count); the gather runs a
+// grid capped at 16 workgroups per CU, one wave per token row. Weight sync
+// loads each master chunk once and stores it to every replica (read-once
+// fan-out), with the replicas' buffer pointers read before any of the
+// stores. Gradient reduction loads the master chunk and each replica chunk
+// in table order and adds them left to right with the running sum held in
+// binary64, then rounds it once to binary32 (round to nearest even; no
+// reassociation, no packed fp32 instructions): the fp32 gradient then lies
+// within one rounding of the exact sum even where replicas cancel the
+// master, at no cost in bandwidth. The gather reads each token row once and
+// writes it to the k dispatch positions of that token. The reduction's and
+// the gather's loads are nontemporal, the sync's plain (measured faster in
+// its one-workgroup-per-chunk form); the reduction's stores are
+// nontemporal, those of the sync and the gather plain (measured 1.3% and
+// 2.5% faster for their 1 : 2 and 1 : 8 mixes).
 #include "ue_internal.h"
 
 namespace ue {
