@@ -736,7 +736,8 @@ __global__ __launch_bounds__(kPlanBlock) void k_plan(
         // (one expert per thread below needs a second round of loads, and
         // reads its rows again, once a thread's chunk exceeds 8 groups)
         const int pt1 = kPlanBlock / E;
-        if ((E & 1) == 0 && (ng + pt1 - 1) / pt1 > 8) {
+        if ((E & 1) == 0 && (ng + pt1 - 1) / pt1 > 8 &&
+            lds_bytes >= 2 * kPlanBlock * sizeof(int32_t)) {
             // Two experts per thread (E even, so every row is 4-byte
             // aligned): one 32-bit load reads a pair's counts in a group's
             // row. PT2 threads per pair (at least 2, since E <= 1024), each
