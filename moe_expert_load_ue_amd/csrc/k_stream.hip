@@ -22,9 +22,11 @@
 // master, at no cost in bandwidth. The gather reads each token row once and
 // writes it to the k dispatch positions of that token. The reduction's and
 // the gather's loads are nontemporal, the sync's plain (measured faster in
-// its one-workgroup-per-chunk form); the reduction's stores are
-// nontemporal, those of the sync and the gather plain (measured 1.3% and
-// 2.5% faster for their 1 : 2 and 1 : 8 mixes).
+// its one-workgroup-per-chunk form, and 1.8% faster than nontemporal ones
+// since); the reduction's and the sync's stores are nontemporal (the
+// sync's 1.5% faster than plain ones once its replicas' stores issue back
+// to back; plain ones were 1.3% faster before), the gather's plain (2.5%
+// faster for its 1 : 8 mix).
 #include "ue_internal.h"
 
 namespace ue {
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void k_weight_sync(StreamArgs g) {
                     if (d[u] == nullptr) continue;
 #pragma unroll
                     for (int i = 0; i < kSyncVec; ++i)
-                        d[u][i * kBlock + tid] = v[i];
+                        __builtin_nontemporal_store(v[i], d[u] + i * kBlock + tid);
                 }
             }
         } else {
