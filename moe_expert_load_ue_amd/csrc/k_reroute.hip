@@ -151,9 +151,9 @@ __host__ __device__ __forceinline__ int region_a_ints(int E, int W) {
 // faster: the hardware already overlaps one workgroup's table reads with
 // others' work, while the LDS per workgroup sets how many share a CU.)
 // After a load the kernel is held to 8 waves per SIMD (at most 64 VGPRs;
-// it uses 59), which it meets without spilling: left to itself the
-// compiler took 68 and 7 waves, 5% slower at dsv3 size. The standalone
-// instance would spill at 64 and is left free.
+// it uses 60, the top-8 instance 64), which it meets without spilling:
+// left to itself the compiler took 68 and 7 waves, 5% slower at dsv3 size.
+// The standalone instances would spill at 64 and are left free.
 template <bool kAfterLoad, bool kFast>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(RerouteArgs g) {
