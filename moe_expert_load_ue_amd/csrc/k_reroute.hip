@@ -552,7 +552,7 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     // of valid items in the tile)
     int n_valid;
     {
-        const int per = (E + kBlock - 1) / kBlock;
+        const int per = kFast ? 1 : (E + kBlock - 1) / kBlock;   // experts per thread
         const int b = tid * per;
         const int eend = (b + per < E) ? b + per : E;
         int local = 0;
@@ -646,9 +646,11 @@ __attribute__((amdgpu_waves_per_eu(kAfterLoad ? 8 : 1, 8))) void k_reroute(Rerou
     // perm in the tile's (expert, j) order: each entry's dispatch position
     // again from its expert's fast path (or the replica walk)
     // (kPermBatch entries per thread at a time, their LDS reads in flight
-    // together: 2.5 us off the 58-layer dsv3 launch against one at a time;
-    // eight at a time needs 64 VGPRs and spills at 8 waves per SIMD)
-    constexpr int kPermBatch = 4;
+    // together: four were 2.5 us off the 58-layer dsv3 launch against one
+    // at a time; the top-8 instance takes eight within its 64 VGPRs, and
+    // with the scan below at one expert per thread the launch measured
+    // 80.1 against 81.0-81.4 us; the general instance would spill at eight)
+    constexpr int kPermBatch = kFast ? 8 : 4;
     for (int s0 = tid; s0 < n_valid; s0 += kPermBatch * kBlock) {
         uint32_t v[kPermBatch];
         int4 f[kPermBatch];
